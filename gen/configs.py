@@ -44,10 +44,10 @@ CONFIGS = {
     "c3": Config("c3", E=384, K=7168, N=4096, T=64, k=8, routing="uniform", act_dist="student_t", seed=1237,
                  N2=7168, K2=2048, desc="Kimi-K2.5 gate_up + down, decode"),
     "c4": Config("c4", E=384, K=7168, N=4096, T=8192, k=8, routing="zipf", act_dist="student_t", seed=1238,
-                 N2=7168, K2=2048, mlp=True, desc="Kimi-K2.5 routed-expert MLP, prefill"),
+                 N2=7168, K2=2048, mlp=True, h_amax_hint=64.0, desc="Kimi-K2.5 routed-expert MLP, prefill"),
     # small cases for parity tests
-    "t_mlp": Config("t_mlp", E=4, K=256, N=256, T=64, k=2, routing="uniform", act_dist="student_t", seed=77,
-                    N2=256, K2=128, mlp=True, desc="tiny MLP (H=256, I=128)"),
+    "t_mlp": Config("t_mlp", E=4, K=256, N=512, T=64, k=2, routing="uniform", act_dist="student_t", seed=77,
+                    N2=256, K2=256, mlp=True, h_amax_hint=2.0, desc="tiny MLP (H=256, I=256)"),
     "t_zipf": Config("t_zipf", E=16, K=512, N=384, T=512, k=4, routing="zipf", zipf_zero=3, seed=78,
                      desc="small Zipf prefill with empty experts and ragged tiles"),
 }

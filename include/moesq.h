@@ -1,0 +1,200 @@
+/*
+ * moesq.h -- C ABI of the MI355X (gfx950) library for the Mixture-of-Experts expert path over
+ * paired-4:8 sparse NVFP4 weights ("libmoesq.so").
+ *
+ * Source of the method: paper "Hardware-Native Joint Sparse-Quantization for Trillion-Scale
+ * Mixture-of-Experts" (arxiv 2610.02241), Section 3.4 (Eq. 5, grouped sparse GEMM execution),
+ * Appendix A (feasible set, storage cost), Appendix D.1 (operand layout, scheduling, serving
+ * integration); model card "Kimi-K2.5-P48NVFP4-MoESQ" (compression details, sparse storage layout
+ * "pair-bitmask v1").
+ *
+ * Conventions for every call
+ *  - Pointers to tensors are DEVICE pointers unless a comment says "host". The caller allocates and
+ *    owns every buffer (including workspace); the library never allocates, frees, or keeps a pointer
+ *    after the call returns.
+ *  - `stream` is a hipStream_t passed as void*. Every call only enqueues work on that stream: no
+ *    host/device synchronization, no host read of device data, so calls can be captured in a HIP
+ *    graph. Results are ready when the stream reaches them.
+ *  - Return value: MOESQ_OK (0) or a negative status. Host-side argument validation happens before
+ *    anything is enqueued; on error nothing is launched. Conditions that only the device can see
+ *    (bad expert ids, invalid mask nibbles) are written to an optional device status word.
+ *  - Tensors are row-major and densely packed unless a leading dimension is given.
+ *  - FP4 codes: E2M1, sign in bit 3, magnitude index in bits 0..2 of the grid
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}; two codes per byte, the lower K index in the low nibble.
+ *    Block scales: UE4M3 codes (E4M3 with bias 7, largest value 448), one per 32 consecutive K.
+ *    Tensor scales: fp32 gamma of Eq. 5; a dequantized value is e2m1 * e4m3 / gamma.
+ *  - Thread safety: stateless; calls on different streams may run concurrently.
+ */
+#ifndef MOESQ_H
+#define MOESQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------------- */
+#define MOESQ_OK 0
+#define MOESQ_ERR_INVALID_ARG -1 /* null pointer, non-positive size, K % 32 != 0, k > E, ... */
+#define MOESQ_ERR_UNSUPPORTED -2 /* valid but not handled by the kernels (e.g. K % 256 != 0)     */
+#define MOESQ_ERR_WORKSPACE -3   /* workspace pointer missing or smaller than required           */
+#define MOESQ_ERR_PATTERN -4     /* (device status) chunk with > 2 nonzero bytes, or mask nibble  */
+                                 /* whose popcount is not 2                                       */
+#define MOESQ_ERR_HIP -5         /* a kernel launch failed (hipGetLastError)                      */
+
+/* ---- dtypes ------------------------------------------------------------------------------------ */
+#define MOESQ_F32 0
+#define MOESQ_BF16 1
+
+/* ---- flags ------------------------------------------------------------------------------------ */
+#define MOESQ_F_DUMP_GATEUP 1u   /* moesq_expert_mlp: also write the fp32 gate_up outputs (after alpha)
+                                    to the workspace region described at moesq_expert_mlp */
+#define MOESQ_F_FORCE_DECODE 2u  /* moesq_grouped_gemm: use the weight-streaming (decode) kernel */
+#define MOESQ_F_FORCE_PREFILL 4u /* moesq_grouped_gemm: use the tiled (prefill) kernel; without either
+                                    flag the kernel is chosen from rows / E (<= 16: decode) */
+
+/* ---- workspace query kinds --------------------------------------------------------------------- */
+#define MOESQ_WS_ROUTE 1
+#define MOESQ_WS_MLP 2
+#define MOESQ_WS_MLP_DUMP 3
+#define MOESQ_WS_COMPRESS 4
+
+/*
+ * Compressed weights of one projection for E experts, pair-bitmask v1 layout (model card, "Sparse
+ * storage layout"): per expert e a row-major [N][K] weight W_e (N = output features, K = contraction)
+ * stored as
+ *   packed [E][N][K/4]  the two kept dense-NVFP4 bytes of every 4-byte chunk, in K order
+ *                       (one byte = one adjacent pair of E2M1 codes)
+ *   mask   [E][N][K/16] 4 bits per chunk, bit i = byte i kept, exactly two bits set,
+ *                       low nibble = lower-K chunk
+ *   scale  [E][N][K/32] UE4M3 block-scale codes
+ *   gscale [E]          fp32 tensor scale gamma_w,e of Eq. 5
+ * The struct itself lives in host memory; its pointers are device pointers read during the call.
+ */
+typedef struct {
+  int32_t E, N, K;
+  const uint8_t *packed;
+  const uint8_t *mask;
+  const uint8_t *scale;
+  const float *gscale;
+} moesq_weights;
+
+/*
+ * Routing / dispatch planning (paper Appendix D.1: token counts stay on the device; the persistent
+ * scheduler reads them there). Per-expert histogram of topk_ids, exclusive prefix scan, and a
+ * stable scatter of the flat slots f = t*k + j into expert-sorted order.
+ *   topk_ids    [T][k] int32 expert ids in [0, E)
+ *   counts      [E]    tokens routed to each expert
+ *   offsets     [E+1]  exclusive prefix sum of counts (offsets[E] = number of placed slots)
+ *   sorted_slot [T*k]  permuted row p holds slot sorted_slot[p]; slots of one expert keep
+ *                      ascending f (stable)
+ *   slot_pos    [T*k]  inverse: slot f sits at permuted row slot_pos[f]; -1 for an invalid id
+ * Ids outside [0, E) are dropped (not counted, slot_pos = -1) and, if dev_status is not NULL,
+ * MOESQ_ERR_INVALID_ARG is written to *dev_status (which the caller zero-initializes).
+ * Workspace: moesq_workspace_bytes(MOESQ_WS_ROUTE, T, k, E, 0, 0, 0) bytes (may be 0).
+ * Limits: E <= 512, T*k < 2^31.
+ */
+int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                        int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
+                        void *workspace, size_t workspace_bytes, int32_t *dev_status);
+
+/*
+ * Dynamic NVFP4 activation quantization (paper Section 3.4 and Appendix D.1: activations are
+ * quantized at run time into 32-element blocks; Eq. 3 + Eq. 5 with the given tensor scale), fused
+ * with token dispatch: permuted row p reads token row gather_slot[p] / k of x.
+ *   x           [T][ld_x] fp32 or bf16 (x_dtype), K <= ld_x, K % 32 == 0
+ *   gather_slot [rows] or NULL. NULL: rows must equal T and row p reads x row p.
+ *   gamma       [G] fp32 tensor scales. With offsets != NULL, row p uses gamma[e] where
+ *               offsets[e] <= p < offsets[e+1] (G = E, the per-expert input scale of the model
+ *               card); with offsets == NULL every row uses gamma[0].
+ *   q           [rows][K/2] E2M1 codes, s [rows][K/32] UE4M3 codes.
+ * Per 32-block b of a row: amax = max |x|; code = E4M3(fp32(fp32(gamma*amax)/6)) rounded to
+ * nearest even, saturating at 448; s = E4M3value/gamma; q = E2M1(x/s) (nearest, ties to the even
+ * code, +0 for zero); q = 0 when s == 0. All in IEEE fp32 without fused multiply-add.
+ */
+int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
+                       const int32_t *gather_slot, int32_t k, int64_t rows, const float *gamma,
+                       const int32_t *offsets, int32_t E, uint8_t *q, uint8_t *s);
+
+/*
+ * Grouped sparse GEMM (paper Section 2: Y_e = X_e W_e^T in one launch for variable per-expert token
+ * counts; Section 3.4: sparse operand W on the left, Y_e^T = W_e X_e^T; block scales applied in the
+ * product, alpha_e = 1/(gamma_w,e * gamma_a,e) applied to the fp32 accumulator).
+ *   q, s        [rows][K/2], [rows][K/32] quantized activations in expert-sorted order
+ *   gamma_a     [E] activation tensor scale of each expert
+ *   offsets     [E+1] from moesq_route_permute (device)
+ *   y           [rows][N] fp32 or bf16 (round to nearest even). Rows >= offsets[E] are not written.
+ * Requires K % 256 == 0 and N % 64 == 0 (MOESQ_ERR_UNSUPPORTED otherwise); E <= 4096.
+ */
+int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s,
+                       const float *gamma_a, const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype,
+                       uint32_t flags);
+
+/*
+ * Routed-expert MLP (paper Appendix D.1 serving integration: the two grouped GEMMs with SwiGLU and
+ * requantization fused into the first GEMM's epilogue):
+ *   gate_up:  W13 with N = 2I: rows [0, I) are the gate projection, rows [I, 2I) the up projection
+ *   h = SiLU(alpha*g) * (alpha*u) in fp32, SiLU(v) = v / (1 + exp(-v))
+ *   requant:  h quantized like moesq_quantize_act with gamma_h[e], 32-blocks along I
+ *   down:     W2 with N = H, K = I, alpha = 1/(gamma_w2,e * gamma_h,e) -> y [rows][H]
+ * Workspace: moesq_workspace_bytes(MOESQ_WS_MLP, ..., rows, k=0, E, K=H, N=0, I) bytes; it holds
+ *   h_q [rows][I/2] at offset 0 and h_s [rows][I/32] right after. With MOESQ_F_DUMP_GATEUP the size
+ *   is moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and the fp32 gate_up outputs [rows][2I] follow
+ *   h_s at the next 256-byte boundary.
+ * Requires H % 256 == 0, I % 256 == 0.
+ */
+int moesq_expert_mlp(void *stream, const moesq_weights *W13, const moesq_weights *W2, const uint8_t *q,
+                     const uint8_t *s, const float *gamma_a, const float *gamma_h, const int32_t *offsets,
+                     int64_t rows, void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                     uint32_t flags);
+
+/*
+ * Router-weighted unpermute + combine (paper Appendix D.1, token combination):
+ *   out[t][c] = sum over j = 0..k-1 (in that order, fp32) of topk_w[t][j] * y_sorted[slot_pos[t*k+j]][c]
+ * Slots with slot_pos = -1 contribute nothing. out is fp32 or bf16 (round to nearest even).
+ *   y_sorted [T*k][H] (y_dtype), slot_pos [T*k], topk_w [T][k] fp32, out [T][H]. Requires H % 8 == 0.
+ */
+int moesq_unpermute_combine(void *stream, const void *y_sorted, int32_t y_dtype, const int32_t *slot_pos,
+                            const float *topk_w, int64_t T, int32_t k, int32_t H, void *out, int32_t out_dtype);
+
+/* ---- setup and parity calls (not on the timed path) ----------------------------------------------
+ *
+ * Weight compression (setup; paper Section 3.4 last paragraph, Appendix A): per 8-group keep the
+ * two adjacent pairs with the largest L2 norm (norms in fp64, ties to the lower pair), compute
+ * gamma_w,e from the pruned expert tensor (Eq. 5), quantize 32-blocks along K like
+ * moesq_quantize_act, and store the dense NVFP4 bytes as pair-bitmask v1 (a chunk with fewer than
+ * two nonzero bytes marks its lowest-index zero bytes as kept).
+ *   w [E][N][K] fp32; outputs as in moesq_weights (gscale is writable here).
+ * Workspace: moesq_workspace_bytes(MOESQ_WS_COMPRESS, 0, 0, E, 0, 0, 0) bytes.
+ * dev_status (optional, caller zero-initializes) receives MOESQ_ERR_PATTERN if a chunk has more
+ * than two nonzero bytes (cannot happen after pruning; reported, not silently packed).
+ */
+int moesq_compress_weights(void *stream, const float *w, int32_t E, int32_t N, int32_t K, uint8_t *packed,
+                           uint8_t *mask, uint8_t *scale, float *gscale, void *workspace,
+                           size_t workspace_bytes, int32_t *dev_status);
+
+/*
+ * Pair-bitmask v1 -> dense NVFP4 bytes [E][N][K/2] (the lossless round trip of the model card).
+ * dev_status (optional) receives MOESQ_ERR_PATTERN for a mask nibble whose popcount is not 2.
+ */
+int moesq_unpack_weights(void *stream, const moesq_weights *W, uint8_t *dense_nvfp4, int32_t *dev_status);
+
+/*
+ * Workspace size in bytes for a call kind (MOESQ_WS_*). Arguments not used by a kind are ignored:
+ *   ROUTE: T, k, E.   MLP / MLP_DUMP: T = rows, E, K = H, I.   COMPRESS: E.
+ */
+size_t moesq_workspace_bytes(int32_t kind, int64_t T, int32_t k, int32_t E, int32_t K, int32_t N, int32_t I);
+
+/* Human-readable text for a status code (static storage). */
+const char *moesq_status_str(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t moesq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOESQ_H */

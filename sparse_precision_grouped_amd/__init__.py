@@ -1,0 +1,255 @@
+"""Python binding of libmoesq.so: the MoE expert path over paired-4:8 sparse NVFP4 weights on
+MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch supplies device
+memory and the current stream. The functions keep the C ABI names (``include/moesq.h``); outputs
+that are not passed in are allocated with ``torch.empty`` on the current device.
+
+There is no CPU fallback: if ``libmoesq.so`` is missing, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm",
+    "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
+    "moesq_workspace_bytes", "moesq_status_str", "moesq_version",
+    "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL",
+    "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoesq.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_PATTERN, ERR_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL = 1, 2, 4
+WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS = 1, 2, 3, 4
+
+
+class MoesqError(RuntimeError):
+    def __init__(self, call, status):
+        super().__init__("%s failed: %s (%d)" % (call, moesq_status_str(status), status))
+        self.status = status
+
+
+class _CWeights(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoesq.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        W = ctypes.POINTER(_CWeights)
+        L.moesq_route_permute.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moesq_quantize_act.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp]
+        L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, i64, vp, i32, u32]
+        L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
+        L.moesq_unpermute_combine.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
+        L.moesq_compress_weights.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moesq_unpack_weights.argtypes = [vp, W, vp, vp]
+        L.moesq_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+        L.moesq_workspace_bytes.restype = sz
+        L.moesq_status_str.argtypes = [i32]
+        L.moesq_status_str.restype = ctypes.c_char_p
+        L.moesq_version.restype = i32
+        for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm", "moesq_expert_mlp",
+                     "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def moesq_status_str(status):
+    return lib().moesq_status_str(int(status)).decode()
+
+
+def moesq_version():
+    return lib().moesq_version()
+
+
+def moesq_workspace_bytes(kind, T=0, k=0, E=0, K=0, N=0, I=0):
+    return int(lib().moesq_workspace_bytes(kind, T, k, E, K, N, I))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(call, rc):
+    if rc != OK:
+        raise MoesqError(call, rc)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise ValueError("unsupported dtype %s" % dt)
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t
+
+
+class Weights:
+    """Pair-bitmask v1 weights of one projection for E experts (device tensors):
+    packed [E,N,K/4] u8, mask [E,N,K/16] u8, scale [E,N,K/32] u8 (UE4M3), gscale [E] f32."""
+
+    def __init__(self, packed, mask, scale, gscale):
+        E, N, K4 = packed.shape
+        self.E, self.N, self.K = E, N, K4 * 4
+        assert mask.shape == (E, N, self.K // 16) and scale.shape == (E, N, self.K // 32) and gscale.shape == (E,)
+        for t in (packed, mask, scale):
+            assert t.dtype == torch.uint8 and t.is_contiguous()
+        assert gscale.dtype == torch.float32
+        self.packed, self.mask, self.scale, self.gscale = packed, mask, scale, gscale
+
+    @classmethod
+    def empty(cls, E, N, K, device="cuda"):
+        u8 = torch.uint8
+        return cls(torch.empty((E, N, K // 4), dtype=u8, device=device),
+                   torch.empty((E, N, K // 16), dtype=u8, device=device),
+                   torch.empty((E, N, K // 32), dtype=u8, device=device),
+                   torch.empty((E,), dtype=torch.float32, device=device))
+
+    def cstruct(self):
+        return _CWeights(self.E, self.N, self.K, self.packed.data_ptr(), self.mask.data_ptr(),
+                         self.scale.data_ptr(), self.gscale.data_ptr())
+
+    def nbytes(self):
+        return self.packed.numel() + self.mask.numel() + self.scale.numel()
+
+
+def moesq_route_permute(topk_ids, E, counts=None, offsets=None, sorted_slot=None, slot_pos=None,
+                        workspace=None, dev_status=None):
+    """Histogram + scan + stable scatter of topk_ids [T, k] (int32). Returns a dict of device tensors."""
+    _dev(topk_ids)
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    i32 = torch.int32
+    counts = torch.empty(E, dtype=i32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=i32, device=dev) if offsets is None else offsets
+    sorted_slot = torch.empty(T * k, dtype=i32, device=dev) if sorted_slot is None else sorted_slot
+    slot_pos = torch.empty(T * k, dtype=i32, device=dev) if slot_pos is None else slot_pos
+    need = moesq_workspace_bytes(WS_ROUTE, T, k, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("moesq_route_permute",
+           lib().moesq_route_permute(_stream(), _p(topk_ids), T, k, E, _p(counts), _p(offsets), _p(sorted_slot),
+                                     _p(slot_pos), _p(workspace), wsb, _p(dev_status)))
+    return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos)
+
+
+def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=None, rows=None):
+    """NVFP4-quantize rows of x [T, K] (fp32/bf16). With gather_slot, permuted row p reads token
+    gather_slot[p] // k and (with offsets) uses gamma[expert of p]. Returns (q [rows,K/2], s [rows,K/32])."""
+    _dev(x)
+    T, K = x.shape
+    assert x.stride(1) == 1
+    if rows is None:
+        rows = T if gather_slot is None else gather_slot.numel()
+    E = 0 if offsets is None else offsets.numel() - 1
+    q = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
+    _check("moesq_quantize_act",
+           lib().moesq_quantize_act(_stream(), _p(x), _dtype_code(x.dtype), T, K, x.stride(0), _p(gather_slot), k,
+                                    rows, _p(gamma), _p(offsets), E, _p(q), _p(s)))
+    return q, s
+
+
+def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0):
+    rows = q.shape[0]
+    if y is None:
+        y = torch.empty((rows, W.N), dtype=y_dtype, device=q.device)
+    c = W.cstruct()
+    _check("moesq_grouped_gemm",
+           lib().moesq_grouped_gemm(_stream(), ctypes.byref(c), _p(q), _p(s), _p(gamma_a), _p(offsets), rows, _p(y),
+                                    _dtype_code(y.dtype), flags))
+    return y
+
+
+def mlp_workspace(rows, I, dump=False, device="cuda"):
+    nb = moesq_workspace_bytes(WS_MLP_DUMP if dump else WS_MLP, rows, 0, 0, 0, 0, I)
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+
+
+def mlp_workspace_views(ws, rows, I, dump=False):
+    """(h_q [rows, I/2], h_s [rows, I/32], gate_up fp32 [rows, 2I] or None) inside an MLP workspace."""
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    hq = ws[:rows * (I // 2)].view(rows, I // 2)
+    o = a(rows * (I // 2))
+    hs = ws[o:o + rows * (I // 32)].view(rows, I // 32)
+    o += a(rows * (I // 32))
+    d = ws[o:o + rows * 2 * I * 4].view(torch.float32).view(rows, 2 * I) if dump else None
+    return hq, hs, d
+
+
+def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=torch.bfloat16, workspace=None,
+                     flags=0):
+    rows = q.shape[0]
+    I = W13.N // 2
+    if y is None:
+        y = torch.empty((rows, W2.N), dtype=y_dtype, device=q.device)
+    if workspace is None:
+        workspace = mlp_workspace(rows, I, bool(flags & F_DUMP_GATEUP), q.device)
+    a, b = W13.cstruct(), W2.cstruct()
+    _check("moesq_expert_mlp",
+           lib().moesq_expert_mlp(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(gamma_a),
+                                  _p(gamma_h), _p(offsets), rows, _p(y), _dtype_code(y.dtype), _p(workspace),
+                                  workspace.numel(), flags))
+    return y, workspace
+
+
+def moesq_unpermute_combine(y_sorted, slot_pos, topk_w, out=None, out_dtype=torch.bfloat16):
+    T, k = topk_w.shape
+    H = y_sorted.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_sorted.device)
+    _check("moesq_unpermute_combine",
+           lib().moesq_unpermute_combine(_stream(), _p(y_sorted), _dtype_code(y_sorted.dtype), _p(slot_pos),
+                                         _p(topk_w), T, k, H, _p(out), _dtype_code(out.dtype)))
+    return out
+
+
+def moesq_compress_weights(w, out=None, workspace=None, dev_status=None):
+    """fp32 weights [E, N, K] -> Weights (paired-4:8 pruning + NVFP4 + pair-bitmask v1)."""
+    _dev(w)
+    assert w.dtype == torch.float32 and w.is_contiguous()
+    E, N, K = w.shape
+    out = Weights.empty(E, N, K, w.device) if out is None else out
+    need = moesq_workspace_bytes(WS_COMPRESS, 0, 0, E)
+    workspace = torch.empty(need, dtype=torch.uint8, device=w.device) if workspace is None else workspace
+    _check("moesq_compress_weights",
+           lib().moesq_compress_weights(_stream(), _p(w), E, N, K, _p(out.packed), _p(out.mask), _p(out.scale),
+                                        _p(out.gscale), _p(workspace), workspace.numel(), _p(dev_status)))
+    return out
+
+
+def moesq_unpack_weights(W, dense=None, dev_status=None):
+    if dense is None:
+        dense = torch.empty((W.E, W.N, W.K // 2), dtype=torch.uint8, device=W.packed.device)
+    c = W.cstruct()
+    _check("moesq_unpack_weights", lib().moesq_unpack_weights(_stream(), ctypes.byref(c), _p(dense), _p(dev_status)))
+    return dense

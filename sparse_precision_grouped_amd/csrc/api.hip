@@ -1,0 +1,177 @@
+// C ABI of libmoesq.so: argument validation on the host, then kernel launches on the caller's
+// stream. No allocation, no synchronization, no host read of device data.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "launch.h"
+
+using namespace moesq;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool weights_ok(const moesq_weights* W) {
+  return W && W->E > 0 && W->N > 0 && W->K > 0 && W->packed && W->mask && W->scale && W->gscale;
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t mlp_ws(int64_t rows, int32_t I, bool dump) {
+  size_t b = align256((size_t)rows * (I / 2)) + align256((size_t)rows * (I / 32));
+  if (dump) b += (size_t)rows * 2 * I * sizeof(float);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moesq_version(void) { return 100; }
+
+const char* moesq_status_str(int32_t status) {
+  switch (status) {
+    case MOESQ_OK: return "ok";
+    case MOESQ_ERR_INVALID_ARG: return "invalid argument";
+    case MOESQ_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOESQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOESQ_ERR_PATTERN: return "invalid paired-4:8 pattern";
+    case MOESQ_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t moesq_workspace_bytes(int32_t kind, int64_t T, int32_t k, int32_t E, int32_t K, int32_t N, int32_t I) {
+  (void)K;
+  (void)N;
+  switch (kind) {
+    case MOESQ_WS_ROUTE: return (T > 0 && k > 0 && E > 0) ? route_workspace_bytes(T * k, E) : 0;
+    case MOESQ_WS_MLP: return T >= 0 && I > 0 ? mlp_ws(T, I, false) : 0;
+    case MOESQ_WS_MLP_DUMP: return T >= 0 && I > 0 ? mlp_ws(T, I, true) : 0;
+    case MOESQ_WS_COMPRESS: return E > 0 ? (size_t)E * sizeof(uint32_t) : 0;
+    default: return 0;
+  }
+}
+
+int moesq_route_permute(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* workspace,
+                        size_t workspace_bytes, int32_t* dev_status) {
+  if (T < 0 || k <= 0 || E <= 0 || k > E) return MOESQ_ERR_INVALID_ARG;
+  if (!counts || !offsets) return MOESQ_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !sorted_slot || !slot_pos)) return MOESQ_ERR_INVALID_ARG;
+  if (E > kMaxExpertsRoute) return MOESQ_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  const size_t need = route_workspace_bytes(T * k, E);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return MOESQ_ERR_WORKSPACE;
+  return launch_route((hipStream_t)stream, topk_ids, T * k, E, counts, offsets, sorted_slot, slot_pos, workspace,
+                      dev_status);
+}
+
+int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
+                       const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
+                       int32_t E, uint8_t* q, uint8_t* s) {
+  if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  if (T < 0 || rows < 0 || K <= 0 || K % 32 != 0 || ld_x < K) return MOESQ_ERR_INVALID_ARG;
+  if (!gamma) return MOESQ_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !q || !s)) return MOESQ_ERR_INVALID_ARG;
+  if (gather_slot) {
+    if (k <= 0) return MOESQ_ERR_INVALID_ARG;
+  } else if (rows != T) {
+    return MOESQ_ERR_INVALID_ARG;
+  }
+  if (offsets && E <= 0) return MOESQ_ERR_INVALID_ARG;
+  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, gather_slot, k, rows, gamma,
+                         offsets, E, q, s);
+}
+
+static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* s, const float* gamma_a,
+                       const int32_t* offsets, int64_t rows, void* y) {
+  if (!weights_ok(W) || rows < 0 || !gamma_a || !offsets) return MOESQ_ERR_INVALID_ARG;
+  if (rows > 0 && (!q || !s || !y)) return MOESQ_ERR_INVALID_ARG;
+  if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
+  if (W->K % 256 != 0 || W->N % 64 != 0 || W->E > kMaxExpertsGemm) return MOESQ_ERR_UNSUPPORTED;
+  if (!aligned(W->packed, 16) || !aligned(W->mask, 4) || !aligned(W->scale, 2) || !aligned(q, 16) ||
+      !aligned(s, 2) || !aligned(y, 16))
+    return MOESQ_ERR_UNSUPPORTED;
+  if (rows >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  return MOESQ_OK;
+}
+
+int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, const uint8_t* s, const float* gamma_a,
+                       const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype, uint32_t flags) {
+  if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  const int rc = gemm_common(W, q, s, gamma_a, offsets, rows, y);
+  if (rc != MOESQ_OK) return rc;
+  GemmArgs a{};
+  a.packed = W->packed; a.mask = W->mask; a.wscale = W->scale; a.gscale = W->gscale;
+  a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
+  a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
+  if (flags & MOESQ_F_FORCE_DECODE) return launch_gemm_variant((hipStream_t)stream, a, rows, 0);
+  if (flags & MOESQ_F_FORCE_PREFILL) return launch_gemm_variant((hipStream_t)stream, a, rows, 1);
+  return launch_gemm((hipStream_t)stream, a, rows);
+}
+
+int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights* W2, const uint8_t* q,
+                     const uint8_t* s, const float* gamma_a, const float* gamma_h, const int32_t* offsets, int64_t rows,
+                     void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes, uint32_t flags) {
+  if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  if (!weights_ok(W13) || !weights_ok(W2) || !gamma_h) return MOESQ_ERR_INVALID_ARG;
+  const int32_t I = W13->N / 2;
+  if (W13->N % 2 != 0 || W2->K != I || W2->E != W13->E) return MOESQ_ERR_INVALID_ARG;
+  int rc = gemm_common(W13, q, s, gamma_a, offsets, rows, y);
+  if (rc != MOESQ_OK) return rc;
+  if (I % 256 != 0 || W13->K % 256 != 0 || W2->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
+  if (!aligned(W2->packed, 16) || !aligned(W2->mask, 4) || !aligned(W2->scale, 2)) return MOESQ_ERR_UNSUPPORTED;
+  const bool dump = (flags & MOESQ_F_DUMP_GATEUP) != 0;
+  const size_t need = mlp_ws(rows, I, dump);
+  if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MOESQ_ERR_WORKSPACE;
+  if (rows == 0) return MOESQ_OK;
+  uint8_t* hq = (uint8_t*)workspace;
+  uint8_t* hs = hq + align256((size_t)rows * (I / 2));
+  float* dumpp = dump ? (float*)(hs + align256((size_t)rows * (I / 32))) : nullptr;
+  GemmArgs a{};
+  a.packed = W13->packed; a.mask = W13->mask; a.wscale = W13->scale; a.gscale = W13->gscale;
+  a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
+  a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0;
+  a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.dump = dumpp;
+  rc = launch_gemm_variant((hipStream_t)stream, a, rows, 1);
+  if (rc != MOESQ_OK) return rc;
+  GemmArgs b{};
+  b.packed = W2->packed; b.mask = W2->mask; b.wscale = W2->scale; b.gscale = W2->gscale;
+  b.q = hq; b.s = hs; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
+  b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16;
+  return launch_gemm_variant((hipStream_t)stream, b, rows, 1);
+}
+
+int moesq_unpermute_combine(void* stream, const void* y_sorted, int32_t y_dtype, const int32_t* slot_pos,
+                            const float* topk_w, int64_t T, int32_t k, int32_t H, void* out, int32_t out_dtype) {
+  if ((y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) || (out_dtype != MOESQ_F32 && out_dtype != MOESQ_BF16))
+    return MOESQ_ERR_INVALID_ARG;
+  if (T < 0 || k <= 0 || H <= 0) return MOESQ_ERR_INVALID_ARG;
+  if (T > 0 && (!y_sorted || !slot_pos || !topk_w || !out)) return MOESQ_ERR_INVALID_ARG;
+  if (H % 8 != 0 || !aligned(y_sorted, 16) || !aligned(out, 16)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_combine((hipStream_t)stream, y_sorted, y_dtype == MOESQ_BF16, slot_pos, topk_w, T, k, H, out,
+                        out_dtype == MOESQ_BF16);
+}
+
+int moesq_compress_weights(void* stream, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed,
+                           uint8_t* mask, uint8_t* scale, float* gscale, void* workspace, size_t workspace_bytes,
+                           int32_t* dev_status) {
+  if (E <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
+  if (!w || !packed || !mask || !scale || !gscale) return MOESQ_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < (size_t)E * sizeof(uint32_t) || !aligned(workspace, 4))
+    return MOESQ_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(packed, 8) || !aligned(mask, 2)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_compress((hipStream_t)stream, w, E, N, K, packed, mask, scale, gscale, workspace, dev_status);
+}
+
+int moesq_unpack_weights(void* stream, const moesq_weights* W, uint8_t* dense_nvfp4, int32_t* dev_status) {
+  if (!W || W->E <= 0 || W->N <= 0 || W->K <= 0 || W->K % 32 != 0 || !W->packed || !W->mask || !dense_nvfp4)
+    return MOESQ_ERR_INVALID_ARG;
+  if (!aligned(dense_nvfp4, 4)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_unpack((hipStream_t)stream, W->packed, W->mask, W->E, W->N, W->K, dense_nvfp4, dev_status);
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Host-side launchers of the kernels (one per translation unit) and shared limits.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moesq.h"
+
+namespace moesq {
+
+constexpr int64_t kRouteSingleMax = 8192;  // slots handled by the one-workgroup routing path
+constexpr int32_t kMaxExpertsRoute = 512;
+constexpr int32_t kMaxExpertsGemm = 4096;
+
+struct GemmArgs {
+  const uint8_t* packed;  // [E][N][K/4]
+  const uint8_t* mask;    // [E][N][K/16]
+  const uint8_t* wscale;  // [E][N][K/32]
+  const float* gscale;    // [E]
+  const uint8_t* q;       // [rows][K/2]
+  const uint8_t* s;       // [rows][K/32]
+  const float* gamma_a;   // [E]
+  const int32_t* offsets; // [E+1]
+  void* y;                // [rows][N] (plain epilogue)
+  int32_t E, N, K;
+  int32_t y_bf16;
+  // MLP gate_up epilogue (N = 2I): SwiGLU + requant into h_q [rows][I/2], h_s [rows][I/32]
+  const float* gamma_h;   // [E] or nullptr for the plain epilogue
+  uint8_t* h_q;
+  uint8_t* h_s;
+  float* dump;            // [rows][N] fp32 gate_up outputs, or nullptr
+};
+
+size_t route_workspace_bytes(int64_t n, int32_t E);
+int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status);
+
+int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
+                    const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
+                    int32_t E, uint8_t* q, uint8_t* s);
+
+int launch_compress(hipStream_t st, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
+                    uint8_t* scale, float* gscale, void* ws, int32_t* dev_status);
+int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, int32_t E, int32_t N, int32_t K,
+                  uint8_t* dense, int32_t* dev_status);
+
+// Grouped GEMM: picks the decode (weight-streaming) or the prefill (tiled) kernel from rows / E.
+int launch_gemm(hipStream_t st, const GemmArgs& a, int64_t rows);
+// variant 0 = decode (weight streaming), 1 = prefill (tiled); the MLP epilogue needs variant 1.
+int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
+
+int launch_combine(hipStream_t st, const void* y, bool y_bf16, const int32_t* slot_pos, const float* w, int64_t T,
+                   int32_t k, int32_t H, void* out, bool out_bf16);
+
+}  // namespace moesq

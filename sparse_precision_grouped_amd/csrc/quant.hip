@@ -1,0 +1,246 @@
+// NVFP4 quantization kernels:
+//  - dispatch + dynamic activation quantization (paper Section 3.4 and Appendix D.1: 32-element
+//    blocks at run time, fused with token dispatch; Eq. 3 + Eq. 5 with the expert's tensor scale);
+//  - weight compression to paired-4:8 NVFP4 in pair-bitmask v1 storage (setup; Section 3.4 last
+//    paragraph, Appendix A; model card "Sparse storage layout");
+//  - pair-bitmask v1 -> dense NVFP4 unpacking (the model card's lossless round trip).
+#include "common.h"
+#include "launch.h"
+
+namespace moesq {
+
+// One wave per permuted row; each lane quantizes 8 consecutive values, four lanes per 32-block
+// (block amax by a 4-lane max reduction across the wave's lanes).
+__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K,
+                                                       int64_t ld_x, const int32_t* __restrict__ gather, int32_t k,
+                                                       int64_t rows, const float* __restrict__ gamma,
+                                                       const int32_t* __restrict__ offsets, int32_t E,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rows) return;
+  int64_t t = p;
+  if (gather) {
+    if (offsets && p >= offsets[E]) return;  // slot dropped by routing (invalid id)
+    t = gather[p] / k;
+    if (t < 0 || t >= T) return;
+  }
+  float g = gamma[0];
+  if (offsets) {
+    int lo = 0, hi = E - 1;  // largest e with offsets[e] <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    g = gamma[lo];
+  }
+  const int nch = K / 8;
+  for (int ch = lane; ch - lane < nch; ch += 64) {
+    const bool valid = ch < nch;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    if (valid) {
+      if (x_bf16) {
+        const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
+          v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
+        const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    }
+    uint32_t codes, sc;
+    quant8_block4(v, g, codes, sc);
+    if (valid) {
+      *(uint32_t*)(q + p * (K / 2) + 4 * ch) = codes;
+      if ((lane & 3) == 0) s[p * (K / 32) + ch / 4] = (uint8_t)sc;
+    }
+  }
+}
+
+int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
+                    const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
+                    int32_t E, uint8_t* q, uint8_t* s) {
+  if (rows == 0) return MOESQ_OK;
+  const int64_t blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x,
+                     gather_slot, k, rows, gamma, offsets, E, q, s);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ weight compression ----------
+// Paired-4:8 pruning of one 8-group in place: keep the two pairs with the largest L2 norm (fp64
+// norms, ties to the lower pair index), zero the other two.
+MOESQ_DEV void prune_group(float v[8]) {
+  double nrm[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const double a = (double)v[2 * i], b = (double)v[2 * i + 1];
+    const double aa = a * a, bb = b * b;
+    nrm[i] = aa + bb;
+  }
+  int first = 0;
+#pragma unroll
+  for (int i = 1; i < 4; i++)
+    if (nrm[i] > nrm[first]) first = i;
+  int second = first == 0 ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (i != first && nrm[i] > nrm[second]) second = i;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    if (i != first && i != second) {
+      v[2 * i] = 0.0f;
+      v[2 * i + 1] = 0.0f;
+    }
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Per expert amax of the pruned weights, as ordered float bits (max of non-negative floats equals
+// max of their bit patterns, so the atomic result does not depend on order).
+__global__ __launch_bounds__(256) void compress_amax_kernel(const float* __restrict__ w, int32_t N, int32_t K,
+                                                            uint32_t* __restrict__ amax_bits) {
+  const int e = blockIdx.y;
+  const int64_t ngroups = (int64_t)N * K / 8;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float m = 0.0f;
+  if (g < ngroups) {
+    const float* src = w + (int64_t)e * N * K + 8 * g;
+    const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    prune_group(v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(&amax_bits[e], __float_as_uint(m));
+}
+
+// One thread per 32-element block of a weight row: prune its four 8-groups, quantize (Eq. 3 + 5
+// with the expert's tensor scale), form dense NVFP4 bytes, and store them as pair-bitmask v1.
+__global__ __launch_bounds__(256) void compress_pack_kernel(const float* __restrict__ w, int32_t N, int32_t K,
+                                                            const uint32_t* __restrict__ amax_bits,
+                                                            uint8_t* __restrict__ packed, uint8_t* __restrict__ mask,
+                                                            uint8_t* __restrict__ scale, float* __restrict__ gscale,
+                                                            int32_t* dev_status) {
+  const int e = blockIdx.y;
+  const int64_t nblocks = (int64_t)N * (K / 32);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float gamma = global_scale_from_amax(__uint_as_float(amax_bits[e]));
+  if (i == 0) gscale[e] = gamma;
+  if (i >= nblocks) return;
+  const float* src = w + (int64_t)e * N * K + 32 * i;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const float4 a = *(const float4*)(src + 4 * j);
+    v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+  }
+#pragma unroll
+  for (int gi = 0; gi < 4; gi++) prune_group(v + 8 * gi);
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; j++) am = __builtin_fmaxf(am, __builtin_fabsf(v[j]));
+  const float t = gamma * am;
+  const float u = t / 6.0f;
+  const uint32_t sc = e4m3_encode(u);
+  const float sv = e4m3_value(sc) / gamma;
+  uint8_t dense[16];
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    uint32_t c0 = 0u, c1 = 0u;
+    if (sv != 0.0f) {
+      c0 = e2m1_encode(v[2 * j] / sv);
+      c1 = e2m1_encode(v[2 * j + 1] / sv);
+    }
+    dense[j] = (uint8_t)(c0 | (c1 << 4));
+  }
+  uint8_t pk[8];
+  uint32_t nibs = 0u;
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    uint32_t nib = 0u, cnt = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      if (dense[4 * c + b] != 0) { nib |= 1u << b; cnt++; }
+    if (cnt > 2u) { bad = true; nib = 0u; cnt = 0u; }
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      if (cnt < 2u && !(nib & (1u << b))) { nib |= 1u << b; cnt++; }
+    int o = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      if (nib & (1u << b)) { pk[2 * c + (o & 1)] = dense[4 * c + b]; o++; }
+    nibs |= nib << (4 * c);
+  }
+  if (bad && dev_status) *dev_status = MOESQ_ERR_PATTERN;
+  const int64_t row = i / (K / 32), b = i % (K / 32);
+  const int64_t rbase = (int64_t)e * N + row;
+  uint2 pw;
+  pw.x = (uint32_t)pk[0] | ((uint32_t)pk[1] << 8) | ((uint32_t)pk[2] << 16) | ((uint32_t)pk[3] << 24);
+  pw.y = (uint32_t)pk[4] | ((uint32_t)pk[5] << 8) | ((uint32_t)pk[6] << 16) | ((uint32_t)pk[7] << 24);
+  *(uint2*)(packed + rbase * (K / 4) + 8 * b) = pw;
+  *(uint16_t*)(mask + rbase * (K / 16) + 2 * b) = (uint16_t)nibs;
+  scale[rbase * (K / 32) + b] = (uint8_t)sc;
+}
+
+int launch_compress(hipStream_t st, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
+                    uint8_t* scale, float* gscale, void* ws, int32_t* dev_status) {
+  uint32_t* amax = (uint32_t*)ws;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((E + 255) / 256), dim3(256), 0, st, amax, E);
+  const int64_t ngroups = (int64_t)N * K / 8;
+  hipLaunchKernelGGL(compress_amax_kernel, dim3((unsigned)((ngroups + 255) / 256), E), dim3(256), 0, st, w, N, K,
+                     amax);
+  const int64_t nblocks = (int64_t)N * (K / 32);
+  hipLaunchKernelGGL(compress_pack_kernel, dim3((unsigned)((nblocks + 255) / 256), E), dim3(256), 0, st, w, N, K,
+                     amax, packed, mask, scale, gscale, dev_status);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ unpack ------------------------
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ packed,
+                                                     const uint8_t* __restrict__ mask, int64_t nchunks,
+                                                     uint8_t* __restrict__ dense, int32_t* dev_status) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const uint32_t mb = mask[c >> 1];
+  const uint32_t nib = (c & 1) ? (mb >> 4) : (mb & 15u);
+  if (__builtin_popcount(nib) != 2 && dev_status) *dev_status = MOESQ_ERR_PATTERN;
+  const uint32_t b0 = packed[2 * c], b1 = packed[2 * c + 1];
+  uint32_t out = 0u;
+  int o = 0;
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    if ((nib & (1u << b)) && o < 2) {
+      out |= (o == 0 ? b0 : b1) << (8 * b);
+      o++;
+    }
+  }
+  *(uint32_t*)(dense + 4 * c) = out;
+}
+
+int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, int32_t E, int32_t N, int32_t K,
+                  uint8_t* dense, int32_t* dev_status) {
+  // Chunks of consecutive rows are contiguous in all three arrays, so the [E][N] rows flatten.
+  const int64_t nchunks = (int64_t)E * N * (K / 8);
+  if (nchunks == 0) return MOESQ_OK;
+  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st, packed, mask, nchunks,
+                     dense, dev_status);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+}  // namespace moesq

@@ -1,0 +1,151 @@
+"""The C-ABI library on the host: it loads, exports every entry point the header declares, and its
+host-side validation rejects bad arguments before anything is launched (no GPU needed: every call
+here returns before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moesq.h")
+LIB = os.path.join(ROOT, "sparse_precision_grouped_amd", "libmoesq.so")
+
+OK, EARG, EUNS, EWS, EPAT, EHIP = 0, -1, -2, -3, -4, -5
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moesq_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoesq.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB)
+    lib.moesq_status_str.restype = ctypes.c_char_p
+    lib.moesq_workspace_bytes.restype = ctypes.c_size_t
+    lib.moesq_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    return lib
+
+
+def test_header_declares_the_five_calls_and_setup():
+    names = _declared()
+    for n in ["moesq_quantize_act", "moesq_route_permute", "moesq_grouped_gemm", "moesq_expert_mlp",
+              "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
+              "moesq_workspace_bytes", "moesq_status_str", "moesq_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (OK, EARG, EUNS, EWS, EPAT, EHIP):
+        assert L.moesq_status_str(code)
+    assert L.moesq_version() >= 100
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def test_route_validation(L):
+    i64, i32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    f = L.moesq_route_permute
+    f.argtypes = [ctypes.c_void_p] * 2 + [i64, i32, i32] + [ctypes.c_void_p] * 5 + [sz, ctypes.c_void_p]
+    args = lambda T=4, k=2, E=8, ids=FAKE, cnt=FAKE: (None, _p(ids), T, k, E, _p(cnt), _p(FAKE), _p(FAKE),  # noqa
+                                                      _p(FAKE), None, 0, None)
+    assert f(*args(k=9)) == EARG          # k > E
+    assert f(*args(k=0)) == EARG
+    assert f(*args(E=0)) == EARG
+    assert f(*args(ids=0)) == EARG        # null ids
+    assert f(*args(cnt=0)) == EARG
+    assert f(*args(E=513)) == EUNS        # beyond the routing limit
+    # multi-block path needs a workspace
+    assert L.moesq_workspace_bytes(1, 65536, 8, 384, 0, 0, 0) > 0
+    assert f(*args(T=65536, k=8, E=384)) == EWS
+    assert L.moesq_workspace_bytes(1, 16, 8, 128, 0, 0, 0) == 0   # one-workgroup path
+
+
+def test_quantize_validation(L):
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    f = L.moesq_quantize_act
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp]
+    base = dict(x=FAKE, dt=0, T=8, K=64, ld=64, g=None, k=1, rows=8, gamma=FAKE, off=None, E=0, q=FAKE, s=FAKE)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(None, _p(a["x"]), a["dt"], a["T"], a["K"], a["ld"], _p(a["g"]) if a["g"] else None, a["k"],
+                 a["rows"], _p(a["gamma"]) if a["gamma"] else None, _p(a["off"]) if a["off"] else None, a["E"],
+                 _p(a["q"]), _p(a["s"]))
+    assert call(K=48, ld=48) == EARG      # K % 32 != 0
+    assert call(dt=7) == EARG             # dtype
+    assert call(ld=32) == EARG            # ld_x < K
+    assert call(gamma=0) == EARG
+    assert call(rows=9) == EARG           # no gather: rows must equal T
+    assert call(x=FAKE + 4) == EUNS       # misaligned x
+
+
+def test_gemm_and_mlp_validation(L):
+    class CW(ctypes.Structure):
+        _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                    ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                    ("gscale", ctypes.c_void_p)]
+    vp = ctypes.c_void_p
+    g = L.moesq_grouped_gemm
+    g.argtypes = [vp, ctypes.POINTER(CW), vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, ctypes.c_uint32]
+    W = CW(4, 128, 256, FAKE, FAKE, FAKE, FAKE)
+    call = lambda W, y=FAKE, dt=0: g(None, ctypes.byref(W), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(y),  # noqa
+                                     dt, 0)
+    assert call(W, dt=3) == EARG
+    assert call(W, y=0) == EARG
+    assert call(CW(4, 128, 240, FAKE, FAKE, FAKE, FAKE)) == EARG     # K % 32 != 0
+    assert call(CW(4, 128, 96, FAKE, FAKE, FAKE, FAKE)) == EUNS      # K % 256 != 0
+    assert call(CW(4, 100, 256, FAKE, FAKE, FAKE, FAKE)) == EUNS     # N % 64 != 0
+    assert call(CW(4, 128, 256, 0, FAKE, FAKE, FAKE)) == EARG        # null packed
+    m = L.moesq_expert_mlp
+    m.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+                  ctypes.c_int32, vp, ctypes.c_size_t, ctypes.c_uint32]
+    W13 = CW(4, 512, 256, FAKE, FAKE, FAKE, FAKE)
+    W2 = CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE)
+    mc = lambda a, b, ws=FAKE, wsb=1 << 30: m(None, ctypes.byref(a), ctypes.byref(b), _p(FAKE), _p(FAKE),  # noqa
+                                             _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(FAKE), 0,
+                                             _p(ws) if ws else None, wsb, 0)
+    assert mc(W13, CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE)) == EARG   # W2.K != I
+    assert mc(W13, CW(3, 256, 256, FAKE, FAKE, FAKE, FAKE)) == EARG   # expert count mismatch
+    assert mc(W13, W2, ws=0) == EWS
+    assert mc(W13, W2, wsb=10) == EWS
+    assert mc(CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE), CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE)) == EUNS  # I = 128
+
+
+def test_combine_compress_unpack_validation(L):
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    c = L.moesq_unpermute_combine
+    c.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
+    assert c(None, _p(FAKE), 0, _p(FAKE), _p(FAKE), 4, 0, 64, _p(FAKE), 0) == EARG   # k = 0
+    assert c(None, _p(FAKE), 0, _p(FAKE), _p(FAKE), 4, 2, 60, _p(FAKE), 0) == EUNS   # H % 8
+    assert c(None, _p(FAKE), 5, _p(FAKE), _p(FAKE), 4, 2, 64, _p(FAKE), 0) == EARG
+    k = L.moesq_compress_weights
+    k.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    assert k(None, _p(FAKE), 2, 8, 48, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 64, None) == EARG
+    assert k(None, _p(FAKE), 2, 8, 64, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), None, 64, None) == EWS
+    assert k(None, _p(FAKE), 2, 8, 64, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 4, None) == EWS
+
+
+def test_workspace_sizes(L):
+    ws = lambda kind, T=0, k=0, E=0, K=0, N=0, I=0: L.moesq_workspace_bytes(kind, T, k, E, K, N, I)  # noqa
+    a = lambda x: (x + 255) // 256 * 256  # noqa
+    rows, I = 1000, 2048
+    assert ws(2, rows, 0, 384, 7168, 0, I) == a(rows * I // 2) + a(rows * I // 32)
+    assert ws(3, rows, 0, 384, 7168, 0, I) == a(rows * I // 2) + a(rows * I // 32) + rows * 2 * I * 4
+    assert ws(4, E=384) == 384 * 4

@@ -1,0 +1,274 @@
+"""GPU parity of every step of the path against the CPU oracle, through the C ABI binding.
+
+Bars: bit-exact for packing, permutation, quantized codes and scales; rel-Frobenius <= 1e-3 for
+fp32 GEMM outputs against the fp64 oracle on identical operands; bf16 outputs against the oracle
+rounded to bf16 (the only difference is fp32 accumulation order, far below 1e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as orc
+
+from gpu_cases import DEV, dev, host, say, sample_rows, single_case
+
+pytestmark = pytest.mark.gpu
+
+mq = pytest.importorskip("sparse_precision_grouped_amd")
+
+GEMM_TOL = 1e-3
+
+
+def bf16_round(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- generator ------------------
+def test_gen_device_bitexact():
+    say("gen device vs host")
+    n = 1 << 20
+    out = torch.empty(n, dtype=torch.float32, device=DEV)
+    gen.gpu_fill_normal(out, 99, gen.weight_stream(0, 3), 0.02, start=12345)
+    assert np.array_equal(host(out), gen.normal(99, gen.weight_stream(0, 3), n, 0.02, start=12345))
+    out2 = torch.empty(1 << 16, dtype=torch.float32, device=DEV)
+    gen.gpu_fill_student_t(out2, 7, gen.act_stream(1), 4)
+    assert np.array_equal(host(out2), gen.student_t(7, gen.act_stream(1), 1 << 16, 4))
+
+
+# ---------------------------------------------------------------- compression ----------------
+@pytest.mark.parametrize("name,proj", [("c0", 0), ("t_mlp", 0), ("t_mlp", 1), ("c1", 0)])
+def test_compress_bitexact(name, proj):
+    c = single_case(name, proj) if proj == 0 else None
+    if c is None:
+        cfg = gen.CONFIGS[name]
+        E, N, K = cfg.E, cfg.N2, cfg.K2
+        w = np.stack([gen.weights_expert(cfg, 1, e, N, K) for e in range(E)])
+        Wd = mq.moesq_compress_weights(dev(w))
+        W = orc.compress(w)
+    else:
+        Wd, Wo = c["Wd"], c["Wo"]
+        W = Wo.as_dict()
+    say("compress", name, proj)
+    assert np.array_equal(host(Wd.gscale), W["gscale"])
+    assert np.array_equal(host(Wd.scale), W["scale"])
+    assert np.array_equal(host(Wd.mask), W["mask"])
+    assert np.array_equal(host(Wd.packed), W["packed"])
+
+
+def test_compress_edge_patterns():
+    """Zero groups, pairs that quantize to 0x00 (pack tie rule), ties in pair norms, and a tiny block
+    whose scale underflows."""
+    say("compress edge patterns")
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((2, 64, 256)) * 0.02).astype(np.float32)
+    w[0, 0, :32] = 0.0                          # all-zero block
+    w[0, 1, :8] = [1e-9, 1e-9, 0.3, 0.3, 0, 0, 0.3, 0.3]  # kept pair far below the block scale -> 0x00
+    w[0, 2, :8] = [0.1, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1]  # four equal pairs: lower two kept
+    w[1, 3, 32:64] = 1e-12                      # underflowing scale
+    w[1, 5, 100] = 1.0                          # tensor amax
+    Wd = mq.moesq_compress_weights(dev(w))
+    W = orc.compress(w)
+    for key in ("packed", "mask", "scale"):
+        assert np.array_equal(host(getattr(Wd, key)), W[key]), key
+    assert np.array_equal(host(Wd.gscale), W["gscale"])
+    dense = mq.moesq_unpack_weights(Wd)
+    assert np.array_equal(host(dense), orc.unpack(W["packed"], W["mask"]))
+
+
+def test_unpack_roundtrip_and_bad_nibble():
+    c = single_case("c0")
+    say("unpack c0")
+    dense = mq.moesq_unpack_weights(c["Wd"])
+    W = c["Wo"].as_dict()
+    assert np.array_equal(host(dense), orc.unpack(W["packed"], W["mask"]))
+    bad = mq.Weights(c["Wd"].packed.clone(), c["Wd"].mask.clone(), c["Wd"].scale, c["Wd"].gscale)
+    bad.mask[0, 0, 0] = 0x37                          # nibble 7: three bits
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mq.moesq_unpack_weights(bad, dev_status=st)
+    assert int(host(st)[0]) == mq.ERR_PATTERN
+
+
+# ---------------------------------------------------------------- routing --------------------
+def _route_check(ids, E):
+    rt = mq.moesq_route_permute(dev(ids.astype(np.int32)), E)
+    R = orc.route(ids, E)
+    for key in ("counts", "offsets", "sorted_slot", "slot_pos"):
+        assert np.array_equal(host(rt[key]), R[key]), key
+    return rt
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4", "t_zipf"])
+def test_route_bitexact(name):
+    cfg = gen.CONFIGS[name]
+    say("route", name)
+    ids, _ = gen.routing(cfg)
+    _route_check(ids, cfg.E)
+
+
+def test_route_edge_cases():
+    say("route edges")
+    _route_check(np.zeros((1, 1), np.int32), 4)                                    # T = 1, k = 1
+    _route_check(np.full((3000, 1), 7, np.int32), 8)                               # all slots to one expert
+    _route_check(np.tile(np.arange(8, dtype=np.int32), (2000, 1)), 384)            # 16000 slots, multi-block
+    ids, _ = gen.route_zipf(3, 9000, 384, 8, 1.1, 0)                                # 72000 slots, uneven chunks
+    _route_check(ids, 384)
+    # ids out of range are dropped and reported
+    ids = np.array([[0, 1], [5, 2], [1, -1]], np.int32)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rt = mq.moesq_route_permute(dev(ids), 4, dev_status=st)
+    assert int(host(st)[0]) == mq.ERR_INVALID_ARG
+    sp = host(rt["slot_pos"])
+    assert sp[2] == -1 and sp[5] == -1
+    assert host(rt["offsets"])[-1] == 4
+    assert np.array_equal(host(rt["counts"]), [1, 2, 1, 0])
+
+
+# ---------------------------------------------------------------- activation quantization ----
+@pytest.mark.parametrize("name", ["c0", "c1", "t_zipf", "t_mlp"])
+def test_quantize_dispatch_bitexact(name):
+    c = single_case(name)
+    say("quantize", name)
+    R, k = c["R"], c["k"]
+    rt = mq.moesq_route_permute(dev(c["ids"]), c["E"])
+    ga = c["ga"] * np.linspace(0.5, 2.0, c["E"]).astype(np.float32)   # distinct per-expert scales
+    q, s = mq.moesq_quantize_act(dev(c["x"]), dev(ga), gather_slot=rt["sorted_slot"], k=k, offsets=rt["offsets"])
+    qo, so = orc.dispatch_quantize(c["x"], R["sorted_slot"], k, R["offsets"], ga)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s), so)
+
+
+def test_quantize_plain_and_bf16_and_zero():
+    say("quantize plain / bf16 / zeros")
+    x = gen.student_t(3, gen.act_stream(9), 37 * 512).reshape(37, 512)
+    x[3] = 0.0
+    x[4, :32] = 1e-30
+    g = np.float32(orc.global_scale_of(x))
+    q, s = mq.moesq_quantize_act(dev(x), dev(np.array([g], np.float32)))
+    qo, so = orc.quantize_rows(x, g)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    q2, s2 = mq.moesq_quantize_act(xb.to(DEV), dev(np.array([g], np.float32)))
+    qo2, so2 = orc.quantize_rows(xb.to(torch.float32).numpy(), g)
+    assert np.array_equal(host(q2), qo2) and np.array_equal(host(s2), so2)
+
+
+# ---------------------------------------------------------------- grouped GEMM ---------------
+def _gemm_inputs(c):
+    R, k = c["R"], c["k"]
+    qo, so = orc.dispatch_quantize(c["x"], R["sorted_slot"], k, R["offsets"], c["ga"])
+    return qo, so
+
+
+@pytest.mark.parametrize("name,proj,nrows", [("c0", 0, None), ("c1", 0, None), ("t_zipf", 0, None),
+                                             ("c2", 0, 384)])
+@pytest.mark.parametrize("flags", ["decode", "prefill"])
+def test_grouped_gemm_parity(name, proj, nrows, flags):
+    c = single_case(name, proj)
+    say("gemm", name, proj, flags)
+    qo, so = _gemm_inputs(c)
+    off = c["R"]["offsets"]
+    rl = None if nrows is None else sample_rows(off, nrows)
+    fl = mq.F_FORCE_DECODE if flags == "decode" else mq.F_FORCE_PREFILL
+    y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl)
+    yb = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.bfloat16,
+                               flags=fl)
+    rows = np.arange(int(off[-1])) if rl is None else rl
+    Wo = c["Wo"].ensure(np.searchsorted(off, rows, side="right") - 1)
+    ref = orc.grouped_gemm(Wo.as_dict(), qo, so, c["ga"], off, rows)
+    got = host(y)[rows]
+    err = orc.rel_frobenius(got, ref)
+    say("rel-Frobenius", err)
+    assert err <= GEMM_TOL
+    gotb = host(yb.to(torch.float32))[rows]
+    assert orc.rel_frobenius(gotb, bf16_round(ref)) <= GEMM_TOL
+
+
+def test_grouped_gemm_deterministic_and_variants_agree():
+    c = single_case("t_zipf")
+    say("gemm determinism t_zipf")
+    qo, so = _gemm_inputs(c)
+    args = (c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(c["R"]["offsets"]))
+    y1 = host(mq.moesq_grouped_gemm(*args, y_dtype=torch.float32))
+    y2 = host(mq.moesq_grouped_gemm(*args, y_dtype=torch.float32))
+    assert np.array_equal(y1, y2)
+
+
+def test_grouped_gemm_edge_cases():
+    """All rows to one expert, T = 1 / k = 1, all-zero activations."""
+    c = single_case("c0")
+    say("gemm edges c0")
+    E, K, N = c["E"], c["K"], c["N"]
+    W = c["Wo"].as_dict()
+    for ids in (np.full((70, 1), 2, np.int32), np.array([[3]], np.int32)):
+        R = orc.route(ids, E)
+        x = gen.activations(c["cfg"], 5, ids.shape[0], K)
+        ga = np.full(E, orc.global_scale_of(x), np.float32)
+        qo, so = orc.dispatch_quantize(x, R["sorted_slot"], ids.shape[1], R["offsets"], ga)
+        for fl in (mq.F_FORCE_DECODE, mq.F_FORCE_PREFILL):
+            y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(ga), dev(R["offsets"]), y_dtype=torch.float32,
+                                      flags=fl)
+            ref = orc.grouped_gemm(W, qo, so, ga, R["offsets"])
+            assert orc.rel_frobenius(host(y), ref) <= GEMM_TOL
+    qz = np.zeros((16, K // 2), np.uint8)
+    sz = np.zeros((16, K // 32), np.uint8)
+    off = np.array([0, 4, 4, 10, 16], np.int32)
+    y = mq.moesq_grouped_gemm(c["Wd"], dev(qz), dev(sz), dev(c["ga"]), dev(off), y_dtype=torch.float32)
+    assert np.all(host(y) == 0)
+
+
+# ---------------------------------------------------------------- combine --------------------
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_combine_parity(ydt):
+    say("combine", ydt)
+    T, k, H, E = 50, 4, 512, 9
+    ids, w = gen.route_uniform(11, T, E, k)
+    R = orc.route(ids, E)
+    y = gen.normal(3, gen.act_stream(3), T * k * H).reshape(T * k, H)
+    yt = torch.from_numpy(y).to(ydt)
+    out = mq.moesq_unpermute_combine(yt.to(DEV), dev(R["slot_pos"]), dev(w), out_dtype=torch.float32)
+    ref = orc.combine(yt.to(torch.float64).numpy(), R["slot_pos"], w)
+    assert orc.rel_frobenius(host(out), ref) <= 1e-6
+    outb = mq.moesq_unpermute_combine(yt.to(DEV), dev(R["slot_pos"]), dev(w), out_dtype=torch.bfloat16)
+    assert orc.rel_frobenius(host(outb.float()), bf16_round(ref)) <= 1e-3
+
+
+# ---------------------------------------------------------------- MLP --------------------------
+def test_mlp_parity_tiny():
+    cfg = gen.CONFIGS["t_mlp"]
+    say("mlp t_mlp")
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13o, W2o = orc.compress(w13), orc.compress(w2)
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    x = gen.activations(cfg, 0, T, H)
+    ids, wts = gen.routing(cfg)
+    R = orc.route(ids, E)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    gh = np.full(E, orc.global_scale(cfg.h_amax_hint), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"])
+    rows = int(R["offsets"][-1])
+    y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
+                                flags=mq.F_DUMP_GATEUP)
+    hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
+    # gate_up GEMM stage
+    assert orc.rel_frobenius(host(dump), M["y13"]) <= GEMM_TOL
+    # requantized h: identical codes except where the oracle's h sits at a rounding boundary
+    hq_g, hs_g = host(hq), host(hs)
+    assert np.mean(hs_g != M["hs"]) <= 1e-3
+    deq_g = orc.dequant(hq_g, hs_g)
+    deq_o = orc.dequant(M["hq"], M["hs"])
+    diff = deq_g != deq_o
+    assert diff.mean() <= 2e-3
+    # down GEMM on the same codes as the oracle's chain -> compare after the combine
+    y_np = host(y)
+    err = orc.rel_frobenius(y_np, M["y2"])
+    say("mlp y2 rel-Frobenius", err, "h code mismatches", int(diff.sum()))
+    assert err <= 1e-2
+    # down GEMM alone on the oracle's h codes: identical operands
+    yd = mq.moesq_grouped_gemm(W2, dev(M["hq"]), dev(M["hs"]), dev(gh), dev(R["offsets"]), y_dtype=torch.float32)
+    assert orc.rel_frobenius(host(yd), M["y2"]) <= GEMM_TOL
+    out = mq.moesq_unpermute_combine(y, dev(R["slot_pos"]), dev(wts), out_dtype=torch.float32)
+    ref = orc.combine(M["y2"], R["slot_pos"], wts)
+    assert orc.rel_frobenius(host(out), ref) <= 1e-2
