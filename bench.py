@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the paired-4:8 sparse NVFP4 MoE expert path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, inputs resident in HBM:
+  single-projection workloads (c0, c1, c2): route/permute -> dispatch+quantize -> grouped GEMM;
+  decode layer (c3): route/permute -> quantize -> gate_up GEMM -> quantize -> down GEMM;
+  MLP (c4): route/permute -> quantize -> gate_up GEMM + SwiGLU + requantize -> down GEMM -> combine.
+Each step is captured once in a HIP graph (one graph per rotation slot) and replayed. Weights and
+input batches rotate over several copies so that repeated steps do not find the weights in the
+last-level cache when the weight set would fit there (c1: 8 copies, about 1.1 GB).
+
+Metric (paper Appendix D.2): TFLOP/s_eff = 2 * M * K * sum_e N_e / t with M the output rows and N_e
+the tokens of expert e, summed over the step's GEMMs. The roofline object reports the dominant
+kernel: its algorithmic bytes (decode: weights of experts with tokens at 2.75 bits per weight, the
+quantized activations, bf16 outputs) or algorithmic flops (prefill: the kept products only, half
+of the dense-equivalent count) per launch, divided by its mean duration measured with HIP events
+on the launch stream.
+
+Prints one JSON line. --gpus N > 1 exits: this build has no multi-GPU path.
+"""
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "grouped sparse-NVFP4 GEMM eff. TFLOP/s + HBM GB/s (decode & prefill, 1 GPU)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16 MFMA; the 2:4 sparse MFMA does kept products at this rate x2 eff
+BITS_PER_WEIGHT = 2.75       # paper Appendix A, Eq. 7
+
+
+def tflops_eff(M, K, sum_n, seconds):
+    """Paper Appendix D.2: TFLOP/s_eff = 2 M K sum_g N_g / (t * 1e12)."""
+    return 2.0 * M * K * sum_n / (seconds * 1e12)
+
+
+def weight_bytes(N, K):
+    return N * K * BITS_PER_WEIGHT / 8.0
+
+
+def gemm_bytes(n_active, N, K, rows, E, out_bytes=2):
+    """Algorithmic HBM bytes of one grouped GEMM launch: compressed weights of the experts that have
+    tokens, NVFP4 activations (codes + block scales), outputs, offsets and per-expert scales."""
+    return (n_active * weight_bytes(N, K) + rows * (K / 2 + K / 32) + rows * N * out_bytes + (E + 1) * 4 + 2 * E * 4)
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "sparse_precision_grouped_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel_key)
+    if not ent or ent.get("src_hash") != _src_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Workload:
+    """Device buffers, graphs and accounting for one named config."""
+
+    def __init__(self, name, rotate, torch, gen, mq):
+        self.torch, self.gen, self.mq = torch, gen, mq
+        self.cfg = cfg = gen.CONFIGS[name]
+        self.name = name
+        dev = "cuda"
+        self.kind = "mlp" if cfg.mlp else ("pair" if cfg.N2 else "single")
+        E, T, k = cfg.E, cfg.T, cfg.k
+        self.rows = T * k
+        # weights: compressed once on the device, then copied for rotation
+        self.W = self._weights(0, cfg.N, cfg.K)
+        self.W2 = self._weights(1, cfg.N2, cfg.K2) if self.kind != "single" else None
+        wset = self.W.nbytes() + (self.W2.nbytes() if self.W2 else 0)
+        self.R = max(1, min(rotate, int(np.ceil(1.2e9 / wset)))) if wset < 512e6 else 1
+        self.Wc = [self.W] + [self._clone(self.W) for _ in range(self.R - 1)]
+        self.W2c = [self.W2] * self.R if self.W2 is None else [self.W2] + [self._clone(self.W2) for _ in
+                                                                          range(self.R - 1)]
+        self.slots = []
+        for r in range(self.R):
+            cr = dataclasses.replace(cfg, seed=cfg.seed + 7919 * r)
+            ids, wts = gen.routing(cr)
+            x = torch.from_numpy(gen.activations(cr, 0, T, cfg.K)).to(dev)
+            sl = dict(ids=torch.from_numpy(ids).to(dev), wts=torch.from_numpy(wts).to(dev), x=x,
+                      counts_host=np.bincount(ids.ravel(), minlength=E))
+            g = mq.moesq_global_scale(x)
+            sl["ga"] = g.expand(E).contiguous()
+            sl["rt"] = mq.moesq_route_permute(sl["ids"], E)
+            sl["ws_route"] = torch.empty(max(1, mq.moesq_workspace_bytes(mq.WS_ROUTE, T, k, E)), dtype=torch.uint8,
+                                         device=dev)
+            sl["q"] = torch.empty((self.rows, cfg.K // 2), dtype=torch.uint8, device=dev)
+            sl["s"] = torch.empty((self.rows, cfg.K // 32), dtype=torch.uint8, device=dev)
+            if self.kind == "single":
+                sl["y"] = torch.empty((self.rows, cfg.N), dtype=torch.bfloat16, device=dev)
+            elif self.kind == "pair":
+                x2 = torch.from_numpy(gen.activations(cr, 1, T, cfg.K2)).to(dev)
+                sl["x2"] = x2
+                sl["ga2"] = mq.moesq_global_scale(x2).expand(E).contiguous()
+                sl["y"] = torch.empty((self.rows, cfg.N), dtype=torch.bfloat16, device=dev)
+                sl["q2"] = torch.empty((self.rows, cfg.K2 // 2), dtype=torch.uint8, device=dev)
+                sl["s2"] = torch.empty((self.rows, cfg.K2 // 32), dtype=torch.uint8, device=dev)
+                sl["y2"] = torch.empty((self.rows, cfg.N2), dtype=torch.bfloat16, device=dev)
+            else:
+                I = cfg.N // 2
+                sl["gh"] = torch.full((E,), cfg.gamma_h, dtype=torch.float32, device=dev)
+                sl["ws_mlp"] = mq.mlp_workspace(self.rows, I, False, dev)
+                sl["y2"] = torch.empty((self.rows, cfg.N2), dtype=torch.bfloat16, device=dev)
+                sl["out"] = torch.empty((T, cfg.N2), dtype=torch.bfloat16, device=dev)
+            self.slots.append(sl)
+        torch.cuda.synchronize()
+        self.graphs = []
+
+    def _weights(self, proj, N, K):
+        torch, gen, mq, cfg = self.torch, self.gen, self.mq, self.cfg
+        W = mq.Weights.empty(cfg.E, N, K)
+        chunk = max(1, min(cfg.E, int(2e9 // (N * K * 4))))
+        buf = torch.empty((chunk, N, K), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mq.moesq_workspace_bytes(mq.WS_COMPRESS, 0, 0, chunk), dtype=torch.uint8, device="cuda")
+        for e0 in range(0, cfg.E, chunk):
+            n = min(chunk, cfg.E - e0)
+            for j in range(n):
+                gen.gpu_fill_normal(buf[j], cfg.seed, gen.weight_stream(proj, e0 + j), cfg.w_std)
+            sub = mq.Weights(W.packed[e0:e0 + n], W.mask[e0:e0 + n], W.scale[e0:e0 + n], W.gscale[e0:e0 + n])
+            mq.moesq_compress_weights(buf[:n], out=sub, workspace=ws)
+        torch.cuda.synchronize()
+        del buf
+        return W
+
+    def _clone(self, W):
+        return self.mq.Weights(W.packed.clone(), W.mask.clone(), W.scale.clone(), W.gscale.clone())
+
+    # ---- one step of the path on slot r (enqueued on the current stream) ----
+    def step(self, r):
+        mq, cfg, sl = self.mq, self.cfg, self.slots[r]
+        rt = sl["rt"]
+        mq.moesq_route_permute(sl["ids"], cfg.E, rt["counts"], rt["offsets"], rt["sorted_slot"], rt["slot_pos"],
+                               sl["ws_route"])
+        mq.moesq_quantize_act(sl["x"], sl["ga"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
+                              q=sl["q"], s=sl["s"])
+        if self.kind == "single":
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+        elif self.kind == "pair":
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+            mq.moesq_quantize_act(sl["x2"], sl["ga2"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
+                                  q=sl["q2"], s=sl["s2"])
+            mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"])
+        else:
+            mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
+                                y=sl["y2"], workspace=sl["ws_mlp"])
+            mq.moesq_unpermute_combine(sl["y2"], rt["slot_pos"], sl["wts"], out=sl["out"])
+
+    def dominant(self, r):
+        """The dominant kernel launch of a step (enqueued on the current stream)."""
+        mq, sl = self.mq, self.slots[r]
+        rt = sl["rt"]
+        if self.kind == "mlp":
+            mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
+                                y=sl["y2"], workspace=sl["ws_mlp"])
+        else:
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+
+    def capture(self):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(self.R):
+                self.step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(self.R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(r)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    # ---- accounting ----
+    def eff_flops_per_step(self):
+        cfg = self.cfg
+        if self.kind == "single":
+            return 2.0 * cfg.N * cfg.K * self.rows
+        if self.kind == "pair":
+            return 2.0 * self.rows * (cfg.N * cfg.K + cfg.N2 * cfg.K2)
+        return 2.0 * self.rows * (cfg.N * cfg.K + cfg.N2 * cfg.K2)
+
+    def roofline_units(self):
+        """(bound, algorithmic units per dominant launch averaged over the slots, unit, peak, kernel)."""
+        cfg = self.cfg
+        decode = self.kind != "mlp" and self.rows <= 16 * cfg.E
+        if decode:
+            b = np.mean([gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N, cfg.K, self.rows, cfg.E)
+                         for sl in self.slots])
+            return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, "gemm_decode_kernel"
+        kept = 0.5 * self.eff_flops_per_step() if self.kind == "mlp" else cfg.N * cfg.K * self.rows
+        kern = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)" if self.kind == "mlp" else "gemm_prefill_kernel"
+        return "mfma", kept / 1e12, "TFLOP/s", F16_PEAK_TFLOPS, kern
+
+
+def cpu_baseline(wl, orc, gen, max_reps=3):
+    """The oracle's step on the host cores, on a bounded sample of the same workload."""
+    cfg = wl.cfg
+    E, T, k, N, K = cfg.E, cfg.T, cfg.k, cfg.N, cfg.K
+    ids, wts = gen.routing(cfg)
+    x = gen.activations(cfg, 0, T, K)
+    rows = T * k
+    R = orc.route(ids, E)
+    if wl.kind == "single" and cfg.E * cfg.N * cfg.K <= 512 * 1024 * 1024:
+        w = np.stack([gen.weights_expert(cfg, 0, e, N, K) for e in range(E)])
+        Wo = orc.compress(w)
+        row_list = None if rows <= 4096 else np.linspace(0, rows - 1, 512).astype(np.int64)
+        sample = "full step (route, dispatch-quantize, GEMM) on %s" % (
+            "all %d rows" % rows if row_list is None else "512 of %d rows (GEMM), all rows (route, quantize)" % rows)
+    else:
+        return None
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    times = []
+    n_rows = rows if row_list is None else row_list.size
+    for _ in range(max_reps):
+        t0 = time.perf_counter()
+        Rr = orc.route(ids, E)
+        q, s = orc.dispatch_quantize(x, Rr["sorted_slot"], k, Rr["offsets"], ga)
+        orc.grouped_gemm(Wo, q, s, ga, Rr["offsets"], row_list)
+        times.append(time.perf_counter() - t0)
+        if sum(times) > 20:
+            break
+    t = float(np.median(times))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": tflops_eff(N, K, n_rows, t), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample + ", median of %d run(s), %.3f s each" % (len(times), t)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--kernel-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no collective or sharded path); "
+              "rerun with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gen
+    import sparse_precision_grouped_amd as mq
+
+    torch.cuda.set_device(0)
+    wl = Workload(args.workload, args.rotate, torch, gen, mq)
+    wl.capture()
+    for i in range(args.warmup):
+        wl.graphs[i % wl.R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.graphs[i % wl.R].replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / args.steps
+    value = wl.eff_flops_per_step() / t / 1e12
+
+    # dominant kernel: HIP events on the launch stream around each launch
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record(st)
+        wl.dominant(i % wl.R)
+        b.record(st)
+    torch.cuda.synchronize()
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    bound, units, unit, peak, kname = wl.roofline_units()
+    achieved = units / (kms * 1e-3)
+    traffic = _traffic("%s:%s" % (args.workload, kname))
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
+                "kernel_ms": round(kms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        cpu = cpu_baseline(wl, orc, gen)
+
+    cfg = wl.cfg
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "nvfp4 operands, f16 sparse MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": "%s: %s (E=%d, K=%d, N=%d, T=%d, top-%d, %s routing%s)" % (
+            args.workload, cfg.desc, cfg.E, cfg.K, cfg.N, cfg.T, cfg.k, cfg.routing,
+            ", then K=%d N=%d" % (cfg.K2, cfg.N2) if cfg.N2 else ""),
+            "rows": wl.rows, "weight_copies": wl.R, "graph_replay": True,
+            "step_gbps_algorithmic": round(
+                (gemm_bytes(np.mean([(sl["counts_host"] > 0).sum() for sl in wl.slots]), cfg.N, cfg.K, wl.rows,
+                            cfg.E) / t / 1e9) if wl.kind == "single" else 0.0, 1)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

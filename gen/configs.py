@@ -26,7 +26,8 @@ class Config:
     N2: int = 0
     K2: int = 0
     mlp: bool = False      # gate_up -> SiLU(gate)*up -> requant -> down -> combine
-    h_amax_hint: float = 0.0   # calibrated amax of h used to set gamma_h (MLP only)
+    gamma_h: float = 0.0   # static tensor scale of the intermediate h (MLP only): 448 / (amax_h / 6) for a
+                           # calibrated amax_h (t_mlp: 2.0, c4: 64.0)
     desc: str = ""
 
     @property
@@ -44,10 +45,10 @@ CONFIGS = {
     "c3": Config("c3", E=384, K=7168, N=4096, T=64, k=8, routing="uniform", act_dist="student_t", seed=1237,
                  N2=7168, K2=2048, desc="Kimi-K2.5 gate_up + down, decode"),
     "c4": Config("c4", E=384, K=7168, N=4096, T=8192, k=8, routing="zipf", act_dist="student_t", seed=1238,
-                 N2=7168, K2=2048, mlp=True, h_amax_hint=64.0, desc="Kimi-K2.5 routed-expert MLP, prefill"),
+                 N2=7168, K2=2048, mlp=True, gamma_h=42.0, desc="Kimi-K2.5 routed-expert MLP, prefill"),
     # small cases for parity tests
     "t_mlp": Config("t_mlp", E=4, K=256, N=512, T=64, k=2, routing="uniform", act_dist="student_t", seed=77,
-                    N2=256, K2=256, mlp=True, h_amax_hint=2.0, desc="tiny MLP (H=256, I=256)"),
+                    N2=256, K2=256, mlp=True, gamma_h=1344.0, desc="tiny MLP (H=256, I=256)"),
     "t_zipf": Config("t_zipf", E=16, K=512, N=384, T=512, k=4, routing="zipf", zipf_zero=3, seed=78,
                      desc="small Zipf prefill with empty experts and ragged tiles"),
 }

@@ -176,6 +176,15 @@ int moesq_compress_weights(void *stream, const float *w, int32_t E, int32_t N, i
                            size_t workspace_bytes, int32_t *dev_status);
 
 /*
+ * Tensor scale of Eq. 5 for a device tensor x [rows][ld_x] (fp32 or bf16, first K columns):
+ * gamma_out[0] = 448 / (amax / 6) in fp32 (1 for an all-zero tensor). Calibration of the static
+ * per-expert activation scale (model card: stored per expert linear); not on the timed path.
+ * gamma_out is used as scratch while the call runs.
+ */
+int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t rows, int32_t K, int64_t ld_x,
+                       float *gamma_out);
+
+/*
  * Pair-bitmask v1 -> dense NVFP4 bytes [E][N][K/2] (the lossless round trip of the model card).
  * dev_status (optional) receives MOESQ_ERR_PATTERN for a mask nibble whose popcount is not 2.
  */

@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm",
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
-    "moesq_workspace_bytes", "moesq_status_str", "moesq_version",
+    "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
     "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL",
     "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS",
 ]
@@ -60,13 +60,14 @@ def lib():
         L.moesq_unpermute_combine.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
         L.moesq_compress_weights.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_unpack_weights.argtypes = [vp, W, vp, vp]
+        L.moesq_global_scale.argtypes = [vp, vp, i32, i64, i32, i64, vp]
         L.moesq_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32]
         L.moesq_workspace_bytes.restype = sz
         L.moesq_status_str.argtypes = [i32]
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
         for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm", "moesq_expert_mlp",
-                     "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights"):
+                     "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -244,6 +245,17 @@ def moesq_compress_weights(w, out=None, workspace=None, dev_status=None):
     _check("moesq_compress_weights",
            lib().moesq_compress_weights(_stream(), _p(w), E, N, K, _p(out.packed), _p(out.mask), _p(out.scale),
                                         _p(out.gscale), _p(workspace), workspace.numel(), _p(dev_status)))
+    return out
+
+
+def moesq_global_scale(x, out=None):
+    """Eq. 5 tensor scale of x [rows, K] (fp32/bf16) computed on the device -> float32 tensor [1]."""
+    _dev(x)
+    rows, K = x.shape
+    assert x.stride(1) == 1
+    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    _check("moesq_global_scale", lib().moesq_global_scale(_stream(), _p(x), _dtype_code(x.dtype), rows, K,
+                                                          x.stride(0), _p(out)))
     return out
 
 

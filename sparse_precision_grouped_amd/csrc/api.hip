@@ -156,6 +156,14 @@ int moesq_unpermute_combine(void* stream, const void* y_sorted, int32_t y_dtype,
                         out_dtype == MOESQ_BF16);
 }
 
+int moesq_global_scale(void* stream, const void* x, int32_t x_dtype, int64_t rows, int32_t K, int64_t ld_x,
+                       float* gamma_out) {
+  if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  if (rows < 0 || K <= 0 || ld_x < K || !gamma_out || (rows > 0 && !x)) return MOESQ_ERR_INVALID_ARG;
+  if (!aligned(gamma_out, 4)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_global_scale((hipStream_t)stream, x, x_dtype == MOESQ_BF16, rows, K, ld_x, gamma_out);
+}
+
 int moesq_compress_weights(void* stream, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed,
                            uint8_t* mask, uint8_t* scale, float* gscale, void* workspace, size_t workspace_bytes,
                            int32_t* dev_status) {

@@ -38,6 +38,9 @@ int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32
                     const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
                     int32_t E, uint8_t* q, uint8_t* s);
 
+int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
+                        float* gamma_out);
+
 int launch_compress(hipStream_t st, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
                     uint8_t* scale, float* gscale, void* ws, int32_t* dev_status);
 int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, int32_t E, int32_t N, int32_t K,

@@ -243,4 +243,42 @@ int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, in
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ tensor scale (Eq. 5) ---------
+// amax of a [rows][K] tensor (leading dimension ld) accumulated as float bits in out[0], then
+// replaced in place by gamma = 448 / (amax / 6).
+__global__ __launch_bounds__(256) void amax_rows_kernel(const void* __restrict__ x, int x_bf16, int64_t rows,
+                                                        int32_t K, int64_t ld, uint32_t* __restrict__ out) {
+  const int64_t n = rows * (int64_t)K;
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / K, c = i % K;
+    const float v = x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[r * ld + c]) : ((const float*)x)[r * ld + c];
+    m = __builtin_fmaxf(m, __builtin_fabsf(v));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(out, __float_as_uint(m));
+}
+
+__global__ void finalize_scale_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) {
+    const float g = global_scale_from_amax(__uint_as_float(out[0]));
+    out[0] = __float_as_uint(g);
+  }
+}
+
+int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
+                        float* gamma_out) {
+  uint32_t* o = (uint32_t*)gamma_out;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, o, 1);
+  const int64_t n = rows * (int64_t)K;
+  if (n > 0) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(amax_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, rows, K, ld, o);
+  }
+  hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(64), 0, st, o);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
 }  // namespace moesq

@@ -1,0 +1,36 @@
+"""The benchmark's metric code, pinned to the pages' Table 10, and its one-GPU contract."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _rows(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return [l.split() for l in f if l.strip() and not l.startswith("#")]
+
+
+def test_tflops_eff_reproduces_table10():
+    for M, K, G, N, ms, printed in _rows("table10_tflops.txt"):
+        M, K, G, N = int(M), int(K), int(G), int(N)
+        pattern = [N, 3 * N // 4, N // 2, N // 4]          # repeated across the G groups
+        sum_n = sum(pattern[g % 4] for g in range(G))
+        got = bench.tflops_eff(M, K, sum_n, float(ms) * 1e-3)
+        # latency printed to 3 decimals: +-0.0005 ms -> <= 0.08 % on the smallest latency
+        assert got == pytest.approx(float(printed), rel=1e-3)
+
+
+def test_weight_bytes_is_eq7():
+    assert bench.weight_bytes(1536, 2048) == 1536 * 2048 * 2.75 / 8 == 1081344
+    assert bench.weight_bytes(4096, 7168) == 10092544
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

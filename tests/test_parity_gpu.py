@@ -152,6 +152,16 @@ def test_quantize_plain_and_bf16_and_zero():
     assert np.array_equal(host(q2), qo2) and np.array_equal(host(s2), so2)
 
 
+def test_global_scale_bitexact():
+    say("global scale")
+    for x in (gen.student_t(4, gen.act_stream(2), 300 * 256).reshape(300, 256),
+              gen.normal(4, gen.act_stream(3), 5 * 4096).reshape(5, 4096), np.zeros((2, 64), np.float32)):
+        g = mq.moesq_global_scale(dev(x))
+        assert host(g)[0] == np.float32(orc.global_scale_of(x))
+        gb = mq.moesq_global_scale(torch.from_numpy(x).to(torch.bfloat16).to(DEV))
+        assert host(gb)[0] == np.float32(orc.global_scale_of(torch.from_numpy(x).to(torch.bfloat16).float().numpy()))
+
+
 # ---------------------------------------------------------------- grouped GEMM ---------------
 def _gemm_inputs(c):
     R, k = c["R"], c["k"]
@@ -245,7 +255,7 @@ def test_mlp_parity_tiny():
     ids, wts = gen.routing(cfg)
     R = orc.route(ids, E)
     ga = np.full(E, orc.global_scale_of(x), np.float32)
-    gh = np.full(E, orc.global_scale(cfg.h_amax_hint), np.float32)
+    gh = np.full(E, cfg.gamma_h, np.float32)
     qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
     M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"])
     rows = int(R["offsets"][-1])
