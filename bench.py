@@ -89,7 +89,7 @@ class Workload:
         # weights: compressed once on the device, then copied for rotation
         self.W = self._weights(0, cfg.N, cfg.K)
         self.W2 = self._weights(1, cfg.N2, cfg.K2) if self.kind != "single" else None
-        wset = self.W.nbytes() + (self.W2.nbytes() if self.W2 else 0)
+        wset = self.W.kl.numel() + (self.W2.kl.numel() if self.W2 else 0)
         self.R = max(1, min(rotate, int(np.ceil(1.2e9 / wset)))) if wset < 512e6 else 1
         self.Wc = [self.W] + [self._clone(self.W) for _ in range(self.R - 1)]
         self.W2c = [self.W2] * self.R if self.W2 is None else [self.W2] + [self._clone(self.W2) for _ in
@@ -139,13 +139,14 @@ class Workload:
             for j in range(n):
                 gen.gpu_fill_normal(buf[j], cfg.seed, gen.weight_stream(proj, e0 + j), cfg.w_std)
             sub = mq.Weights(W.packed[e0:e0 + n], W.mask[e0:e0 + n], W.scale[e0:e0 + n], W.gscale[e0:e0 + n])
-            mq.moesq_compress_weights(buf[:n], out=sub, workspace=ws)
+            mq.moesq_compress_weights(buf[:n], out=sub, workspace=ws, prepack=False)
+        W.prepack()
         torch.cuda.synchronize()
         del buf
         return W
 
     def _clone(self, W):
-        return self.mq.Weights(W.packed.clone(), W.mask.clone(), W.scale.clone(), W.gscale.clone())
+        return self.mq.Weights(W.packed, W.mask, W.scale, W.gscale.clone(), W.kl.clone())
 
     # ---- one step of the path on slot r (enqueued on the current stream) ----
     def step(self, r):

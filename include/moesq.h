@@ -71,7 +71,11 @@ extern "C" {
  *                       low nibble = lower-K chunk
  *   scale  [E][N][K/32] UE4M3 block-scale codes
  *   gscale [E]          fp32 tensor scale gamma_w,e of Eq. 5
- * The struct itself lives in host memory; its pointers are device pointers read during the call.
+ *   kl                  the same weights in the kernel layout (moesq_prepack_weights), read by the
+ *                       GEMM calls; moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned
+ * The GEMM calls read only kl and gscale (packed/mask/scale may then be NULL); the storage calls
+ * (prepack, unpack) read packed/mask/scale. The struct itself lives in host memory; its pointers
+ * are device pointers read during the call.
  */
 typedef struct {
   int32_t E, N, K;
@@ -79,6 +83,7 @@ typedef struct {
   const uint8_t *mask;
   const uint8_t *scale;
   const float *gscale;
+  const uint8_t *kl;
 } moesq_weights;
 
 /*
@@ -126,7 +131,8 @@ int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, 
  *   gamma_a     [E] activation tensor scale of each expert
  *   offsets     [E+1] from moesq_route_permute (device)
  *   y           [rows][N] fp32 or bf16 (round to nearest even). Rows >= offsets[E] are not written.
- * Requires K % 256 == 0 and N % 64 == 0 (MOESQ_ERR_UNSUPPORTED otherwise); E <= 4096.
+ * Requires W->kl (MOESQ_ERR_INVALID_ARG if NULL), K % 256 == 0 and N % 64 == 0
+ * (MOESQ_ERR_UNSUPPORTED otherwise); E <= 4096.
  */
 int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s,
                        const float *gamma_a, const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype,
@@ -183,6 +189,20 @@ int moesq_compress_weights(void *stream, const float *w, int32_t E, int32_t N, i
  */
 int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t rows, int32_t K, int64_t ld_x,
                        float *gamma_out);
+
+/*
+ * Load-time repack (model card: the sparse checkpoint is rebuilt into the kernel's own layout at
+ * load time) of pair-bitmask v1 weights into the GEMM's fragment layout, same size (2.75 bits per
+ * weight): per expert, per 16-row block, per 256-K super-step a 1408-byte fragment; lane
+ * l = 16c + r (row r of the block, K [64c, +64) of the super-step) owns bytes [16l, +16) (its
+ * eight 8-groups, the two kept bytes (b0, b1) of each stored as (lo b0 | lo b1 << 4,
+ * hi b0 | hi b1 << 4)), [1024 + 4l, +4) (mask bytes) and [1280 + 2l, +2) (scale codes).
+ *   kl: moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned. Requires K % 256 == 0, N % 16 == 0.
+ */
+int moesq_prepack_weights(void *stream, const moesq_weights *W, uint8_t *kl, size_t kl_bytes);
+
+/* Bytes of the kernel layout of E experts of [N][K] weights: E * N * K * 11 / 32. */
+size_t moesq_kernel_layout_bytes(int32_t E, int32_t N, int32_t K);
 
 /*
  * Pair-bitmask v1 -> dense NVFP4 bytes [E][N][K/2] (the lossless round trip of the model card).

@@ -16,6 +16,7 @@ __all__ = [
     "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm",
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
     "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
+    "moesq_prepack_weights", "moesq_kernel_layout_bytes",
     "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL",
     "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS",
 ]
@@ -38,7 +39,7 @@ class MoesqError(RuntimeError):
 class _CWeights(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("gscale", ctypes.c_void_p)]
+                ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
 
 
 _lib = None
@@ -61,13 +62,17 @@ def lib():
         L.moesq_compress_weights.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_unpack_weights.argtypes = [vp, W, vp, vp]
         L.moesq_global_scale.argtypes = [vp, vp, i32, i64, i32, i64, vp]
+        L.moesq_prepack_weights.argtypes = [vp, W, vp, sz]
+        L.moesq_kernel_layout_bytes.argtypes = [i32, i32, i32]
+        L.moesq_kernel_layout_bytes.restype = sz
         L.moesq_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32]
         L.moesq_workspace_bytes.restype = sz
         L.moesq_status_str.argtypes = [i32]
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
         for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm", "moesq_expert_mlp",
-                     "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale"):
+                     "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale",
+                     "moesq_prepack_weights"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -113,17 +118,27 @@ def _dev(t):
 
 
 class Weights:
-    """Pair-bitmask v1 weights of one projection for E experts (device tensors):
-    packed [E,N,K/4] u8, mask [E,N,K/16] u8, scale [E,N,K/32] u8 (UE4M3), gscale [E] f32."""
+    """Weights of one projection for E experts (device tensors): pair-bitmask v1 storage
+    packed [E,N,K/4] u8, mask [E,N,K/16] u8, scale [E,N,K/32] u8 (UE4M3), gscale [E] f32, and
+    kl, the same bytes in the GEMM's kernel layout (built by ``prepack``)."""
 
-    def __init__(self, packed, mask, scale, gscale):
+    def __init__(self, packed, mask, scale, gscale, kl=None):
         E, N, K4 = packed.shape
         self.E, self.N, self.K = E, N, K4 * 4
         assert mask.shape == (E, N, self.K // 16) and scale.shape == (E, N, self.K // 32) and gscale.shape == (E,)
         for t in (packed, mask, scale):
             assert t.dtype == torch.uint8 and t.is_contiguous()
         assert gscale.dtype == torch.float32
-        self.packed, self.mask, self.scale, self.gscale = packed, mask, scale, gscale
+        self.packed, self.mask, self.scale, self.gscale, self.kl = packed, mask, scale, gscale, kl
+
+    def prepack(self):
+        """Build (or rebuild) the kernel layout from the pair-bitmask storage."""
+        nb = moesq_kernel_layout_bytes(self.E, self.N, self.K)
+        if self.kl is None or self.kl.numel() < nb:
+            self.kl = torch.empty(nb, dtype=torch.uint8, device=self.packed.device)
+        c = self.cstruct()
+        _check("moesq_prepack_weights", lib().moesq_prepack_weights(_stream(), ctypes.byref(c), _p(self.kl), nb))
+        return self
 
     @classmethod
     def empty(cls, E, N, K, device="cuda"):
@@ -135,7 +150,8 @@ class Weights:
 
     def cstruct(self):
         return _CWeights(self.E, self.N, self.K, self.packed.data_ptr(), self.mask.data_ptr(),
-                         self.scale.data_ptr(), self.gscale.data_ptr())
+                         self.scale.data_ptr(), self.gscale.data_ptr(),
+                         None if self.kl is None else self.kl.data_ptr())
 
     def nbytes(self):
         return self.packed.numel() + self.mask.numel() + self.scale.numel()
@@ -234,8 +250,17 @@ def moesq_unpermute_combine(y_sorted, slot_pos, topk_w, out=None, out_dtype=torc
     return out
 
 
-def moesq_compress_weights(w, out=None, workspace=None, dev_status=None):
-    """fp32 weights [E, N, K] -> Weights (paired-4:8 pruning + NVFP4 + pair-bitmask v1)."""
+def moesq_kernel_layout_bytes(E, N, K):
+    return int(lib().moesq_kernel_layout_bytes(E, N, K))
+
+
+def moesq_prepack_weights(W):
+    return W.prepack()
+
+
+def moesq_compress_weights(w, out=None, workspace=None, dev_status=None, prepack=True):
+    """fp32 weights [E, N, K] -> Weights (paired-4:8 pruning + NVFP4 + pair-bitmask v1), plus the
+    kernel layout when ``prepack`` (and K % 256 == 0)."""
     _dev(w)
     assert w.dtype == torch.float32 and w.is_contiguous()
     E, N, K = w.shape
@@ -245,6 +270,8 @@ def moesq_compress_weights(w, out=None, workspace=None, dev_status=None):
     _check("moesq_compress_weights",
            lib().moesq_compress_weights(_stream(), _p(w), E, N, K, _p(out.packed), _p(out.mask), _p(out.scale),
                                         _p(out.gscale), _p(workspace), workspace.numel(), _p(dev_status)))
+    if prepack and K % 256 == 0 and N % 16 == 0:
+        out.prepack()
     return out
 
 

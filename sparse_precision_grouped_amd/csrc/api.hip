@@ -13,7 +13,7 @@ namespace {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool weights_ok(const moesq_weights* W) {
-  return W && W->E > 0 && W->N > 0 && W->K > 0 && W->packed && W->mask && W->scale && W->gscale;
+  return W && W->E > 0 && W->N > 0 && W->K > 0 && W->kl && W->gscale;
 }
 
 constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -81,6 +81,7 @@ int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, 
     return MOESQ_ERR_INVALID_ARG;
   }
   if (offsets && E <= 0) return MOESQ_ERR_INVALID_ARG;
+  if (offsets && E > 4096) return MOESQ_ERR_UNSUPPORTED;
   if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4)) return MOESQ_ERR_UNSUPPORTED;
   return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, gather_slot, k, rows, gamma,
                          offsets, E, q, s);
@@ -92,10 +93,11 @@ static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* 
   if (rows > 0 && (!q || !s || !y)) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 256 != 0 || W->N % 64 != 0 || W->E > kMaxExpertsGemm) return MOESQ_ERR_UNSUPPORTED;
-  if (!aligned(W->packed, 16) || !aligned(W->mask, 4) || !aligned(W->scale, 2) || !aligned(q, 16) ||
-      !aligned(s, 2) || !aligned(y, 16))
-    return MOESQ_ERR_UNSUPPORTED;
+  if (!aligned(W->kl, 16) || !aligned(q, 16) || !aligned(s, 2) || !aligned(y, 16)) return MOESQ_ERR_UNSUPPORTED;
   if (rows >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: one expert's weights, and all activation rows
+  if ((int64_t)W->N * W->K / 32 * 11 >= ((int64_t)1 << 31) || rows * (W->K / 2) >= ((int64_t)1 << 31))
+    return MOESQ_ERR_UNSUPPORTED;
   return MOESQ_OK;
 }
 
@@ -105,7 +107,7 @@ int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, c
   const int rc = gemm_common(W, q, s, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   GemmArgs a{};
-  a.packed = W->packed; a.mask = W->mask; a.wscale = W->scale; a.gscale = W->gscale;
+  a.kl = W->kl; a.gscale = W->gscale;
   a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
   a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
   if (flags & MOESQ_F_FORCE_DECODE) return launch_gemm_variant((hipStream_t)stream, a, rows, 0);
@@ -123,7 +125,9 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   int rc = gemm_common(W13, q, s, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   if (I % 256 != 0 || W13->K % 256 != 0 || W2->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
-  if (!aligned(W2->packed, 16) || !aligned(W2->mask, 4) || !aligned(W2->scale, 2)) return MOESQ_ERR_UNSUPPORTED;
+  if (!aligned(W2->kl, 16)) return MOESQ_ERR_UNSUPPORTED;
+  if ((int64_t)W2->N * W2->K / 32 * 11 >= ((int64_t)1 << 31) || rows * (I / 2) >= ((int64_t)1 << 31))
+    return MOESQ_ERR_UNSUPPORTED;
   const bool dump = (flags & MOESQ_F_DUMP_GATEUP) != 0;
   const size_t need = mlp_ws(rows, I, dump);
   if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MOESQ_ERR_WORKSPACE;
@@ -132,14 +136,14 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   uint8_t* hs = hq + align256((size_t)rows * (I / 2));
   float* dumpp = dump ? (float*)(hs + align256((size_t)rows * (I / 32))) : nullptr;
   GemmArgs a{};
-  a.packed = W13->packed; a.mask = W13->mask; a.wscale = W13->scale; a.gscale = W13->gscale;
+  a.kl = W13->kl; a.gscale = W13->gscale;
   a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
   a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0;
   a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.dump = dumpp;
   rc = launch_gemm_variant((hipStream_t)stream, a, rows, 1);
   if (rc != MOESQ_OK) return rc;
   GemmArgs b{};
-  b.packed = W2->packed; b.mask = W2->mask; b.wscale = W2->scale; b.gscale = W2->gscale;
+  b.kl = W2->kl; b.gscale = W2->gscale;
   b.q = hq; b.s = hs; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
   b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16;
   return launch_gemm_variant((hipStream_t)stream, b, rows, 1);
@@ -173,6 +177,22 @@ int moesq_compress_weights(void* stream, const float* w, int32_t E, int32_t N, i
     return MOESQ_ERR_WORKSPACE;
   if (!aligned(w, 16) || !aligned(packed, 8) || !aligned(mask, 2)) return MOESQ_ERR_UNSUPPORTED;
   return launch_compress((hipStream_t)stream, w, E, N, K, packed, mask, scale, gscale, workspace, dev_status);
+}
+
+size_t moesq_kernel_layout_bytes(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)E * (size_t)N * (size_t)K / 32 * 11;
+}
+
+int moesq_prepack_weights(void* stream, const moesq_weights* W, uint8_t* kl, size_t kl_bytes) {
+  if (!W || W->E <= 0 || W->N <= 0 || W->K <= 0 || !W->packed || !W->mask || !W->scale || !kl)
+    return MOESQ_ERR_INVALID_ARG;
+  if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
+  if (W->K % 256 != 0 || W->N % 16 != 0) return MOESQ_ERR_UNSUPPORTED;
+  if (kl_bytes < moesq_kernel_layout_bytes(W->E, W->N, W->K)) return MOESQ_ERR_WORKSPACE;
+  if (!aligned(kl, 16) || !aligned(W->packed, 16) || !aligned(W->mask, 4) || !aligned(W->scale, 2))
+    return MOESQ_ERR_UNSUPPORTED;
+  return launch_prepack((hipStream_t)stream, W->packed, W->mask, W->scale, W->E, W->N, W->K, kl);
 }
 
 int moesq_unpack_weights(void* stream, const moesq_weights* W, uint8_t* dense_nvfp4, int32_t* dev_status) {

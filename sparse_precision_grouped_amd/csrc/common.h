@@ -94,22 +94,6 @@ MOESQ_DEV void quant8_block4(const float v[8], float gamma, uint32_t& codes, uin
 MOESQ_DEV uint32_t f16x2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 MOESQ_DEV f16x2 bits_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 
-// Weight operand of one lane for one K-step: word w = the 4 kept bytes of two consecutive 8-groups
-// (bytes 0,1: group 0 pairs i<j; bytes 2,3: group 1), scaled by the block scale sc (f16x2). Output
-// order = de-interleaved 4-groups: (g0 even: lo b0, lo b1), (g0 odd: hi b0, hi b1), same for g1.
-MOESQ_DEV f16x8 decode_w_step(uint32_t w, f16x2 sc) {
-  const uint32_t x0 = f16x2_bits(MOESQ_CVT_FP4(w, 0) * sc);
-  const uint32_t x1 = f16x2_bits(MOESQ_CVT_FP4(w, 1) * sc);
-  const uint32_t x2 = f16x2_bits(MOESQ_CVT_FP4(w, 2) * sc);
-  const uint32_t x3 = f16x2_bits(MOESQ_CVT_FP4(w, 3) * sc);
-  u32x4 o;
-  o.x = __builtin_amdgcn_perm(x1, x0, 0x05040100u);  // (lo x0, lo x1)
-  o.y = __builtin_amdgcn_perm(x1, x0, 0x07060302u);  // (hi x0, hi x1)
-  o.z = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-  o.w = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-  return __builtin_bit_cast(f16x8, o);
-}
-
 // Dense activation 8-group (codes word c: element i in nibble i) -> 4 f16x2 in de-interleaved
 // order (a0,a2), (a4,a6), (a1,a3), (a5,a7), scaled by sc.
 MOESQ_DEV u32x4 decode_x_group(uint32_t c, f16x2 sc) {

@@ -11,11 +11,13 @@
 //    16-bit index word). E2M1 codes are expanded with the gfx950 FP4->f16 convert and multiplied
 //    by the UE4M3 block scale in f16: e2m1 * e4m3 has at most 6 significant bits, so every operand
 //    is exact and the only rounding is the fp32 accumulation.
-//  - K is traversed in super-steps of 256: lane (row r, chunk c) of an A fragment reads 16
-//    contiguous packed bytes, 4 mask bytes and 2 scale bytes of one row (one 128-bit load plus two
-//    small loads straight from the pair-bitmask storage, no repacking), and covers K
-//    [64c + 16s, +16) at step s. The activation (B) operand follows the same K mapping.
-//  - Decode (few tokens per expert): weight streaming. One workgroup = 64 weight rows of one
+//  - Weights are read from the kernel layout built at load time (prepack_kernel): per 16 rows x
+//    256 K fragment, lane (row r, chunk c) finds its 16 packed bytes, 4 mask bytes and 2 scale
+//    bytes at fixed offsets, so a wave reads 1408 contiguous bytes per fragment with three buffer
+//    loads (SGPR fragment offset, no per-lane 64-bit address arithmetic). The lane covers K
+//    [64c + 16s, +16) at step s of the super-step; the activation (B) operand follows the same K
+//    mapping. Buffer loads past an expert's last token return zero, which pads partial tiles.
+//  - Decode (few tokens per expert): weight streaming. One workgroup = 16*MF weight rows of one
 //    expert; its 4 waves split K and reduce through LDS in a fixed order (deterministic).
 //  - Prefill: 256 x 64 tiles (4 waves x 4 m-fragments x 16 rows, 4 n-fragments x 16 tokens);
 //    the activation tile of each super-step is decoded once into LDS (f16, de-interleaved) and
@@ -25,6 +27,8 @@
 //    32-element scale block per token.
 #include "common.h"
 #include "launch.h"
+
+#include <stdlib.h>
 
 namespace moesq {
 
@@ -62,87 +66,161 @@ MOESQ_DEV void store4(void* y, int64_t off, f32x4 v, float alpha, int bf16) {
   }
 }
 
-// ============================================================================ decode kernel =====
-// grid (N / (16*MF), E), 256 threads. Wave w takes super-steps ss = w, w+4, ...; the 4 partial
-// accumulators are summed in wave order. Experts with more than 16 tokens loop over 16-token
-// blocks re-reading their weights (cache-resident after the first pass).
+// ============================================================== operand stages (registers) =====
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+MOESQ_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 256-K super-step of MF A fragments (16 rows each) for one lane.
 template <int MF>
+struct WStage {
+  u32x4 pk[MF];
+  uint32_t mk[MF];
+  uint32_t sw[MF];
+};
+
+// soff[f]: byte offset (wave uniform) of fragment f's first super-step within the expert's layout.
+template <int MF>
+MOESQ_DEV void load_w(WStage<MF>& st, rsrc_t rw, const uint32_t (&soff)[MF], int lane, int ss) {
+#pragma unroll
+  for (int f = 0; f < MF; f++) {
+    const int so = (int)(soff[f] + (uint32_t)ss * kFragBytes);
+    st.pk[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * lane, so, 0));
+    st.mk[f] = __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * lane + 1024, so, 0);
+    st.sw[f] = __builtin_amdgcn_raw_buffer_load_b16(rw, 2 * lane + 1280, so, 0);
+  }
+}
+
+// A operand of step s (0..3) for m-fragment f: the kernel layout's nibble order makes each FP4
+// convert produce one de-interleaved operand register directly.
+template <int MF>
+MOESQ_DEV f16x8 w_frag(const WStage<MF>& w, int f, int s, const DecodeTables& tab, int& idx) {
+  const f16x2 sc = bits_f16x2(tab.scl[(w.sw[f] >> (8 * (s >> 1))) & 0xFFu]);
+  const uint32_t wd = s == 0 ? w.pk[f].x : s == 1 ? w.pk[f].y : s == 2 ? w.pk[f].z : w.pk[f].w;
+  idx = tab.idx[(w.mk[f] >> (8 * s)) & 0xFFu];
+  u32x4 o;
+  o.x = f16x2_bits(MOESQ_CVT_FP4(wd, 0) * sc);
+  o.y = f16x2_bits(MOESQ_CVT_FP4(wd, 1) * sc);
+  o.z = f16x2_bits(MOESQ_CVT_FP4(wd, 2) * sc);
+  o.w = f16x2_bits(MOESQ_CVT_FP4(wd, 3) * sc);
+  return __builtin_bit_cast(f16x8, o);
+}
+
+// Activation operand of one lane for one super-step (decode kernel): for each of the 4 K-steps two
+// 8-groups (codes) and the two block-scale pairs. Rows past the expert's tokens read as zero.
+struct XStage {
+  uint32_t bc[8];
+  uint32_t bs0, bs1;
+};
+
+MOESQ_DEV void load_x(XStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, int ss) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    st.bc[2 * s] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(voq + 128u * ss + 8u * s), 0, 0);
+    st.bc[2 * s + 1] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(voq + 128u * ss + 64u + 8u * s), 0, 0);
+  }
+  st.bs0 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
+  st.bs1 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss + 4u), 0, 0);
+}
+
+template <int MF>
+MOESQ_DEV void mma_superstep_x(f32x4 (&acc)[MF], const WStage<MF>& w, const XStage& x, const DecodeTables& tab) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const f16x2 sb1 = bits_f16x2(tab.scl[(x.bs0 >> (8 * (s >> 1))) & 0xFFu]);
+    const f16x2 sb2 = bits_f16x2(tab.scl[(x.bs1 >> (8 * (s >> 1))) & 0xFFu]);
+    const f16x16 B = concat_x(decode_x_group(x.bc[2 * s], sb1), decode_x_group(x.bc[2 * s + 1], sb2));
+#pragma unroll
+    for (int f = 0; f < MF; f++) {
+      int idx;
+      const f16x8 A = w_frag(w, f, s, tab, idx);
+      acc[f] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A, B, acc[f], idx, 0, 0);
+    }
+  }
+}
+
+MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
+
+// ============================================================================ decode kernel =====
+// Weight streaming for few tokens per expert. Workgroup = 4 waves; a wave owns 16*MF weight rows.
+// KSPLIT = 4: the 4 waves share the same rows and take super-steps ss = w, w+4, ...; their partial
+// sums are added in wave order through LDS (deterministic). KSPLIT = 1: the 4 waves own 4 row
+// blocks and each streams the whole K. Both keep two super-steps of operands in flight per wave
+// (register double buffering). Experts with more than 16 tokens loop over 16-token blocks.
+// grid (N / (16*MF*(4/KSPLIT)), E).
+template <int MF, int KSPLIT>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   __shared__ DecodeTables tab;
-  __shared__ f32x4 red[4][MF][64];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
+  __shared__ f32x4 red[KSPLIT][MF][64];
   const int e = blockIdx.y;
-  init_tables(tab);
   const int off = a.offsets[e];
   const int ne = a.offsets[e + 1] - off;
-  __syncthreads();
   if (ne <= 0) return;
-  const int K = a.K, nss = K / 256;
-  const int n0 = blockIdx.x * (16 * MF);
-  const int64_t row0 = (int64_t)e * a.N + n0 + r16;
-  const uint8_t* P = a.packed + row0 * (K / 4) + 16 * c;
-  const uint8_t* M = a.mask + row0 * (K / 16) + 4 * c;
-  const uint8_t* S = a.wscale + row0 * (K / 32) + 2 * c;
-  const int64_t fP = 16 * (int64_t)(K / 4), fM = 16 * (int64_t)(K / 16), fS = 16 * (int64_t)(K / 32);
+  init_tables(tab);
+  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.K, N = a.N, nss = K / 256;
+  const int rb0 = blockIdx.x * (MF * (4 / KSPLIT)) + (KSPLIT == 1 ? w * MF : 0);
+  const uint32_t ekl = expert_kl_bytes(N, K);
+  const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
+  uint32_t soff[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) soff[f] = (uint32_t)(rb0 + f) * (uint32_t)nss * kFragBytes;
+  const rsrc_t rq = make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
+  const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
   const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
-  const int gB = 32 * (c >> 1) + 4 * (c & 1);  // byte offset of the lane's first activation group (step 0)
+  const int n0 = rb0 * 16;
+  const int ss0 = KSPLIT == 1 ? 0 : w;
   for (int tb = 0; tb < ne; tb += 16) {
     f32x4 acc[MF];
 #pragma unroll
     for (int f = 0; f < MF; f++) acc[f] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const int tok = tb + r16;
     const bool tv = tok < ne;
-    const uint8_t* Q = a.q + (int64_t)(off + (tv ? tok : 0)) * (K / 2) + gB;
-    const uint8_t* SA = a.s + (int64_t)(off + (tv ? tok : 0)) * (K / 32) + 2 * (c >> 1);
-    for (int ss = w; ss < nss; ss += 4) {
-      u32x4 pk[MF];
-      uint32_t mk[MF], sw[MF];
-#pragma unroll
-      for (int f = 0; f < MF; f++) {
-        pk[f] = *(const u32x4*)(P + f * fP + 64 * ss);
-        mk[f] = *(const uint32_t*)(M + f * fM + 16 * ss);
-        sw[f] = *(const uint16_t*)(S + f * fS + 8 * ss);
+    // byte offsets of the lane's first activation group (step 0) and its block scales
+    const uint32_t voq = (uint32_t)tok * (K / 2) + 32u * (c >> 1) + 4u * (c & 1);
+    const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
+    WStage<MF> w0, w1;
+    XStage x0, x1;
+    int ss = ss0;
+    if (ss < nss) {
+      load_w(w0, rw, soff, lane, ss);
+      load_x(x0, rq, rs, voq, vos, ss);
+    }
+    while (ss < nss) {
+      const int s1 = ss + KSPLIT, s2 = ss + 2 * KSPLIT;
+      if (s1 < nss) {
+        load_w(w1, rw, soff, lane, s1);
+        load_x(x1, rq, rs, voq, vos, s1);
       }
-      uint32_t bc[8];
-      uint32_t bs0 = 0u, bs1 = 0u;
+      mma_superstep_x(acc, w0, x0, tab);
+      if (s2 < nss) {
+        load_w(w0, rw, soff, lane, s2);
+        load_x(x0, rq, rs, voq, vos, s2);
+      }
+      if (s1 < nss) mma_superstep_x(acc, w1, x1, tab);
+      ss = s2;
+    }
+    if (KSPLIT == 1) {
       if (tv) {
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-          bc[2 * s] = *(const uint32_t*)(Q + 128 * ss + 8 * s);
-          bc[2 * s + 1] = *(const uint32_t*)(Q + 128 * ss + 64 + 8 * s);
-        }
-        bs0 = *(const uint16_t*)(SA + 8 * ss);
-        bs1 = *(const uint16_t*)(SA + 8 * ss + 4);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; i++) bc[i] = 0u;
+        for (int f = 0; f < MF; f++) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, acc[f], alpha, a.y_bf16);
       }
+    } else {
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        const f16x2 sb1 = bits_f16x2(tab.scl[(bs0 >> (8 * (s >> 1))) & 0xFFu]);
-        const f16x2 sb2 = bits_f16x2(tab.scl[(bs1 >> (8 * (s >> 1))) & 0xFFu]);
-        const f16x16 B = concat_x(decode_x_group(bc[2 * s], sb1), decode_x_group(bc[2 * s + 1], sb2));
+      for (int f = 0; f < MF; f++) red[w][f][lane] = acc[f];
+      __syncthreads();
+      for (int f = w; f < MF; f += 4) {
+        f32x4 sum = red[0][f][lane];
 #pragma unroll
-        for (int f = 0; f < MF; f++) {
-          const f16x2 scw = bits_f16x2(tab.scl[(sw[f] >> (8 * (s >> 1))) & 0xFFu]);
-          const uint32_t wd = s == 0 ? pk[f].x : s == 1 ? pk[f].y : s == 2 ? pk[f].z : pk[f].w;
-          const f16x8 A = decode_w_step(wd, scw);
-          const int idx = tab.idx[(mk[f] >> (8 * s)) & 0xFFu];
-          acc[f] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A, B, acc[f], idx, 0, 0);
-        }
+        for (int v = 1; v < KSPLIT; v++) sum = sum + red[v][f][lane];
+        if (tv) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
       }
+      __syncthreads();
     }
-#pragma unroll
-    for (int f = 0; f < MF; f++) red[w][f][lane] = acc[f];
-    __syncthreads();
-    for (int f = w; f < MF; f += 4) {
-      f32x4 sum = red[0][f][lane];
-      sum = sum + red[1][f][lane];
-      sum = sum + red[2][f][lane];
-      sum = sum + red[3][f][lane];
-      if (tv) store4(a.y, (int64_t)(off + tok) * a.N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
-    }
-    __syncthreads();
   }
 }
 
@@ -181,10 +259,61 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
     run += (offsets[e + 1] - offsets[e] + kPfTokens - 1) / kPfTokens;
   }
   if (hi == E && lo < hi) tile_pre[E] = run;
-  if (E == 0 && tid == 0) tile_pre[0] = 0;
   __syncthreads();
 }
 
+// Activation staging of one super-step (prefill): thread (token tt, part) reads 32 code bytes
+// (8 groups = 64 K) and their two block scales, decodes them to f16 (de-interleaved) into LDS.
+struct PStage {
+  u32x4 cw0, cw1;
+  uint32_t sc2;
+};
+
+MOESQ_DEV void load_p(PStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, int ss) {
+  st.cw0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss), 0, 0));
+  st.cw1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss + 16u), 0, 0));
+  st.sc2 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
+}
+
+MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bw, const DecodeTables& tab) {
+  const f16x2 s0 = bits_f16x2(tab.scl[st.sc2 & 0xFFu]);
+  const f16x2 s1 = bits_f16x2(tab.scl[(st.sc2 >> 8) & 0xFFu]);
+  *(u32x4*)(Bw + 0) = decode_x_group(st.cw0.x, s0);
+  *(u32x4*)(Bw + 16) = decode_x_group(st.cw0.y, s0);
+  *(u32x4*)(Bw + 32) = decode_x_group(st.cw0.z, s0);
+  *(u32x4*)(Bw + 48) = decode_x_group(st.cw0.w, s0);
+  *(u32x4*)(Bw + 64) = decode_x_group(st.cw1.x, s1);
+  *(u32x4*)(Bw + 80) = decode_x_group(st.cw1.y, s1);
+  *(u32x4*)(Bw + 96) = decode_x_group(st.cw1.z, s1);
+  *(u32x4*)(Bw + 112) = decode_x_group(st.cw1.w, s1);
+}
+
+// All MFMAs of one super-step for a wave: A from registers, B from the LDS tile.
+template <int MF, int NF>
+MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const uint8_t* Bs, int r16, int c,
+                                 const DecodeTables& tab) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    f16x8 A[MF];
+    int idx[MF];
+#pragma unroll
+    for (int f = 0; f < MF; f++) A[f] = w_frag(w, f, s, tab, idx[f]);
+    const int g1 = 8 * (c >> 1) + 2 * s + (c & 1);
+#pragma unroll
+    for (int n = 0; n < NF; n++) {
+      const uint8_t* br = Bs + (n * 16 + r16) * kPfRowBytes;
+      const f16x16 B = concat_x(*(const u32x4*)(br + 16 * g1), *(const u32x4*)(br + 16 * (g1 + 16)));
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+        acc[f][n] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[f], B, acc[f][n], idx[f], 0, 0);
+    }
+  }
+}
+
+// Tiled kernel: 256 weight rows (4 waves x 4 m-fragments) x 64 tokens of one expert per workgroup;
+// tile y of the grid maps to (expert, token block) through the per-expert tile prefix. The
+// activation tile is decoded into a double-buffered LDS tile while the previous super-step
+// computes; weights and activation codes of the next super-step are in flight meanwhile.
 template <bool MLP>
 __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = 4;
@@ -192,9 +321,11 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   __shared__ DecodeTables tab;
   __shared__ int32_t part[256];
   __shared__ int32_t tinfo[2];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int32_t* tile_pre = (int32_t*)dyn;                               // [E+1]
-  uint8_t* Bs = dyn + (((a.E + 1) * 4 + 15) / 16) * 16;           // [64][kPfRowBytes]
+  uint8_t* Bs0 = dyn + (((a.E + 1) * 4 + 15) / 16) * 16;          // [64][kPfRowBytes]
+  uint8_t* Bs1 = Bs0 + kPfTokens * kPfRowBytes;
   init_tables(tab);
   build_tile_prefix(a.offsets, a.E, tile_pre, part);
   const int ty = blockIdx.y;
@@ -219,20 +350,25 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   const int ne = a.offsets[e + 1] - off;
   const int K = a.K, N = a.N, nss = K / 256;
 
-  // weight rows of this wave's m-fragments
-  int64_t rowf[MF];
+  // 16-row blocks of this wave's m-fragments: consecutive (plain) or gate / up halves (MLP)
   bool wave_on = true;
+  int rbf[MF];
   if (MLP) {
     const int I = N / 2;
     const int i0 = blockIdx.x * 128 + 32 * w;
 #pragma unroll
-    for (int f = 0; f < MF; f++) rowf[f] = (int64_t)e * N + (f < 2 ? 0 : I) + i0 + 16 * (f & 1) + r16;
+    for (int f = 0; f < MF; f++) rbf[f] = ((f < 2 ? 0 : I) + i0 + 16 * (f & 1)) / 16;
   } else {
     const int n0 = blockIdx.x * 256 + 64 * w;
     wave_on = n0 < N;
 #pragma unroll
-    for (int f = 0; f < MF; f++) rowf[f] = (int64_t)e * N + (wave_on ? n0 + 16 * f : 0) + r16;
+    for (int f = 0; f < MF; f++) rbf[f] = (wave_on ? n0 : 0) / 16 + f;
   }
+  const uint32_t ekl = expert_kl_bytes(N, K);
+  const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
+  uint32_t soff[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) soff[f] = (uint32_t)rbf[f] * (uint32_t)nss * kFragBytes;
   const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
 
   f32x4 acc[MF][NF];
@@ -241,64 +377,38 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // activation staging role: token tt, groups 8*part4 .. +8 of the super-step
+  // staging role: token tt of the tile, groups 8*part4 .. +8 of each super-step
   const int tt = tid >> 2, part4 = tid & 3;
-  const bool st_valid = tb + tt < ne;
-  const uint8_t* Qs = a.q + (int64_t)(off + (st_valid ? tb + tt : 0)) * (K / 2) + 32 * part4;
-  const uint8_t* Ss = a.s + (int64_t)(off + (st_valid ? tb + tt : 0)) * (K / 32) + 2 * part4;
-  uint8_t* Bw = Bs + tt * kPfRowBytes + part4 * 8 * 16;
+  const rsrc_t rq = make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
+  const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
+  const uint32_t voq = (uint32_t)(tb + tt) * (K / 2) + 32u * part4;
+  const uint32_t vos = (uint32_t)(tb + tt) * (K / 32) + 2u * part4;
+  const int bw_off = tt * kPfRowBytes + part4 * 8 * 16;
 
-  for (int ss = 0; ss < nss; ss++) {
-    u32x4 pk[MF];
-    uint32_t mk[MF], sw[MF];
-    if (wave_on) {
-#pragma unroll
-      for (int f = 0; f < MF; f++) {
-        pk[f] = *(const u32x4*)(a.packed + rowf[f] * (K / 4) + 64 * ss + 16 * c);
-        mk[f] = *(const uint32_t*)(a.mask + rowf[f] * (K / 16) + 16 * ss + 4 * c);
-        sw[f] = *(const uint16_t*)(a.wscale + rowf[f] * (K / 32) + 8 * ss + 2 * c);
-      }
+  WStage<MF> wa0, wa1;
+  PStage p0, p1;
+  if (wave_on) load_w(wa0, rw, soff, lane, 0);
+  load_p(p0, rq, rs, voq, vos, 0);
+  stage_p(p0, Bs0 + bw_off, tab);
+  __syncthreads();
+  for (int ss = 0; ss < nss; ss += 2) {
+    const bool has1 = ss + 1 < nss, has2 = ss + 2 < nss;
+    if (has1) {
+      if (wave_on) load_w(wa1, rw, soff, lane, ss + 1);
+      load_p(p1, rq, rs, voq, vos, ss + 1);
     }
-    // stage + decode the activation tile of this super-step
-    {
-      u32x4 cw0 = (u32x4){0u, 0u, 0u, 0u}, cw1 = cw0;
-      uint32_t sc2 = 0u;
-      if (st_valid) {
-        cw0 = *(const u32x4*)(Qs + 128 * ss);
-        cw1 = *(const u32x4*)(Qs + 128 * ss + 16);
-        sc2 = *(const uint16_t*)(Ss + 8 * ss);
-      }
-      const f16x2 s0 = bits_f16x2(tab.scl[sc2 & 0xFFu]);
-      const f16x2 s1 = bits_f16x2(tab.scl[sc2 >> 8]);
-      const uint32_t cws[8] = {cw0.x, cw0.y, cw0.z, cw0.w, cw1.x, cw1.y, cw1.z, cw1.w};
-#pragma unroll
-      for (int g = 0; g < 8; g++) *(u32x4*)(Bw + 16 * g) = decode_x_group(cws[g], g < 4 ? s0 : s1);
-    }
+    if (wave_on) mma_superstep_lds<MF, NF>(acc, wa0, Bs0, r16, c, tab);
+    if (has1) stage_p(p1, Bs1 + bw_off, tab);
     __syncthreads();
-    if (wave_on) {
-#pragma unroll
-      for (int s = 0; s < 4; s++) {
-        f16x8 A[MF];
-        int idx[MF];
-#pragma unroll
-        for (int f = 0; f < MF; f++) {
-          const f16x2 scw = bits_f16x2(tab.scl[(sw[f] >> (8 * (s >> 1))) & 0xFFu]);
-          const uint32_t wd = s == 0 ? pk[f].x : s == 1 ? pk[f].y : s == 2 ? pk[f].z : pk[f].w;
-          A[f] = decode_w_step(wd, scw);
-          idx[f] = tab.idx[(mk[f] >> (8 * s)) & 0xFFu];
-        }
-        const int g1 = 8 * (c >> 1) + 2 * s + (c & 1);
-#pragma unroll
-        for (int n = 0; n < NF; n++) {
-          const uint8_t* br = Bs + (n * 16 + r16) * kPfRowBytes;
-          const f16x16 B = concat_x(*(const u32x4*)(br + 16 * g1), *(const u32x4*)(br + 16 * (g1 + 16)));
-#pragma unroll
-          for (int f = 0; f < MF; f++)
-            acc[f][n] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[f], B, acc[f][n], idx[f], 0, 0);
-        }
+    if (has1) {
+      if (has2) {
+        if (wave_on) load_w(wa0, rw, soff, lane, ss + 2);
+        load_p(p0, rq, rs, voq, vos, ss + 2);
       }
+      if (wave_on) mma_superstep_lds<MF, NF>(acc, wa1, Bs1, r16, c, tab);
+      if (has2) stage_p(p0, Bs0 + bw_off, tab);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (!wave_on) return;
@@ -365,12 +475,35 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
   }
 }
 
-static size_t prefill_lds_bytes(int E) { return (size_t)(((E + 1) * 4 + 15) / 16) * 16 + (size_t)kPfTokens * kPfRowBytes; }
+static size_t prefill_lds_bytes(int E) {
+  return (size_t)(((E + 1) * 4 + 15) / 16) * 16 + 2 * (size_t)kPfTokens * kPfRowBytes;
+}
+
+// Decode variants: MF (rows per wave / 16) and KSPLIT. The default is picked by measurement; the
+// environment variable MOESQ_DECODE_VARIANT (0..3) overrides it for tuning.
+static int decode_variant_default() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MOESQ_DECODE_VARIANT");
+    v = e ? atoi(e) : 0;
+    if (v < 0 || v > 3) v = 0;
+  }
+  return v;
+}
 
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
   if (rows == 0) return MOESQ_OK;
   if (variant == 0) {
-    hipLaunchKernelGGL(gemm_decode_kernel<4>, dim3(a.N / 64, a.E), dim3(256), 0, st, a);
+    int v = decode_variant_default();
+    // KSPLIT = 1 needs N to be a multiple of the 4-wave row block
+    if ((v == 2 && a.N % 256 != 0) || (v == 3 && a.N % 512 != 0)) v = 0;
+    if (v == 1 && a.N % 128 != 0) v = 0;
+    switch (v) {
+      case 0: hipLaunchKernelGGL((gemm_decode_kernel<4, 4>), dim3(a.N / 64, a.E), dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((gemm_decode_kernel<8, 4>), dim3(a.N / 128, a.E), dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((gemm_decode_kernel<4, 1>), dim3(a.N / 256, a.E), dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((gemm_decode_kernel<8, 1>), dim3(a.N / 512, a.E), dim3(256), 0, st, a); break;
+    }
   } else {
     const int64_t tiles = (rows + kPfTokens - 1) / kPfTokens + a.E;
     const size_t lds = prefill_lds_bytes(a.E);

@@ -11,10 +11,10 @@ constexpr int64_t kRouteSingleMax = 8192;  // slots handled by the one-workgroup
 constexpr int32_t kMaxExpertsRoute = 512;
 constexpr int32_t kMaxExpertsGemm = 4096;
 
+constexpr int kFragBytes = 1408;  // 16 rows x 256 K of the kernel weight layout
+
 struct GemmArgs {
-  const uint8_t* packed;  // [E][N][K/4]
-  const uint8_t* mask;    // [E][N][K/16]
-  const uint8_t* wscale;  // [E][N][K/32]
+  const uint8_t* kl;      // kernel layout [E][N/16][K/256][1408 B]
   const float* gscale;    // [E]
   const uint8_t* q;       // [rows][K/2]
   const uint8_t* s;       // [rows][K/32]
@@ -43,6 +43,8 @@ int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows
 
 int launch_compress(hipStream_t st, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
                     uint8_t* scale, float* gscale, void* ws, int32_t* dev_status);
+int launch_prepack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, const uint8_t* scale, int32_t E,
+                   int32_t N, int32_t K, uint8_t* kl);
 int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, int32_t E, int32_t N, int32_t K,
                   uint8_t* dense, int32_t* dev_status);
 

@@ -9,59 +9,71 @@
 
 namespace moesq {
 
-// One wave per permuted row; each lane quantizes 8 consecutive values, four lanes per 32-block
-// (block amax by a 4-lane max reduction across the wave's lanes).
+// One wave quantizes one 512-element chunk of one permuted row (64 lanes x 8 values); each lane
+// quantizes 8 consecutive values, four lanes per 32-block (block amax by a 4-lane max reduction).
+// The workgroup (4 waves) first copies the expert offsets into LDS so that the expert of a row is
+// found by a binary search in LDS, not by a chain of dependent global loads.
+constexpr int kQuantMaxE = 4096;
+
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K,
                                                        int64_t ld_x, const int32_t* __restrict__ gather, int32_t k,
                                                        int64_t rows, const float* __restrict__ gamma,
                                                        const int32_t* __restrict__ offsets, int32_t E,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  __shared__ int32_t off_l[kQuantMaxE + 1];
   const int lane = threadIdx.x & 63;
-  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nchunk = (K + 511) / 512;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t p = wid / nchunk;
+  const int chunk = (int)(wid % nchunk);
+  if (offsets) {
+    for (int i = threadIdx.x; i <= E; i += 256) off_l[i] = offsets[i];
+    __syncthreads();
+  }
   if (p >= rows) return;
   int64_t t = p;
   if (gather) {
-    if (offsets && p >= offsets[E]) return;  // slot dropped by routing (invalid id)
+    if (offsets && p >= off_l[E]) return;  // slot dropped by routing (invalid id)
     t = gather[p] / k;
     if (t < 0 || t >= T) return;
   }
-  float g = gamma[0];
+  float g;
   if (offsets) {
     int lo = 0, hi = E - 1;  // largest e with offsets[e] <= p
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (offsets[mid] <= p) lo = mid; else hi = mid - 1;
+      if (off_l[mid] <= p) lo = mid; else hi = mid - 1;
     }
     g = gamma[lo];
+  } else {
+    g = gamma[0];
   }
-  const int nch = K / 8;
-  for (int ch = lane; ch - lane < nch; ch += 64) {
-    const bool valid = ch < nch;
-    float v[8];
+  const int ch = chunk * 64 + lane;  // 8-value group index within the row
+  const bool valid = ch < K / 8;
+  float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    if (valid) {
-      if (x_bf16) {
-        const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int i = 0; i < 8; i++) v[i] = 0.0f;
+  if (valid) {
+    if (x_bf16) {
+      const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
-          v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
-        }
-      } else {
-        const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
-        const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      for (int i = 0; i < 4; i++) {
+        v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
       }
+    } else {
+      const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
+      const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
-    uint32_t codes, sc;
-    quant8_block4(v, g, codes, sc);
-    if (valid) {
-      *(uint32_t*)(q + p * (K / 2) + 4 * ch) = codes;
-      if ((lane & 3) == 0) s[p * (K / 32) + ch / 4] = (uint8_t)sc;
-    }
+  }
+  uint32_t codes, sc;
+  quant8_block4(v, g, codes, sc);
+  if (valid) {
+    *(uint32_t*)(q + p * (K / 2) + 4 * ch) = codes;
+    if ((lane & 3) == 0) s[p * (K / 32) + ch / 4] = (uint8_t)sc;
   }
 }
 
@@ -69,7 +81,8 @@ int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32
                     const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
                     int32_t E, uint8_t* q, uint8_t* s) {
   if (rows == 0) return MOESQ_OK;
-  const int64_t blocks = (rows + 3) / 4;
+  const int64_t waves = rows * ((K + 511) / 512);
+  const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x,
                      gather_slot, k, rows, gamma, offsets, E, q, s);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
@@ -240,6 +253,57 @@ int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, in
   if (nchunks == 0) return MOESQ_OK;
   hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st, packed, mask, nchunks,
                      dense, dev_status);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ kernel layout -----------------
+// Load-time repack of pair-bitmask v1 weights into the GEMM's fragment layout (same bytes, 2.75
+// bits per weight). Fragment (e, rb, ss) covers rows 16rb..16rb+15 and K [256ss, +256) and holds,
+// for lane l = 16c + r (row 16rb + r, K [256ss + 64c, +64)):
+//   [16 l, +16)        the 16 packed bytes of the lane's eight 8-groups, each group's two kept
+//                      bytes (b0, b1) rewritten as (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4), so one
+//                      FP4->f16 convert yields a de-interleaved 2:4 operand register;
+//   [1024 + 4 l, +4)   the 4 mask bytes (pair nibbles, unchanged);
+//   [1280 + 2 l, +2)   the 2 UE4M3 block-scale codes.
+// Fragments are stored e-major, then rb, then ss, so one wave streams K with contiguous reads.
+__global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict__ packed,
+                                                      const uint8_t* __restrict__ mask,
+                                                      const uint8_t* __restrict__ scale, int32_t N, int32_t K,
+                                                      int64_t nfrag, uint8_t* __restrict__ kl) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nfrag * 64) return;
+  const int64_t frag = i >> 6;
+  const int l = (int)(i & 63), r = l & 15, c = l >> 4;
+  const int nss = K / 256;
+  const int64_t ss = frag % nss;
+  const int64_t rowblk = frag / nss;               // e * (N/16) + rb
+  const int64_t row = rowblk * 16 + r;             // e * N + 16 rb + r
+  const uint4 pk = *(const uint4*)(packed + row * (K / 4) + 64 * ss + 16 * c);
+  const uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    // two groups per word: bytes (b0, b1) of group 0 and (b2, b3) of group 1
+    const uint32_t lo = w[j] & 0x0F0F0F0Fu, hi = (w[j] >> 4) & 0x0F0F0F0Fu;
+    // lo holds (lo b0, lo b1, lo b2, lo b3) in the low nibbles of bytes 0..3; pack pairs of bytes
+    const uint32_t l01 = (lo & 0xFFu) | ((lo >> 4) & 0xF0u);           // lo b0 | lo b1 << 4
+    const uint32_t h01 = (hi & 0xFFu) | ((hi >> 4) & 0xF0u);
+    const uint32_t l23 = ((lo >> 16) & 0xFFu) | ((lo >> 20) & 0xF0u);
+    const uint32_t h23 = ((hi >> 16) & 0xFFu) | ((hi >> 20) & 0xF0u);
+    o[j] = l01 | (h01 << 8) | (l23 << 16) | (h23 << 24);
+  }
+  uint8_t* F = kl + frag * 1408;
+  *(uint4*)(F + 16 * l) = make_uint4(o[0], o[1], o[2], o[3]);
+  *(uint32_t*)(F + 1024 + 4 * l) = *(const uint32_t*)(mask + row * (K / 16) + 16 * ss + 4 * c);
+  *(uint16_t*)(F + 1280 + 2 * l) = *(const uint16_t*)(scale + row * (K / 32) + 8 * ss + 2 * c);
+}
+
+int launch_prepack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, const uint8_t* scale, int32_t E,
+                   int32_t N, int32_t K, uint8_t* kl) {
+  const int64_t nfrag = (int64_t)E * (N / 16) * (K / 256);
+  if (nfrag == 0) return MOESQ_OK;
+  hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)((nfrag * 64 + 255) / 256)), dim3(256), 0, st, packed, mask, scale,
+                     N, K, nfrag, kl);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

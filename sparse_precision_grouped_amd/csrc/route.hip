@@ -10,9 +10,9 @@
 
 namespace moesq {
 
-constexpr int kRouteThreads = 1024;  // 16 waves
-constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteThreads = 1024;  // multi-block path: 16 waves
 constexpr int kRouteChunk = 4096;    // slots per block in the multi-block path
+constexpr int kSmallThreads = 256;   // single-workgroup path: 4 waves
 
 // Rank of this lane among the lanes of its wave holding the same key (lower lanes first), and the
 // number of such lanes. Lanes with valid == false take no part. The loop runs once per distinct key.
@@ -33,12 +33,14 @@ MOESQ_DEV void wave_match_rank(int key, bool valid, int& rank, int& count) {
   }
 }
 
-// Scatter one round of up to kRouteThreads consecutive slots starting at `base_slot`, given the
-// running per-expert positions pos_base[e] (LDS). Waves are ordered: wave w's slots come after
-// waves 0..w-1 of the same round. wave_tab is LDS [kRouteWaves][E].
+// Scatter one round of up to THREADS consecutive slots starting at `base_slot`, given the running
+// per-expert positions pos_base[e] (LDS). Waves are ordered: wave w's slots come after waves
+// 0..w-1 of the same round. wave_tab is LDS [THREADS/64][E].
+template <int THREADS>
 MOESQ_DEV void scatter_round(const int32_t* __restrict__ ids, int64_t n, int64_t base_slot, int32_t E,
                              int32_t* pos_base, int32_t* wave_tab, int32_t* __restrict__ sorted_slot,
                              int32_t* __restrict__ slot_pos, int32_t* dev_status) {
+  constexpr int WAVES = THREADS / 64;
   const int tid = threadIdx.x, w = tid >> 6;
   const int64_t f = base_slot + tid;
   int e = -1;
@@ -48,16 +50,17 @@ MOESQ_DEV void scatter_round(const int32_t* __restrict__ ids, int64_t n, int64_t
     slot_pos[f] = -1;
     if (dev_status) *dev_status = MOESQ_ERR_INVALID_ARG;
   }
-  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wave_tab[i] = 0;
+  for (int i = tid; i < WAVES * E; i += THREADS) wave_tab[i] = 0;
   __syncthreads();
   int rank, count;
   wave_match_rank(e, valid, rank, count);
   if (valid && rank == count - 1) wave_tab[w * E + e] = count;  // one writer per (wave, expert)
   __syncthreads();
   // exclusive prefix over waves per expert, then advance pos_base
-  for (int x = tid; x < E; x += kRouteThreads) {
+  for (int x = tid; x < E; x += THREADS) {
     int run = pos_base[x];
-    for (int v = 0; v < kRouteWaves; v++) {
+#pragma unroll
+    for (int v = 0; v < WAVES; v++) {
       const int c = wave_tab[v * E + x];
       wave_tab[v * E + x] = run;
       run += c;
@@ -70,63 +73,73 @@ MOESQ_DEV void scatter_round(const int32_t* __restrict__ ids, int64_t n, int64_t
     sorted_slot[p] = (int32_t)f;
     slot_pos[f] = p;
   }
-  __syncthreads();
 }
 
-// Exclusive block scan of counts[0..E) held in LDS `vals`, written to offsets[0..E] (global) and
-// to LDS `out` (E+1 entries). Serial per thread over a contiguous range, then a scan of the
-// per-thread sums.
-MOESQ_DEV void block_exclusive_scan(const int32_t* vals, int32_t E, int32_t* out, int32_t* tmp) {
-  const int tid = threadIdx.x;
-  const int per = (E + kRouteThreads - 1) / kRouteThreads;
-  const int lo = tid * per, hi = min(E, lo + per);
+// Exclusive scan of vals[0..E) (LDS) into out[0..E] (LDS, out[E] = total) by a block of THREADS:
+// each thread sums a contiguous range, wave shuffles scan the per-thread sums, one LDS exchange
+// combines the waves.
+template <int THREADS>
+MOESQ_DEV void block_exclusive_scan(const int32_t* vals, int32_t E, int32_t* out, int32_t* wsum) {
+  constexpr int WAVES = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (E + THREADS - 1) / THREADS;
+  const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; i++) sum += vals[i];
-  tmp[tid] = sum;
-  __syncthreads();
-  for (int d = 1; d < kRouteThreads; d <<= 1) {  // Hillis-Steele over 1024 partial sums
-    const int v = tid >= d ? tmp[tid - d] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
   }
-  int run = tmp[tid] - sum;
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; v++) before += (v < w) ? wsum[v] : 0;
+  int run = before + incl - sum;
   for (int i = lo; i < hi; i++) {
     out[i] = run;
     run += vals[i];
   }
-  if (tid == kRouteThreads - 1) out[E] = tmp[tid];
+  if (tid == THREADS - 1) {
+    int tot = 0;
+#pragma unroll
+    for (int v = 0; v < WAVES; v++) tot += wsum[v];
+    out[E] = tot;
+  }
   __syncthreads();
 }
 
-// Single-workgroup path: histogram, scan and all scatter rounds in one launch.
-__global__ __launch_bounds__(kRouteThreads) void route_single_kernel(const int32_t* __restrict__ ids, int64_t n,
+// Single-workgroup path (4 waves): histogram, scan and all scatter rounds in one launch.
+__global__ __launch_bounds__(kSmallThreads) void route_single_kernel(const int32_t* __restrict__ ids, int64_t n,
                                                                      int32_t E, int32_t* __restrict__ counts,
                                                                      int32_t* __restrict__ offsets,
                                                                      int32_t* __restrict__ sorted_slot,
                                                                      int32_t* __restrict__ slot_pos,
                                                                      int32_t* dev_status) {
   extern __shared__ int32_t lds[];
-  int32_t* hist = lds;                  // [E]
-  int32_t* pos = hist + E;              // [E+1]
-  int32_t* tmp = pos + E + 1;           // [kRouteThreads]
-  int32_t* wave_tab = tmp + kRouteThreads;  // [kRouteWaves * E]
+  int32_t* hist = lds;                        // [E]
+  int32_t* pos = hist + E;                    // [E+1]
+  int32_t* wave_tab = pos + E + 1;            // [4 * E]
+  __shared__ int32_t wsum[kSmallThreads / 64];
   const int tid = threadIdx.x;
-  for (int i = tid; i < E; i += kRouteThreads) hist[i] = 0;
+  for (int i = tid; i < E; i += kSmallThreads) hist[i] = 0;
   __syncthreads();
-  for (int64_t f = tid; f < n; f += kRouteThreads) {
+  for (int64_t f = tid; f < n; f += kSmallThreads) {
     const int e = ids[f];
     if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
-  block_exclusive_scan(hist, E, pos, tmp);
-  for (int i = tid; i <= E; i += kRouteThreads) {
+  block_exclusive_scan<kSmallThreads>(hist, E, pos, wsum);
+  for (int i = tid; i <= E; i += kSmallThreads) {
     offsets[i] = pos[i];
     if (i < E) counts[i] = hist[i];
   }
-  __syncthreads();
-  for (int64_t b = 0; b < n; b += kRouteThreads)
-    scatter_round(ids, n, b, E, pos, wave_tab, sorted_slot, slot_pos, dev_status);
+  for (int64_t b = 0; b < n; b += kSmallThreads) {
+    scatter_round<kSmallThreads>(ids, n, b, E, pos, wave_tab, sorted_slot, slot_pos, dev_status);
+    __syncthreads();
+  }
 }
 
 // Multi-block path, step 1: per-chunk histograms hist[chunk][E].
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int32_t* __re
   extern __shared__ int32_t lds[];
   int32_t* tot = lds;          // [E]
   int32_t* pos = tot + E;      // [E+1]
-  int32_t* tmp = pos + E + 1;  // [kRouteThreads]
+  __shared__ int32_t wsum[kRouteThreads / 64];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kRouteThreads) {
     int run = 0;
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int32_t* __re
     tot[e] = run;
   }
   __syncthreads();
-  block_exclusive_scan(tot, E, pos, tmp);
+  block_exclusive_scan<kRouteThreads>(tot, E, pos, wsum);
   for (int e = tid; e <= E; e += kRouteThreads) {
     offsets[e] = pos[e];
     if (e < E) counts[e] = tot[e];
@@ -182,22 +195,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
                                                                       int32_t* dev_status) {
   extern __shared__ int32_t lds[];
   int32_t* pos = lds;                // [E]
-  int32_t* wave_tab = pos + E;       // [kRouteWaves * E]
+  int32_t* wave_tab = pos + E;       // [16 * E]
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kRouteThreads) pos[e] = base_g[(int64_t)blockIdx.x * E + e];
   __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * kRouteChunk;
   const int64_t hi = min(n, lo + kRouteChunk);
-  for (int64_t b = lo; b < hi; b += kRouteThreads)
-    scatter_round(ids, hi, b, E, pos, wave_tab, sorted_slot, slot_pos, dev_status);
+  for (int64_t b = lo; b < hi; b += kRouteThreads) {
+    scatter_round<kRouteThreads>(ids, hi, b, E, pos, wave_tab, sorted_slot, slot_pos, dev_status);
+    __syncthreads();
+  }
 }
 
-static size_t route_single_lds(int32_t E) {
-  return sizeof(int32_t) * ((size_t)E + (E + 1) + kRouteThreads + (size_t)kRouteWaves * E);
-}
+static size_t route_single_lds(int32_t E) { return sizeof(int32_t) * ((size_t)E + (E + 1) + 4 * (size_t)E); }
 
 size_t route_workspace_bytes(int64_t n, int32_t E) {
-  if (route_single_lds(E) <= 64 * 1024 && n <= kRouteSingleMax) return 0;
+  if (n <= kRouteSingleMax) return 0;
   const int64_t chunks = (n + kRouteChunk - 1) / kRouteChunk;
   return sizeof(int32_t) * (size_t)chunks * (size_t)E;
 }
@@ -205,18 +218,18 @@ size_t route_workspace_bytes(int64_t n, int32_t E) {
 int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t* counts, int32_t* offsets,
                  int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status) {
   if (route_workspace_bytes(n, E) == 0) {
-    hipLaunchKernelGGL(route_single_kernel, dim3(1), dim3(kRouteThreads), route_single_lds(E), st, ids, n, E,
+    hipLaunchKernelGGL(route_single_kernel, dim3(1), dim3(kSmallThreads), route_single_lds(E), st, ids, n, E,
                        counts, offsets, sorted_slot, slot_pos, dev_status);
     return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
   }
   const int32_t chunks = (int32_t)((n + kRouteChunk - 1) / kRouteChunk);
   int32_t* hist = (int32_t*)ws;
   hipLaunchKernelGGL(route_hist_kernel, dim3(chunks), dim3(kRouteThreads), sizeof(int32_t) * E, st, ids, n, E, hist);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads),
-                     sizeof(int32_t) * ((size_t)E + E + 1 + kRouteThreads), st, hist, chunks, E, counts, offsets);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), sizeof(int32_t) * ((size_t)E + E + 1), st,
+                     hist, chunks, E, counts, offsets);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(chunks), dim3(kRouteThreads),
-                     sizeof(int32_t) * ((size_t)E + (size_t)kRouteWaves * E), st, ids, n, E, hist, sorted_slot,
-                     slot_pos, dev_status);
+                     sizeof(int32_t) * ((size_t)E + 16 * (size_t)E), st, ids, n, E, hist, sorted_slot, slot_pos,
+                     dev_status);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

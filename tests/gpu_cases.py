@@ -70,7 +70,9 @@ def device_weights(cfg, proj, E, N, K, host_draw):
         for j in range(n):
             gen.gpu_fill_normal(buf[j], cfg.seed, gen.weight_stream(proj, e0 + j), cfg.w_std)
         sub = mq.Weights(Wd.packed[e0:e0 + n], Wd.mask[e0:e0 + n], Wd.scale[e0:e0 + n], Wd.gscale[e0:e0 + n])
-        mq.moesq_compress_weights(buf[:n].contiguous() if n < buf.shape[0] else buf, out=sub, workspace=ws)
+        mq.moesq_compress_weights(buf[:n].contiguous() if n < buf.shape[0] else buf, out=sub, workspace=ws,
+                                  prepack=False)
+    Wd.prepack()
     torch.cuda.synchronize()
     return Wd, None
 

@@ -100,32 +100,51 @@ def test_gemm_and_mlp_validation(L):
     class CW(ctypes.Structure):
         _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                     ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                    ("gscale", ctypes.c_void_p)]
+                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
     vp = ctypes.c_void_p
     g = L.moesq_grouped_gemm
     g.argtypes = [vp, ctypes.POINTER(CW), vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, ctypes.c_uint32]
-    W = CW(4, 128, 256, FAKE, FAKE, FAKE, FAKE)
+    W = CW(4, 128, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
     call = lambda W, y=FAKE, dt=0: g(None, ctypes.byref(W), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(y),  # noqa
                                      dt, 0)
     assert call(W, dt=3) == EARG
     assert call(W, y=0) == EARG
-    assert call(CW(4, 128, 240, FAKE, FAKE, FAKE, FAKE)) == EARG     # K % 32 != 0
-    assert call(CW(4, 128, 96, FAKE, FAKE, FAKE, FAKE)) == EUNS      # K % 256 != 0
-    assert call(CW(4, 100, 256, FAKE, FAKE, FAKE, FAKE)) == EUNS     # N % 64 != 0
-    assert call(CW(4, 128, 256, 0, FAKE, FAKE, FAKE)) == EARG        # null packed
+    assert call(CW(4, 128, 240, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG     # K % 32 != 0
+    assert call(CW(4, 128, 96, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS      # K % 256 != 0
+    assert call(CW(4, 100, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS     # N % 64 != 0
+    assert call(CW(4, 128, 256, 0, 0, 0, FAKE, 0)) == EARG            # no kernel layout
     m = L.moesq_expert_mlp
     m.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                   ctypes.c_int32, vp, ctypes.c_size_t, ctypes.c_uint32]
-    W13 = CW(4, 512, 256, FAKE, FAKE, FAKE, FAKE)
-    W2 = CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE)
+    W13 = CW(4, 512, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
+    W2 = CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
     mc = lambda a, b, ws=FAKE, wsb=1 << 30: m(None, ctypes.byref(a), ctypes.byref(b), _p(FAKE), _p(FAKE),  # noqa
                                              _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(FAKE), 0,
                                              _p(ws) if ws else None, wsb, 0)
-    assert mc(W13, CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE)) == EARG   # W2.K != I
-    assert mc(W13, CW(3, 256, 256, FAKE, FAKE, FAKE, FAKE)) == EARG   # expert count mismatch
+    assert mc(W13, CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # W2.K != I
+    assert mc(W13, CW(3, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # expert count mismatch
     assert mc(W13, W2, ws=0) == EWS
     assert mc(W13, W2, wsb=10) == EWS
-    assert mc(CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE), CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE)) == EUNS  # I = 128
+    assert mc(CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE), CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS  # I = 128
+
+
+def test_prepack_validation_and_size(L):
+    class CW(ctypes.Structure):
+        _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                    ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
+    vp = ctypes.c_void_p
+    L.moesq_kernel_layout_bytes.restype = ctypes.c_size_t
+    L.moesq_kernel_layout_bytes.argtypes = [ctypes.c_int32] * 3
+    assert L.moesq_kernel_layout_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 11 // 32
+    f = L.moesq_prepack_weights
+    f.argtypes = [vp, ctypes.POINTER(CW), vp, ctypes.c_size_t]
+    W = CW(2, 32, 512, FAKE, FAKE, FAKE, FAKE, 0)
+    need = L.moesq_kernel_layout_bytes(2, 32, 512)
+    assert f(None, ctypes.byref(W), None, need) == EARG
+    assert f(None, ctypes.byref(W), _p(FAKE), need - 1) == EWS
+    assert f(None, ctypes.byref(CW(2, 32, 480, FAKE, FAKE, FAKE, FAKE, 0)), _p(FAKE), 1 << 20) == EUNS
+    assert f(None, ctypes.byref(CW(2, 24, 512, FAKE, FAKE, FAKE, FAKE, 0)), _p(FAKE), 1 << 20) == EUNS
 
 
 def test_combine_compress_unpack_validation(L):

@@ -75,6 +75,35 @@ def test_compress_edge_patterns():
     assert np.array_equal(host(dense), orc.unpack(W["packed"], W["mask"]))
 
 
+def _kernel_layout_reference(packed, mask, scale):
+    """The kernel weight layout built with numpy from its definition (a byte permutation plus the
+    per-pair nibble interleave), independent of the device prepack."""
+    E, N, K4 = packed.shape
+    K = K4 * 4
+    nss = K // 256
+    out = np.zeros((E, N // 16, nss, 1408), np.uint8)
+    pk = packed.reshape(E, N // 16, 16, nss, 4, 16)            # [e, rb, r, ss, c, 16 bytes]
+    b0, b1 = pk[..., 0::2], pk[..., 1::2]
+    sh = np.empty_like(pk)
+    sh[..., 0::2] = (b0 & 15) | ((b1 & 15) << 4)
+    sh[..., 1::2] = (b0 >> 4) | (b1 & 0xF0)
+    out[..., :1024] = sh.transpose(0, 1, 3, 4, 2, 5).reshape(E, N // 16, nss, 1024)
+    mk = mask.reshape(E, N // 16, 16, nss, 4, 4).transpose(0, 1, 3, 4, 2, 5)
+    out[..., 1024:1280] = mk.reshape(E, N // 16, nss, 256)
+    sc = scale.reshape(E, N // 16, 16, nss, 4, 2).transpose(0, 1, 3, 4, 2, 5)
+    out[..., 1280:] = sc.reshape(E, N // 16, nss, 128)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("name", ["c0", "t_zipf"])
+def test_prepack_kernel_layout(name):
+    c = single_case(name)
+    say("prepack", name)
+    Wd = c["Wd"]
+    ref = _kernel_layout_reference(host(Wd.packed), host(Wd.mask), host(Wd.scale))
+    assert np.array_equal(host(Wd.kl), ref)
+
+
 def test_unpack_roundtrip_and_bad_nibble():
     c = single_case("c0")
     say("unpack c0")
