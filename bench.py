@@ -86,6 +86,7 @@ class Workload:
         self.kind = "mlp" if cfg.mlp else ("pair" if cfg.N2 else "single")
         E, T, k = cfg.E, cfg.T, cfg.k
         self.rows = T * k
+        self.tiled = self.kind == "mlp" or self.rows > 16 * E
         # weights: compressed once on the device, then copied for rotation
         self.W = self._weights(0, cfg.N, cfg.K)
         self.W2 = self._weights(1, cfg.N2, cfg.K2) if self.kind != "single" else None
@@ -108,6 +109,9 @@ class Workload:
                                          device=dev)
             sl["q"] = torch.empty((self.rows, cfg.K // 2), dtype=torch.uint8, device=dev)
             sl["s"] = torch.empty((self.rows, cfg.K // 32), dtype=torch.uint8, device=dev)
+            # the tiled (prefill) kernel reads the f16 operand copy written by the quantizer
+            sl["xk"] = (torch.empty((self.rows, cfg.K), dtype=torch.float16, device=dev)
+                        if self.tiled else None)
             if self.kind == "single":
                 sl["y"] = torch.empty((self.rows, cfg.N), dtype=torch.bfloat16, device=dev)
             elif self.kind == "pair":
@@ -155,9 +159,9 @@ class Workload:
         mq.moesq_route_permute(sl["ids"], cfg.E, rt["counts"], rt["offsets"], rt["sorted_slot"], rt["slot_pos"],
                                sl["ws_route"])
         mq.moesq_quantize_act(sl["x"], sl["ga"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
-                              q=sl["q"], s=sl["s"])
+                              q=sl["q"], s=sl["s"], xk=sl["xk"])
         if self.kind == "single":
-            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
         elif self.kind == "pair":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
             mq.moesq_quantize_act(sl["x2"], sl["ga2"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
@@ -165,7 +169,7 @@ class Workload:
             mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"])
         else:
             mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
-                                y=sl["y2"], workspace=sl["ws_mlp"])
+                                y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
             mq.moesq_unpermute_combine(sl["y2"], rt["slot_pos"], sl["wts"], out=sl["out"])
 
     def dominant(self, r):
@@ -174,9 +178,9 @@ class Workload:
         rt = sl["rt"]
         if self.kind == "mlp":
             mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
-                                y=sl["y2"], workspace=sl["ws_mlp"])
+                                y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
         else:
-            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
 
     def capture(self):
         torch = self.torch

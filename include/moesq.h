@@ -115,26 +115,32 @@ int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_
  *               offsets[e] <= p < offsets[e+1] (G = E, the per-expert input scale of the model
  *               card); with offsets == NULL every row uses gamma[0].
  *   q           [rows][K/2] E2M1 codes, s [rows][K/32] UE4M3 codes.
+ *   xk          optional (NULL to skip), 16-byte aligned: [rows][K] f16, the same values dequantized
+ *               (e2m1 * e4m3, exact in f16) with every 8-group of K stored in the order
+ *               (0, 2, 4, 6, 1, 3, 5, 7) -- the GEMM's operand order, read by moesq_grouped_gemm /
+ *               moesq_expert_mlp instead of decoding q and s once per weight-row block.
  * Per 32-block b of a row: amax = max |x|; code = E4M3(fp32(fp32(gamma*amax)/6)) rounded to
  * nearest even, saturating at 448; s = E4M3value/gamma; q = E2M1(x/s) (nearest, ties to the even
  * code, +0 for zero); q = 0 when s == 0. All in IEEE fp32 without fused multiply-add.
  */
 int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
                        const int32_t *gather_slot, int32_t k, int64_t rows, const float *gamma,
-                       const int32_t *offsets, int32_t E, uint8_t *q, uint8_t *s);
+                       const int32_t *offsets, int32_t E, uint8_t *q, uint8_t *s, void *xk);
 
 /*
  * Grouped sparse GEMM (paper Section 2: Y_e = X_e W_e^T in one launch for variable per-expert token
  * counts; Section 3.4: sparse operand W on the left, Y_e^T = W_e X_e^T; block scales applied in the
  * product, alpha_e = 1/(gamma_w,e * gamma_a,e) applied to the fp32 accumulator).
  *   q, s        [rows][K/2], [rows][K/32] quantized activations in expert-sorted order
+ *   xk          optional [rows][K] f16 copy from moesq_quantize_act (same rows); when given the tiled
+ *               kernel stages it straight into LDS instead of decoding q and s
  *   gamma_a     [E] activation tensor scale of each expert
  *   offsets     [E+1] from moesq_route_permute (device)
  *   y           [rows][N] fp32 or bf16 (round to nearest even). Rows >= offsets[E] are not written.
  * Requires W->kl (MOESQ_ERR_INVALID_ARG if NULL), K % 256 == 0 and N % 64 == 0
  * (MOESQ_ERR_UNSUPPORTED otherwise); E <= 4096.
  */
-int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s,
+int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s, const void *xk,
                        const float *gamma_a, const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype,
                        uint32_t flags);
 
@@ -145,16 +151,17 @@ int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, c
  *   h = SiLU(alpha*g) * (alpha*u) in fp32, SiLU(v) = v / (1 + exp(-v))
  *   requant:  h quantized like moesq_quantize_act with gamma_h[e], 32-blocks along I
  *   down:     W2 with N = H, K = I, alpha = 1/(gamma_w2,e * gamma_h,e) -> y [rows][H]
- * Workspace: moesq_workspace_bytes(MOESQ_WS_MLP, ..., rows, k=0, E, K=H, N=0, I) bytes; it holds
- *   h_q [rows][I/2] at offset 0 and h_s [rows][I/32] right after. With MOESQ_F_DUMP_GATEUP the size
- *   is moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and the fp32 gate_up outputs [rows][2I] follow
- *   h_s at the next 256-byte boundary.
+ * xk is the optional f16 copy of (q, s) from moesq_quantize_act.
+ * Workspace: moesq_workspace_bytes(MOESQ_WS_MLP, ..., rows, k=0, E, K=H, N=0, I) bytes; it holds, each
+ *   region starting on a 256-byte boundary, h_q [rows][I/2], h_s [rows][I/32] and h_k [rows][I] (the
+ *   f16 copy of the requantized h read by the down GEMM). With MOESQ_F_DUMP_GATEUP the size is
+ *   moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and the fp32 gate_up outputs [rows][2I] follow.
  * Requires H % 256 == 0, I % 256 == 0.
  */
 int moesq_expert_mlp(void *stream, const moesq_weights *W13, const moesq_weights *W2, const uint8_t *q,
-                     const uint8_t *s, const float *gamma_a, const float *gamma_h, const int32_t *offsets,
-                     int64_t rows, void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
-                     uint32_t flags);
+                     const uint8_t *s, const void *xk, const float *gamma_a, const float *gamma_h,
+                     const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype, void *workspace,
+                     size_t workspace_bytes, uint32_t flags);
 
 /*
  * Router-weighted unpermute + combine (paper Appendix D.1, token combination):
@@ -196,7 +203,8 @@ int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t row
  * weight): per expert, per 16-row block, per 256-K super-step a 1408-byte fragment; lane
  * l = 16c + r (row r of the block, K [64c, +64) of the super-step) owns bytes [16l, +16) (its
  * eight 8-groups, the two kept bytes (b0, b1) of each stored as (lo b0 | lo b1 << 4,
- * hi b0 | hi b1 << 4)), [1024 + 4l, +4) (mask bytes) and [1280 + 2l, +2) (scale codes).
+ * hi b0 | hi b1 << 4)), [1024 + 4l, +4) (per group the code i | j << 2 of its kept pairs i < j,
+ * one nibble each, groups in the order 0, 2, 4, 6, 1, 3, 5, 7) and [1280 + 2l, +2) (scale codes).
  *   kl: moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned. Requires K % 256 == 0, N % 16 == 0.
  */
 int moesq_prepack_weights(void *stream, const moesq_weights *W, uint8_t *kl, size_t kl_bytes);

@@ -55,9 +55,9 @@ def lib():
         vp, i64, i32, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         W = ctypes.POINTER(_CWeights)
         L.moesq_route_permute.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
-        L.moesq_quantize_act.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp]
-        L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, i64, vp, i32, u32]
-        L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
+        L.moesq_quantize_act.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp, vp]
+        L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, vp, i64, vp, i32, u32]
+        L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
         L.moesq_unpermute_combine.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
         L.moesq_compress_weights.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_unpack_weights.argtypes = [vp, W, vp, vp]
@@ -179,9 +179,11 @@ def moesq_route_permute(topk_ids, E, counts=None, offsets=None, sorted_slot=None
     return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos)
 
 
-def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=None, rows=None):
+def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=None, rows=None, xk=None):
     """NVFP4-quantize rows of x [T, K] (fp32/bf16). With gather_slot, permuted row p reads token
-    gather_slot[p] // k and (with offsets) uses gamma[expert of p]. Returns (q [rows,K/2], s [rows,K/32])."""
+    gather_slot[p] // k and (with offsets) uses gamma[expert of p]. Returns (q [rows,K/2], s [rows,K/32]);
+    with ``xk`` (a [rows, K] float16 tensor, or True to allocate one) also writes the GEMM's f16
+    operand copy and returns (q, s, xk)."""
     _dev(x)
     T, K = x.shape
     assert x.stride(1) == 1
@@ -190,20 +192,23 @@ def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=
     E = 0 if offsets is None else offsets.numel() - 1
     q = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
+    want_xk = xk is not None
+    if xk is True:
+        xk = torch.empty((rows, K), dtype=torch.float16, device=x.device)
     _check("moesq_quantize_act",
            lib().moesq_quantize_act(_stream(), _p(x), _dtype_code(x.dtype), T, K, x.stride(0), _p(gather_slot), k,
-                                    rows, _p(gamma), _p(offsets), E, _p(q), _p(s)))
-    return q, s
+                                    rows, _p(gamma), _p(offsets), E, _p(q), _p(s), _p(xk if want_xk else None)))
+    return (q, s, xk) if want_xk else (q, s)
 
 
-def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0):
+def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):
     rows = q.shape[0]
     if y is None:
         y = torch.empty((rows, W.N), dtype=y_dtype, device=q.device)
     c = W.cstruct()
     _check("moesq_grouped_gemm",
-           lib().moesq_grouped_gemm(_stream(), ctypes.byref(c), _p(q), _p(s), _p(gamma_a), _p(offsets), rows, _p(y),
-                                    _dtype_code(y.dtype), flags))
+           lib().moesq_grouped_gemm(_stream(), ctypes.byref(c), _p(q), _p(s), _p(xk), _p(gamma_a), _p(offsets), rows,
+                                    _p(y), _dtype_code(y.dtype), flags))
     return y
 
 
@@ -213,18 +218,20 @@ def mlp_workspace(rows, I, dump=False, device="cuda"):
 
 
 def mlp_workspace_views(ws, rows, I, dump=False):
-    """(h_q [rows, I/2], h_s [rows, I/32], gate_up fp32 [rows, 2I] or None) inside an MLP workspace."""
+    """(h_q [rows, I/2], h_s [rows, I/32], gate_up fp32 [rows, 2I] or None) inside an MLP workspace
+    (the f16 copy of h sits between h_s and the gate_up dump)."""
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     hq = ws[:rows * (I // 2)].view(rows, I // 2)
     o = a(rows * (I // 2))
     hs = ws[o:o + rows * (I // 32)].view(rows, I // 32)
     o += a(rows * (I // 32))
+    o += a(rows * I * 2)
     d = ws[o:o + rows * 2 * I * 4].view(torch.float32).view(rows, 2 * I) if dump else None
     return hq, hs, d
 
 
 def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=torch.bfloat16, workspace=None,
-                     flags=0):
+                     flags=0, xk=None):
     rows = q.shape[0]
     I = W13.N // 2
     if y is None:
@@ -233,7 +240,7 @@ def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=t
         workspace = mlp_workspace(rows, I, bool(flags & F_DUMP_GATEUP), q.device)
     a, b = W13.cstruct(), W2.cstruct()
     _check("moesq_expert_mlp",
-           lib().moesq_expert_mlp(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(gamma_a),
+           lib().moesq_expert_mlp(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(xk), _p(gamma_a),
                                   _p(gamma_h), _p(offsets), rows, _p(y), _dtype_code(y.dtype), _p(workspace),
                                   workspace.numel(), flags))
     return y, workspace

@@ -18,8 +18,10 @@ bool weights_ok(const moesq_weights* W) {
 
 constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// MLP workspace: h_q [rows][I/2], h_s [rows][I/32], h_k [rows][I] f16, then (dump) fp32 [rows][2I],
+// each region starting on a 256-byte boundary.
 size_t mlp_ws(int64_t rows, int32_t I, bool dump) {
-  size_t b = align256((size_t)rows * (I / 2)) + align256((size_t)rows * (I / 32));
+  size_t b = align256((size_t)rows * (I / 2)) + align256((size_t)rows * (I / 32)) + align256((size_t)rows * I * 2);
   if (dump) b += (size_t)rows * 2 * I * sizeof(float);
   return b;
 }
@@ -70,7 +72,7 @@ int moesq_route_permute(void* stream, const int32_t* topk_ids, int64_t T, int32_
 
 int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
                        const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
-                       int32_t E, uint8_t* q, uint8_t* s) {
+                       int32_t E, uint8_t* q, uint8_t* s, void* xk) {
   if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
   if (T < 0 || rows < 0 || K <= 0 || K % 32 != 0 || ld_x < K) return MOESQ_ERR_INVALID_ARG;
   if (!gamma) return MOESQ_ERR_INVALID_ARG;
@@ -82,18 +84,20 @@ int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, 
   }
   if (offsets && E <= 0) return MOESQ_ERR_INVALID_ARG;
   if (offsets && E > 4096) return MOESQ_ERR_UNSUPPORTED;
-  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4)) return MOESQ_ERR_UNSUPPORTED;
+  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4) || !aligned(xk, 16)) return MOESQ_ERR_UNSUPPORTED;
   return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, gather_slot, k, rows, gamma,
-                         offsets, E, q, s);
+                         offsets, E, q, s, xk);
 }
 
-static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* s, const float* gamma_a,
-                       const int32_t* offsets, int64_t rows, void* y) {
+static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,
+                       const float* gamma_a, const int32_t* offsets, int64_t rows, void* y) {
   if (!weights_ok(W) || rows < 0 || !gamma_a || !offsets) return MOESQ_ERR_INVALID_ARG;
   if (rows > 0 && (!q || !s || !y)) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 256 != 0 || W->N % 64 != 0 || W->E > kMaxExpertsGemm) return MOESQ_ERR_UNSUPPORTED;
-  if (!aligned(W->kl, 16) || !aligned(q, 16) || !aligned(s, 2) || !aligned(y, 16)) return MOESQ_ERR_UNSUPPORTED;
+  if (!aligned(W->kl, 16) || !aligned(q, 16) || !aligned(s, 2) || !aligned(y, 16) || !aligned(xk, 16))
+    return MOESQ_ERR_UNSUPPORTED;
+  if (xk && rows * W->K * 2 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
   if (rows >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: one expert's weights, and all activation rows
   if ((int64_t)W->N * W->K / 32 * 11 >= ((int64_t)1 << 31) || rows * (W->K / 2) >= ((int64_t)1 << 31))
@@ -101,14 +105,15 @@ static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* 
   return MOESQ_OK;
 }
 
-int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, const uint8_t* s, const float* gamma_a,
-                       const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype, uint32_t flags) {
+int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,
+                       const float* gamma_a, const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype,
+                       uint32_t flags) {
   if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
-  const int rc = gemm_common(W, q, s, gamma_a, offsets, rows, y);
+  const int rc = gemm_common(W, q, s, xk, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   GemmArgs a{};
   a.kl = W->kl; a.gscale = W->gscale;
-  a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
+  a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
   a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
   if (flags & MOESQ_F_FORCE_DECODE) return launch_gemm_variant((hipStream_t)stream, a, rows, 0);
   if (flags & MOESQ_F_FORCE_PREFILL) return launch_gemm_variant((hipStream_t)stream, a, rows, 1);
@@ -116,13 +121,14 @@ int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, c
 }
 
 int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights* W2, const uint8_t* q,
-                     const uint8_t* s, const float* gamma_a, const float* gamma_h, const int32_t* offsets, int64_t rows,
-                     void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes, uint32_t flags) {
+                     const uint8_t* s, const void* xk, const float* gamma_a, const float* gamma_h,
+                     const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype, void* workspace,
+                     size_t workspace_bytes, uint32_t flags) {
   if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
   if (!weights_ok(W13) || !weights_ok(W2) || !gamma_h) return MOESQ_ERR_INVALID_ARG;
   const int32_t I = W13->N / 2;
   if (W13->N % 2 != 0 || W2->K != I || W2->E != W13->E) return MOESQ_ERR_INVALID_ARG;
-  int rc = gemm_common(W13, q, s, gamma_a, offsets, rows, y);
+  int rc = gemm_common(W13, q, s, xk, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   if (I % 256 != 0 || W13->K % 256 != 0 || W2->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
   if (!aligned(W2->kl, 16)) return MOESQ_ERR_UNSUPPORTED;
@@ -132,19 +138,21 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   const size_t need = mlp_ws(rows, I, dump);
   if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MOESQ_ERR_WORKSPACE;
   if (rows == 0) return MOESQ_OK;
+  if (rows * (int64_t)I * 2 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
   uint8_t* hq = (uint8_t*)workspace;
   uint8_t* hs = hq + align256((size_t)rows * (I / 2));
-  float* dumpp = dump ? (float*)(hs + align256((size_t)rows * (I / 32))) : nullptr;
+  uint8_t* hk = hs + align256((size_t)rows * (I / 32));
+  float* dumpp = dump ? (float*)(hk + align256((size_t)rows * I * 2)) : nullptr;
   GemmArgs a{};
   a.kl = W13->kl; a.gscale = W13->gscale;
-  a.q = q; a.s = s; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
+  a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
   a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0;
-  a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.dump = dumpp;
+  a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk; a.dump = dumpp;
   rc = launch_gemm_variant((hipStream_t)stream, a, rows, 1);
   if (rc != MOESQ_OK) return rc;
   GemmArgs b{};
   b.kl = W2->kl; b.gscale = W2->gscale;
-  b.q = hq; b.s = hs; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
+  b.q = hq; b.s = hs; b.xk = hk; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
   b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16;
   return launch_gemm_variant((hipStream_t)stream, b, rows, 1);
 }

@@ -94,6 +94,14 @@ MOESQ_DEV void quant8_block4(const float v[8], float gamma, uint32_t& codes, uin
 MOESQ_DEV uint32_t f16x2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 MOESQ_DEV f16x2 bits_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 
+// Two UE4M3 codes in the low 16 bits of w -> (v0, v0) and (v1, v1) as f16x2 (exact: the gfx950
+// FP8 convert with unit scale, on the bytes duplicated by a perm).
+MOESQ_DEV void e4m3_pair_f16x2(uint32_t w, f16x2& s0, f16x2& s1) {
+  const uint32_t d = __builtin_amdgcn_perm(0u, w, 0x01010000u);  // bytes (b0, b0, b1, b1)
+  s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false);
+  s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
+}
+
 // Dense activation 8-group (codes word c: element i in nibble i) -> 4 f16x2 in de-interleaved
 // order (a0,a2), (a4,a6), (a1,a3), (a5,a7), scaled by sc.
 MOESQ_DEV u32x4 decode_x_group(uint32_t c, f16x2 sc) {
@@ -109,25 +117,23 @@ MOESQ_DEV u32x4 decode_x_group(uint32_t c, f16x2 sc) {
   return o;
 }
 
-// Index nibble of a pair-bitmask nibble (exactly two bits i < j set): i | j << 2. Both 4-groups of
-// the de-interleaved 8-group use it.
+// Sparse-index code of a pair-bitmask nibble (exactly two bits i < j set): i | j << 2. Both
+// 4-groups of the de-interleaved 8-group use it.
 MOESQ_DEV uint32_t pair_index_code(uint32_t nib) {
   const uint32_t i = (uint32_t)__builtin_ctz(nib | 16u);
   const uint32_t j = (uint32_t)(31 - __builtin_clz(nib | 1u));
   return (i & 3u) | ((j & 3u) << 2);
 }
 
-// 16-bit sparse index operand for two consecutive 8-groups whose mask nibbles are in byte mb.
-MOESQ_DEV uint32_t pair_index_word(uint32_t mb) {
-  const uint32_t a = pair_index_code(mb & 15u), b = pair_index_code(mb >> 4);
-  return a | (a << 4) | (b << 8) | (b << 12);
-}
-
-// f16x2 (v, v) of a UE4M3 code (exact in f16: 2^-9 .. 448).
-MOESQ_DEV uint32_t e4m3_f16x2_bits(uint32_t c) {
-  const _Float16 h = (_Float16)e4m3_value(c);
-  const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, h);
-  return b | (b << 16);
+// Sparse index operands of one lane for a 256-K super-step. The kernel layout stores the index
+// codes of the lane's eight 8-groups g = 2s + h (step s, half h) as nibbles in the order
+// (g0, g2, g4, g6, g1, g3, g5, g7). Returns i02 = index words of steps 0 (low 16 bits) and 2
+// (high), i13 = steps 1 and 3; each 16-bit word is c(s,0)*0x11 | c(s,1)*0x11 << 8.
+MOESQ_DEV void sparse_index_words(uint32_t m, uint32_t& i02, uint32_t& i13) {
+  const uint32_t e = (m & 0x0F0F0F0Fu) * 17u;          // bytes c(0,0) c(2,0) c(0,1) c(2,1), duplicated
+  const uint32_t o = ((m >> 4) & 0x0F0F0F0Fu) * 17u;   // bytes c(1,0) c(3,0) c(1,1) c(3,1)
+  i02 = __builtin_amdgcn_perm(0u, e, 0x03010200u);
+  i13 = __builtin_amdgcn_perm(0u, o, 0x03010200u);
 }
 
 // Round an fp32 to bf16 bits, nearest even (finite inputs).

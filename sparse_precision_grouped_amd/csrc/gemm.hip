@@ -7,10 +7,11 @@
 // MI355X design:
 //  - The paired-4:8 weights feed v_smfmac_f32_16x16x64_f16 (2:4 structured-sparse MFMA) after an
 //    even/odd de-interleave of every 8-group, which turns each of the six paired patterns into a
-//    valid 2:4 pattern; the pair mask becomes the sparse index operand (an LDS table, mask byte ->
-//    16-bit index word). E2M1 codes are expanded with the gfx950 FP4->f16 convert and multiplied
-//    by the UE4M3 block scale in f16: e2m1 * e4m3 has at most 6 significant bits, so every operand
-//    is exact and the only rounding is the fp32 accumulation.
+//    valid 2:4 pattern; the pair mask becomes the sparse index operand (two steps' 16-bit index
+//    words per VGPR, picked by the instruction's abid field). E2M1 codes are expanded with the
+//    gfx950 FP4->f16 convert and multiplied by the UE4M3 block scale (FP8->f16 convert) in f16:
+//    e2m1 * e4m3 has at most 6 significant bits, so every operand is exact and the only rounding
+//    is the fp32 accumulation. No lookup tables: all decoding is VALU work in registers.
 //  - Weights are read from the kernel layout built at load time (prepack_kernel): per 16 rows x
 //    256 K fragment, lane (row r, chunk c) finds its 16 packed bytes, 4 mask bytes and 2 scale
 //    bytes at fixed offsets, so a wave reads 1408 contiguous bytes per fragment with three buffer
@@ -31,19 +32,6 @@
 #include <stdlib.h>
 
 namespace moesq {
-
-// LDS tables: mask byte (two pair nibbles) -> 16-bit sparse index word; UE4M3 code -> f16x2 (v, v).
-struct DecodeTables {
-  uint16_t idx[256];
-  uint32_t scl[256];
-};
-
-MOESQ_DEV void init_tables(DecodeTables& t) {
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    t.idx[i] = (uint16_t)pair_index_word((uint32_t)i);
-    t.scl[i] = e4m3_f16x2_bits((uint32_t)i);
-  }
-}
 
 MOESQ_DEV f16x16 concat_x(u32x4 lo, u32x4 hi) {
   typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
@@ -93,19 +81,40 @@ MOESQ_DEV void load_w(WStage<MF>& st, rsrc_t rw, const uint32_t (&soff)[MF], int
   }
 }
 
+// Per-fragment metadata of one super-step: sparse index words (steps 0/2 and 1/3) and the block
+// scales of steps 0-1 and 2-3 as f16x2 pairs.
+struct WMeta {
+  uint32_t i02, i13;
+  f16x2 s01, s23;
+};
+
+template <int MF>
+MOESQ_DEV WMeta w_meta(const WStage<MF>& w, int f) {
+  WMeta m;
+  sparse_index_words(w.mk[f], m.i02, m.i13);
+  e4m3_pair_f16x2(w.sw[f], m.s01, m.s23);
+  return m;
+}
+
 // A operand of step s (0..3) for m-fragment f: the kernel layout's nibble order makes each FP4
 // convert produce one de-interleaved operand register directly.
 template <int MF>
-MOESQ_DEV f16x8 w_frag(const WStage<MF>& w, int f, int s, const DecodeTables& tab, int& idx) {
-  const f16x2 sc = bits_f16x2(tab.scl[(w.sw[f] >> (8 * (s >> 1))) & 0xFFu]);
+MOESQ_DEV f16x8 w_frag(const WStage<MF>& w, const WMeta& m, int f, int s) {
+  const f16x2 sc = s < 2 ? m.s01 : m.s23;
   const uint32_t wd = s == 0 ? w.pk[f].x : s == 1 ? w.pk[f].y : s == 2 ? w.pk[f].z : w.pk[f].w;
-  idx = tab.idx[(w.mk[f] >> (8 * s)) & 0xFFu];
   u32x4 o;
   o.x = f16x2_bits(MOESQ_CVT_FP4(wd, 0) * sc);
   o.y = f16x2_bits(MOESQ_CVT_FP4(wd, 1) * sc);
   o.z = f16x2_bits(MOESQ_CVT_FP4(wd, 2) * sc);
   o.w = f16x2_bits(MOESQ_CVT_FP4(wd, 3) * sc);
   return __builtin_bit_cast(f16x8, o);
+}
+
+// One sparse MFMA of step S (a compile-time constant): the index word's half is chosen by
+// abid = S / 2.
+template <int S>
+MOESQ_DEV f32x4 smfmac_step(f16x8 A, f16x16 B, f32x4 C, const WMeta& m) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(A, B, C, (int)((S & 1) ? m.i13 : m.i02), 0, S >> 1);
 }
 
 // Activation operand of one lane for one super-step (decode kernel): for each of the 4 K-steps two
@@ -125,20 +134,27 @@ MOESQ_DEV void load_x(XStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t v
   st.bs1 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss + 4u), 0, 0);
 }
 
+template <int S, int MF>
+MOESQ_DEV void x_step(f32x4 (&acc)[MF], const WStage<MF>& w, const WMeta (&m)[MF], const XStage& x, f16x2 a01,
+                      f16x2 a23, f16x2 b01, f16x2 b23) {
+  const f16x16 B = concat_x(decode_x_group(x.bc[2 * S], S < 2 ? a01 : a23),
+                            decode_x_group(x.bc[2 * S + 1], S < 2 ? b01 : b23));
+#pragma unroll
+  for (int f = 0; f < MF; f++) acc[f] = smfmac_step<S>(w_frag(w, m[f], f, S), B, acc[f], m[f]);
+}
+
 template <int MF>
-MOESQ_DEV void mma_superstep_x(f32x4 (&acc)[MF], const WStage<MF>& w, const XStage& x, const DecodeTables& tab) {
+MOESQ_DEV void mma_superstep_x(f32x4 (&acc)[MF], const WStage<MF>& w, const XStage& x) {
+  WMeta m[MF];
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    const f16x2 sb1 = bits_f16x2(tab.scl[(x.bs0 >> (8 * (s >> 1))) & 0xFFu]);
-    const f16x2 sb2 = bits_f16x2(tab.scl[(x.bs1 >> (8 * (s >> 1))) & 0xFFu]);
-    const f16x16 B = concat_x(decode_x_group(x.bc[2 * s], sb1), decode_x_group(x.bc[2 * s + 1], sb2));
-#pragma unroll
-    for (int f = 0; f < MF; f++) {
-      int idx;
-      const f16x8 A = w_frag(w, f, s, tab, idx);
-      acc[f] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A, B, acc[f], idx, 0, 0);
-    }
-  }
+  for (int f = 0; f < MF; f++) m[f] = w_meta(w, f);
+  f16x2 a01, a23, b01, b23;
+  e4m3_pair_f16x2(x.bs0, a01, a23);
+  e4m3_pair_f16x2(x.bs1, b01, b23);
+  x_step<0>(acc, w, m, x, a01, a23, b01, b23);
+  x_step<1>(acc, w, m, x, a01, a23, b01, b23);
+  x_step<2>(acc, w, m, x, a01, a23, b01, b23);
+  x_step<3>(acc, w, m, x, a01, a23, b01, b23);
 }
 
 MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
@@ -152,14 +168,11 @@ MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (
 // grid (N / (16*MF*(4/KSPLIT)), E).
 template <int MF, int KSPLIT>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
-  __shared__ DecodeTables tab;
   __shared__ f32x4 red[KSPLIT][MF][64];
   const int e = blockIdx.y;
   const int off = a.offsets[e];
   const int ne = a.offsets[e + 1] - off;
   if (ne <= 0) return;
-  init_tables(tab);
-  __syncthreads();
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.K, N = a.N, nss = K / 256;
@@ -196,12 +209,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
         load_w(w1, rw, soff, lane, s1);
         load_x(x1, rq, rs, voq, vos, s1);
       }
-      mma_superstep_x(acc, w0, x0, tab);
+      mma_superstep_x(acc, w0, x0);
       if (s2 < nss) {
         load_w(w0, rw, soff, lane, s2);
         load_x(x0, rq, rs, voq, vos, s2);
       }
-      if (s1 < nss) mma_superstep_x(acc, w1, x1, tab);
+      if (s1 < nss) mma_superstep_x(acc, w1, x1);
       ss = s2;
     }
     if (KSPLIT == 1) {
@@ -225,17 +238,85 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
 }
 
 // =========================================================================== prefill kernel =====
-constexpr int kPfTokens = 64;                 // T_N
-constexpr int kPfGroups = 32;                 // 8-element groups per 256-K super-step
-constexpr int kPfRowBytes = kPfGroups * 16 + 16;  // decoded f16 groups of one token (+ pad)
+constexpr int kPfTokens = 64;                     // T_N
+constexpr int kPfGroups = 32;                     // 8-element groups per 256-K super-step
+constexpr int kPfRowBytes = kPfGroups * 16 + 16;  // FP4-staging path: decoded groups of one token (+ pad)
+constexpr int kPfTileBytes = kPfTokens * kPfRowBytes;
 
-// Tile table: tile_pre[e] = sum over e' < e of ceil(n_e' / 64), built in LDS by every workgroup.
-MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int32_t* tile_pre, int32_t* part) {
+// Activation tile (B) in LDS. FP4-staging path: token row r, group g at r * kPfRowBytes + 16 g.
+// f16 path (direct-to-LDS loads): chunk (r, g) at 16 * (32 r + (g ^ (r & 31))), an XOR swizzle that
+// keeps the 16 rows read by one B fragment on distinct banks.
+template <bool XK>
+MOESQ_DEV const uint8_t* b_chunk(const uint8_t* Bs, int r, int g) {
+  if (XK) return Bs + 16 * (32 * r + (g ^ (r & 31)));
+  return Bs + r * kPfRowBytes + 16 * g;
+}
+
+// Activation staging of one super-step from NVFP4 codes: thread (lane = token, wave = quarter of the
+// super-step) reads 32 code bytes (8 groups = 64 K) and their two block scales and decodes them to
+// f16 (de-interleaved) into LDS.
+struct PStage {
+  u32x4 cw0, cw1;
+  uint32_t sc2;
+};
+
+MOESQ_DEV void load_p(PStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, int ss) {
+  st.cw0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss), 0, 0));
+  st.cw1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss + 16u), 0, 0));
+  st.sc2 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
+}
+
+MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bw) {
+  f16x2 s0, s1;
+  e4m3_pair_f16x2(st.sc2, s0, s1);
+  *(u32x4*)(Bw + 0) = decode_x_group(st.cw0.x, s0);
+  *(u32x4*)(Bw + 16) = decode_x_group(st.cw0.y, s0);
+  *(u32x4*)(Bw + 32) = decode_x_group(st.cw0.z, s0);
+  *(u32x4*)(Bw + 48) = decode_x_group(st.cw0.w, s0);
+  *(u32x4*)(Bw + 64) = decode_x_group(st.cw1.x, s1);
+  *(u32x4*)(Bw + 80) = decode_x_group(st.cw1.y, s1);
+  *(u32x4*)(Bw + 96) = decode_x_group(st.cw1.z, s1);
+  *(u32x4*)(Bw + 112) = decode_x_group(st.cw1.w, s1);
+}
+
+template <int S, int MF, int NF, bool XK>
+MOESQ_DEV void lds_step(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const WMeta (&m)[MF], const uint8_t* Bs, int r16,
+                        int c) {
+  f16x8 A[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) A[f] = w_frag(w, m[f], f, S);
+  const int g1 = 8 * (c >> 1) + 2 * S + (c & 1);
+#pragma unroll
+  for (int n = 0; n < NF; n++) {
+    const int r = n * 16 + r16;
+    const f16x16 B = concat_x(*(const u32x4*)b_chunk<XK>(Bs, r, g1), *(const u32x4*)b_chunk<XK>(Bs, r, g1 + 16));
+#pragma unroll
+    for (int f = 0; f < MF; f++) acc[f][n] = smfmac_step<S>(A[f], B, acc[f][n], m[f]);
+  }
+}
+
+template <int MF, int NF, bool XK>
+MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const uint8_t* Bs, int r16, int c) {
+  WMeta m[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) m[f] = w_meta(w, f);
+  lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c);
+  lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c);
+  lds_step<2, MF, NF, XK>(acc, w, m, Bs, r16, c);
+  lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c);
+}
+
+// Per-expert tile counts ceil(n_e / 64) -> exclusive prefix tile_pre[0..E] in LDS (E+1 entries),
+// and the expert offsets copied to off_l[0..E].
+MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int32_t* tile_pre, int32_t* off_l,
+                                 int32_t* part) {
   const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += 256) off_l[i] = offsets[i];
+  __syncthreads();
   const int per = (E + 255) / 256;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; e++) sum += (offsets[e + 1] - offsets[e] + kPfTokens - 1) / kPfTokens;
+  for (int e = lo; e < hi; e++) sum += (off_l[e + 1] - off_l[e] + kPfTokens - 1) / kPfTokens;
   part[tid] = sum;
   __syncthreads();
   if (tid < 64) {  // wave 0 scans the 256 partial sums (4 per lane)
@@ -256,120 +337,191 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
   int run = part[tid];
   for (int e = lo; e < hi; e++) {
     tile_pre[e] = run;
-    run += (offsets[e + 1] - offsets[e] + kPfTokens - 1) / kPfTokens;
+    run += (off_l[e + 1] - off_l[e] + kPfTokens - 1) / kPfTokens;
   }
   if (hi == E && lo < hi) tile_pre[E] = run;
   __syncthreads();
 }
 
-// Activation staging of one super-step (prefill): thread (token tt, part) reads 32 code bytes
-// (8 groups = 64 K) and their two block scales, decodes them to f16 (de-interleaved) into LDS.
-struct PStage {
-  u32x4 cw0, cw1;
-  uint32_t sc2;
+// One output tile of the persistent schedule and the per-tile operand addressing.
+template <int MF>
+struct TileCtx {
+  int e, off, ne, tb, rb;
+  float alpha;
+  rsrc_t rw;          // expert's weights (kernel layout)
+  uint32_t soff[MF];  // fragment offsets of the wave's m-fragments (super-step 0)
+  rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
 };
 
-MOESQ_DEV void load_p(PStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, int ss) {
-  st.cw0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss), 0, 0));
-  st.cw1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(voq + 128u * ss + 16u), 0, 0));
-  st.sc2 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
+// Tile t of the list ordered expert -> token tile -> row block (row block fastest): the 4-wave
+// workgroups of one XCD that run neighbouring tiles share the activation tile in L2.
+template <int MF, bool MLP, bool XK>
+MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, int RB, int t,
+                                int w, int r16) {
+  TileCtx<MF> c;
+  int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] * RB <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_pre[mid] * RB <= t) lo = mid; else hi = mid - 1;
+  }
+  c.e = __builtin_amdgcn_readfirstlane(lo);
+  const int local = t - __builtin_amdgcn_readfirstlane(tile_pre[c.e]) * RB;
+  c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kPfTokens);
+  c.rb = __builtin_amdgcn_readfirstlane(local % RB);
+  c.off = __builtin_amdgcn_readfirstlane(off_l[c.e]);
+  c.ne = __builtin_amdgcn_readfirstlane(off_l[c.e + 1]) - c.off;
+  const int K = a.K, N = a.N, nss = K / 256;
+  const uint32_t ekl = expert_kl_bytes(N, K);
+  c.rw = make_rsrc(a.kl + (size_t)c.e * ekl, ekl);
+#pragma unroll
+  for (int f = 0; f < MF; f++) {
+    int rbf;
+    if (MLP) rbf = ((f < 2 ? 0 : N / 2) + c.rb * 128 + 32 * w + 16 * (f & 1)) / 16;
+    else rbf = min(c.rb * 256 + 64 * w, N - 64) / 16 + f;
+    c.soff[f] = __builtin_amdgcn_readfirstlane((uint32_t)rbf * (uint32_t)nss * kFragBytes);
+  }
+  c.alpha = 1.0f / (a.gscale[c.e] * a.gamma_a[c.e]);
+  if (XK) {
+    c.rq = make_rsrc((const uint8_t*)a.xk + (size_t)c.off * K * 2, (uint32_t)c.ne * K * 2);
+    c.rs = c.rq;
+  } else {
+    c.rq = make_rsrc(a.q + (size_t)c.off * (K / 2), (uint32_t)c.ne * (K / 2));
+    c.rs = make_rsrc(a.s + (size_t)c.off * (K / 32), (uint32_t)c.ne * (K / 32));
+  }
+  (void)r16;
+  return c;
 }
 
-MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bw, const DecodeTables& tab) {
-  const f16x2 s0 = bits_f16x2(tab.scl[st.sc2 & 0xFFu]);
-  const f16x2 s1 = bits_f16x2(tab.scl[(st.sc2 >> 8) & 0xFFu]);
-  *(u32x4*)(Bw + 0) = decode_x_group(st.cw0.x, s0);
-  *(u32x4*)(Bw + 16) = decode_x_group(st.cw0.y, s0);
-  *(u32x4*)(Bw + 32) = decode_x_group(st.cw0.z, s0);
-  *(u32x4*)(Bw + 48) = decode_x_group(st.cw0.w, s0);
-  *(u32x4*)(Bw + 64) = decode_x_group(st.cw1.x, s1);
-  *(u32x4*)(Bw + 80) = decode_x_group(st.cw1.y, s1);
-  *(u32x4*)(Bw + 96) = decode_x_group(st.cw1.z, s1);
-  *(u32x4*)(Bw + 112) = decode_x_group(st.cw1.w, s1);
+// Issue the activation operand of super-step ss of tile c: f16 path = 8 direct-to-LDS loads per wave
+// (wave w fills chunks [512 w, 512 w + 512) of the swizzled tile); FP4 path = register loads.
+template <int MF, bool XK>
+MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int w, int lane, int K) {
+  if (XK) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int q = (8 * w + j) * 64 + lane;
+      const int r = q >> 5, g = (q & 31) ^ (r & 31);
+      const uint32_t vo = (uint32_t)(c.tb + r) * (uint32_t)(2 * K) + 16u * g + 512u * ss;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (__attribute__((address_space(3))) void*)(Bs + (8 * w + j) * 1024),
+                                               16, (int)vo, 0, 0, 0);
+#else
+      (void)vo;
+#endif
+    }
+  } else {
+    const uint32_t voq = (uint32_t)(c.tb + lane) * (K / 2) + 32u * w;
+    const uint32_t vos = (uint32_t)(c.tb + lane) * (K / 32) + 2u * w;
+    load_p(p, c.rq, c.rs, voq, vos, ss);
+  }
 }
 
-// All MFMAs of one super-step for a wave: A from registers, B from the LDS tile.
-template <int MF, int NF>
-MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const uint8_t* Bs, int r16, int c,
-                                 const DecodeTables& tab) {
-#pragma unroll
-  for (int s = 0; s < 4; s++) {
-    f16x8 A[MF];
-    int idx[MF];
-#pragma unroll
-    for (int f = 0; f < MF; f++) A[f] = w_frag(w, f, s, tab, idx[f]);
-    const int g1 = 8 * (c >> 1) + 2 * s + (c & 1);
+// Epilogue of a finished tile.
+template <int MF, int NF, bool MLP>
+MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc) {
+  const int N = a.N;
+  const float alpha = c.alpha;
+  if (!MLP) {
+    const int n0 = c.rb * 256 + 64 * w;
+    if (n0 >= N) return;
 #pragma unroll
     for (int n = 0; n < NF; n++) {
-      const uint8_t* br = Bs + (n * 16 + r16) * kPfRowBytes;
-      const f16x16 B = concat_x(*(const u32x4*)(br + 16 * g1), *(const u32x4*)(br + 16 * (g1 + 16)));
+      const int tok = c.tb + n * 16 + r16;
+      if (tok >= c.ne) continue;
 #pragma unroll
-      for (int f = 0; f < MF; f++)
-        acc[f][n] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[f], B, acc[f][n], idx[f], 0, 0);
+      for (int f = 0; f < MF; f++) store4(a.y, (int64_t)(c.off + tok) * N + n0 + 16 * f + 4 * cc, acc[f][n], alpha, a.y_bf16);
+    }
+    return;
+  }
+  const int I = N / 2;
+  const int ib = c.rb * 128 + 32 * w;  // first intermediate column of this wave (one 32-block)
+  const float gh = a.gamma_h[c.e];
+#pragma unroll
+  for (int n = 0; n < NF; n++) {
+    const int tok = c.tb + n * 16 + r16;
+    const bool tv = tok < c.ne;
+    float h[8];
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const float g = acc[f][n][r] * alpha;
+        const float u = acc[f + 2][n][r] * alpha;
+        h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
+      }
+      if (tv && a.dump) {
+        const int64_t rowo = (int64_t)(c.off + tok) * N;
+        float4 gv, uv;
+        gv.x = acc[f][n][0] * alpha; gv.y = acc[f][n][1] * alpha; gv.z = acc[f][n][2] * alpha; gv.w = acc[f][n][3] * alpha;
+        uv.x = acc[f + 2][n][0] * alpha; uv.y = acc[f + 2][n][1] * alpha; uv.z = acc[f + 2][n][2] * alpha;
+        uv.w = acc[f + 2][n][3] * alpha;
+        *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
+        *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
+      }
+    }
+    // requantize: the 32-block of this token is spread over the 4 lanes cc = 0..3 (xor 16, 32)
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
+    am = __builtin_fmaxf(am, __shfl_xor(am, 16));
+    am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+    const float t = gh * am;
+    const float uq = t / 6.0f;
+    const uint32_t sc = e4m3_encode(uq);
+    const float sv = e4m3_value(sc) / gh;
+    if (tv) {
+      const int64_t p = c.off + tok;
+      f16x2 s01, s01b;
+      e4m3_pair_f16x2(sc, s01, s01b);
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        uint32_t codes = 0u;
+        if (sv != 0.0f) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) codes |= e2m1_encode(h[4 * f + r] / sv) << (4 * r);
+        }
+        const int i0 = ib + 16 * f + 4 * cc;  // 4 consecutive intermediate columns: half (cc & 1) of an 8-group
+        *(uint16_t*)(a.h_q + p * (I / 2) + i0 / 2) = (uint16_t)codes;
+        if (a.h_k) {
+          // f16 copy in the de-interleaved group order (a0,a2,a4,a6,a1,a3,a5,a7): this lane holds
+          // a[4h..4h+3] (h = cc & 1) and writes words h ((a4h, a4h+2)) and 2 + h ((a4h+1, a4h+3)).
+          const uint32_t v01 = f16x2_bits(MOESQ_CVT_FP4(codes, 0) * s01);  // (v0, v1)
+          const uint32_t v23 = f16x2_bits(MOESQ_CVT_FP4(codes, 1) * s01);  // (v2, v3)
+          uint8_t* grp = (uint8_t*)a.h_k + (p * I + (i0 & ~7)) * 2;
+          *(uint32_t*)(grp + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x05040100u);
+          *(uint32_t*)(grp + 8 + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x07060302u);
+        }
+      }
+      if (cc == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
     }
   }
 }
 
-// Tiled kernel: 256 weight rows (4 waves x 4 m-fragments) x 64 tokens of one expert per workgroup;
-// tile y of the grid maps to (expert, token block) through the per-expert tile prefix. The
-// activation tile is decoded into a double-buffered LDS tile while the previous super-step
-// computes; weights and activation codes of the next super-step are in flight meanwhile.
-template <bool MLP>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
+// Persistent tiled kernel: 256 weight rows (4 waves x 4 m-fragments) x 64 tokens per tile. The grid
+// holds 8*J workgroups; the workgroups of XCD x (blockIdx % 8 == x) take the x-th contiguous eighth
+// of the tile list, slot j handling tiles start + j, + J, ... The super-steps of all the workgroup's
+// tiles form one pipeline: while step i computes, the weights (registers) and activations (LDS) of
+// step i+1 -- possibly the first step of the next tile -- are in flight; one barrier per step.
+template <bool MLP, bool XK>
+__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = 4;
   extern __shared__ __align__(16) uint8_t dyn[];
-  __shared__ DecodeTables tab;
   __shared__ int32_t part[256];
-  __shared__ int32_t tinfo[2];
-  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, cc = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int32_t* tile_pre = (int32_t*)dyn;                               // [E+1]
-  uint8_t* Bs0 = dyn + (((a.E + 1) * 4 + 15) / 16) * 16;          // [64][kPfRowBytes]
-  uint8_t* Bs1 = Bs0 + kPfTokens * kPfRowBytes;
-  init_tables(tab);
-  build_tile_prefix(a.offsets, a.E, tile_pre, part);
-  const int ty = blockIdx.y;
-  if (tid == 0) {
-    int e = -1;
-    if (ty < tile_pre[a.E]) {
-      int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] <= ty
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_pre[mid] <= ty) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
-    }
-    tinfo[0] = e;
-    tinfo[1] = e >= 0 ? ty - tile_pre[e] : 0;
-  }
-  __syncthreads();
-  const int e = tinfo[0];
-  if (e < 0) return;
-  const int tb = tinfo[1] * kPfTokens;
-  const int off = a.offsets[e];
-  const int ne = a.offsets[e + 1] - off;
-  const int K = a.K, N = a.N, nss = K / 256;
-
-  // 16-row blocks of this wave's m-fragments: consecutive (plain) or gate / up halves (MLP)
-  bool wave_on = true;
-  int rbf[MF];
-  if (MLP) {
-    const int I = N / 2;
-    const int i0 = blockIdx.x * 128 + 32 * w;
-#pragma unroll
-    for (int f = 0; f < MF; f++) rbf[f] = ((f < 2 ? 0 : I) + i0 + 16 * (f & 1)) / 16;
-  } else {
-    const int n0 = blockIdx.x * 256 + 64 * w;
-    wave_on = n0 < N;
-#pragma unroll
-    for (int f = 0; f < MF; f++) rbf[f] = (wave_on ? n0 : 0) / 16 + f;
-  }
-  const uint32_t ekl = expert_kl_bytes(N, K);
-  const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
-  uint32_t soff[MF];
-#pragma unroll
-  for (int f = 0; f < MF; f++) soff[f] = (uint32_t)rbf[f] * (uint32_t)nss * kFragBytes;
-  const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
+  uint8_t* Bs0 = dyn;                                    // two activation tiles
+  uint8_t* Bs1 = dyn + kPfTileBytes;
+  int32_t* tile_pre = (int32_t*)(dyn + 2 * kPfTileBytes);  // [E+1]
+  int32_t* off_l = tile_pre + a.E + 1;                   // [E+1]
+  build_tile_prefix(a.offsets, a.E, tile_pre, off_l, part);
+  const int K = a.K, nss = K / 256;
+  const int RB = MLP ? a.N / 256 : (a.N + 255) / 256;   // MLP: 128 gate + 128 up rows per tile
+  const int T = tile_pre[a.E] * RB;
+  const int J = gridDim.x >> 3, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int chunk = (T + 7) / 8;
+  const int tend = min(T, (x + 1) * chunk);
+  int t = x * chunk + j;
+  if (t >= tend) return;
 
   f32x4 acc[MF][NF];
 #pragma unroll
@@ -377,106 +529,68 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // staging role: token tt of the tile, groups 8*part4 .. +8 of each super-step
-  const int tt = tid >> 2, part4 = tid & 3;
-  const rsrc_t rq = make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
-  const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
-  const uint32_t voq = (uint32_t)(tb + tt) * (K / 2) + 32u * part4;
-  const uint32_t vos = (uint32_t)(tb + tt) * (K / 32) + 2u * part4;
-  const int bw_off = tt * kPfRowBytes + part4 * 8 * 16;
-
+  TileCtx<MF> cur = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t, w, r16);
   WStage<MF> wa0, wa1;
   PStage p0, p1;
-  if (wave_on) load_w(wa0, rw, soff, lane, 0);
-  load_p(p0, rq, rs, voq, vos, 0);
-  stage_p(p0, Bs0 + bw_off, tab);
+  load_w(wa0, cur.rw, cur.soff, lane, 0);
+  issue_b<MF, XK>(cur, 0, Bs0, p0, w, lane, K);
+  if (!XK) stage_p(p0, Bs0 + lane * kPfRowBytes + w * 128);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int ss = 0; ss < nss; ss += 2) {
-    const bool has1 = ss + 1 < nss, has2 = ss + 2 < nss;
-    if (has1) {
-      if (wave_on) load_w(wa1, rw, soff, lane, ss + 1);
-      load_p(p1, rq, rs, voq, vos, ss + 1);
-    }
-    if (wave_on) mma_superstep_lds<MF, NF>(acc, wa0, Bs0, r16, c, tab);
-    if (has1) stage_p(p1, Bs1 + bw_off, tab);
-    __syncthreads();
-    if (has1) {
-      if (has2) {
-        if (wave_on) load_w(wa0, rw, soff, lane, ss + 2);
-        load_p(p0, rq, rs, voq, vos, ss + 2);
+  int ss = 0;
+  bool more = true;
+  while (more) {
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      // coordinates of the next step
+      int ss_n = ss + 1, t_n = t;
+      if (ss_n == nss) {
+        ss_n = 0;
+        t_n = t + J;
       }
-      if (wave_on) mma_superstep_lds<MF, NF>(acc, wa1, Bs1, r16, c, tab);
-      if (has2) stage_p(p0, Bs0 + bw_off, tab);
+      const bool has_n = t_n < tend;
+      TileCtx<MF> nxt = cur;
+      if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t_n, w, r16);
+      uint8_t* Bc = half == 0 ? Bs0 : Bs1;
+      uint8_t* Bn = half == 0 ? Bs1 : Bs0;
+      if (has_n) {
+        load_w(half == 0 ? wa1 : wa0, nxt.rw, nxt.soff, lane, ss_n);
+        issue_b<MF, XK>(nxt, ss_n, Bn, half == 0 ? p1 : p0, w, lane, K);
+      }
+      mma_superstep_lds<MF, NF, XK>(acc, half == 0 ? wa0 : wa1, Bc, r16, cc);
+      if (ss == nss - 1) {
+        tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
+#pragma unroll
+        for (int f = 0; f < MF; f++)
+#pragma unroll
+          for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+      if (has_n && !XK) stage_p(half == 0 ? p1 : p0, Bn + lane * kPfRowBytes + w * 128);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-    }
-  }
-
-  if (!wave_on) return;
-  if (!MLP) {
-    const int n0 = blockIdx.x * 256 + 64 * w;
-#pragma unroll
-    for (int n = 0; n < NF; n++) {
-      const int tok = tb + n * 16 + r16;
-      if (tok >= ne) continue;
-#pragma unroll
-      for (int f = 0; f < MF; f++) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, acc[f][n], alpha, a.y_bf16);
-    }
-  } else {
-    const int I = N / 2;
-    const int ib = blockIdx.x * 128 + 32 * w;  // first intermediate column of this wave (32-block)
-    const float gh = a.gamma_h[e];
-#pragma unroll
-    for (int n = 0; n < NF; n++) {
-      const int tok = tb + n * 16 + r16;
-      const bool tv = tok < ne;
-      float h[8];
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const float g = acc[f][n][r] * alpha;
-          const float u = acc[f + 2][n][r] * alpha;
-          h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
-        }
-        if (tv && a.dump) {
-          const int64_t rowo = (int64_t)(off + tok) * N;
-          float4 gv, uv;
-          gv.x = acc[f][n][0] * alpha; gv.y = acc[f][n][1] * alpha; gv.z = acc[f][n][2] * alpha; gv.w = acc[f][n][3] * alpha;
-          uv.x = acc[f + 2][n][0] * alpha; uv.y = acc[f + 2][n][1] * alpha; uv.z = acc[f + 2][n][2] * alpha;
-          uv.w = acc[f + 2][n][3] * alpha;
-          *(float4*)(a.dump + rowo + ib + 16 * f + 4 * c) = gv;
-          *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * c) = uv;
-        }
+      if (!has_n) {
+        more = false;
+        break;
       }
-      // requantize: the 32-block of this token is spread over the 4 lanes c = 0..3 (xor 16, 32)
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 16));
-      am = __builtin_fmaxf(am, __shfl_xor(am, 32));
-      const float t = gh * am;
-      const float uq = t / 6.0f;
-      const uint32_t sc = e4m3_encode(uq);
-      const float sv = e4m3_value(sc) / gh;
-      if (tv) {
-        const int64_t p = off + tok;
-#pragma unroll
-        for (int f = 0; f < 2; f++) {
-          uint32_t codes = 0u;
-          if (sv != 0.0f) {
-#pragma unroll
-            for (int r = 0; r < 4; r++) codes |= e2m1_encode(h[4 * f + r] / sv) << (4 * r);
-          }
-          *(uint16_t*)(a.h_q + p * (I / 2) + (ib + 16 * f + 4 * c) / 2) = (uint16_t)codes;
-        }
-        if (c == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
-      }
+      cur = nxt;
+      t = t_n;
+      ss = ss_n;
     }
   }
 }
 
-static size_t prefill_lds_bytes(int E) {
-  return (size_t)(((E + 1) * 4 + 15) / 16) * 16 + 2 * (size_t)kPfTokens * kPfRowBytes;
+static size_t prefill_lds_bytes(int E) { return 2 * (size_t)kPfTileBytes + 2 * (size_t)(E + 1) * 4; }
+
+static int device_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
 }
 
 // Decode variants: MF (rows per wave / 16) and KSPLIT. The default is picked by measurement; the
@@ -505,13 +619,16 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
       default: hipLaunchKernelGGL((gemm_decode_kernel<8, 1>), dim3(a.N / 512, a.E), dim3(256), 0, st, a); break;
     }
   } else {
-    const int64_t tiles = (rows + kPfTokens - 1) / kPfTokens + a.E;
+    // persistent grid: two 4-wave workgroups per CU, a multiple of the 8 XCDs
+    const int grid = 8 * ((2 * device_cu_count() + 7) / 8);
     const size_t lds = prefill_lds_bytes(a.E);
+    const bool xk = a.xk != nullptr;
     if (a.gamma_h) {
-      hipLaunchKernelGGL(gemm_prefill_kernel<true>, dim3(a.N / 256, (unsigned)tiles), dim3(256), lds, st, a);
+      if (xk) hipLaunchKernelGGL((gemm_prefill_kernel<true, true>), dim3(grid), dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<true, false>), dim3(grid), dim3(256), lds, st, a);
     } else {
-      hipLaunchKernelGGL(gemm_prefill_kernel<false>, dim3((a.N + 255) / 256, (unsigned)tiles), dim3(256), lds, st,
-                         a);
+      if (xk) hipLaunchKernelGGL((gemm_prefill_kernel<false, true>), dim3(grid), dim3(256), lds, st, a);
+      else hipLaunchKernelGGL((gemm_prefill_kernel<false, false>), dim3(grid), dim3(256), lds, st, a);
     }
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;

@@ -18,6 +18,7 @@ struct GemmArgs {
   const float* gscale;    // [E]
   const uint8_t* q;       // [rows][K/2]
   const uint8_t* s;       // [rows][K/32]
+  const void* xk;         // [rows][K] f16 activations in the kernel's group order, or nullptr
   const float* gamma_a;   // [E]
   const int32_t* offsets; // [E+1]
   void* y;                // [rows][N] (plain epilogue)
@@ -27,6 +28,7 @@ struct GemmArgs {
   const float* gamma_h;   // [E] or nullptr for the plain epilogue
   uint8_t* h_q;
   uint8_t* h_s;
+  void* h_k;              // [rows][I] f16 copy of the requantized h in the kernel's group order, or nullptr
   float* dump;            // [rows][N] fp32 gate_up outputs, or nullptr
 };
 
@@ -36,7 +38,7 @@ int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
                     const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
-                    int32_t E, uint8_t* q, uint8_t* s);
+                    int32_t E, uint8_t* q, uint8_t* s, void* xk);
 
 int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
                         float* gamma_out);

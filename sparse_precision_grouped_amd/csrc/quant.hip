@@ -19,7 +19,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                                                        int64_t ld_x, const int32_t* __restrict__ gather, int32_t k,
                                                        int64_t rows, const float* __restrict__ gamma,
                                                        const int32_t* __restrict__ offsets, int32_t E,
-                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                       uint8_t* __restrict__ xk) {
   __shared__ int32_t off_l[kQuantMaxE + 1];
   const int lane = threadIdx.x & 63;
   const int nchunk = (K + 511) / 512;
@@ -74,17 +75,23 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   if (valid) {
     *(uint32_t*)(q + p * (K / 2) + 4 * ch) = codes;
     if ((lane & 3) == 0) s[p * (K / 32) + ch / 4] = (uint8_t)sc;
+    if (xk) {
+      // the same values dequantized (exact in f16), in the GEMM's de-interleaved group order
+      f16x2 sv, unused;
+      e4m3_pair_f16x2(sc, sv, unused);
+      *(u32x4*)(xk + (p * K + 8 * ch) * 2) = decode_x_group(codes, sv);
+    }
   }
 }
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
                     const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
-                    int32_t E, uint8_t* q, uint8_t* s) {
+                    int32_t E, uint8_t* q, uint8_t* s, void* xk) {
   if (rows == 0) return MOESQ_OK;
   const int64_t waves = rows * ((K + 511) / 512);
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x,
-                     gather_slot, k, rows, gamma, offsets, E, q, s);
+                     gather_slot, k, rows, gamma, offsets, E, q, s, (uint8_t*)xk);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 
@@ -263,7 +270,8 @@ int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, in
 //   [16 l, +16)        the 16 packed bytes of the lane's eight 8-groups, each group's two kept
 //                      bytes (b0, b1) rewritten as (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4), so one
 //                      FP4->f16 convert yields a de-interleaved 2:4 operand register;
-//   [1024 + 4 l, +4)   the 4 mask bytes (pair nibbles, unchanged);
+//   [1024 + 4 l, +4)   the sparse-index codes (i | j << 2 of the kept pairs i < j) of the eight
+//                      groups, one nibble each, in the group order 0, 2, 4, 6, 1, 3, 5, 7;
 //   [1280 + 2 l, +2)   the 2 UE4M3 block-scale codes.
 // Fragments are stored e-major, then rb, then ss, so one wave streams K with contiguous reads.
 __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict__ packed,
@@ -294,7 +302,14 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
   }
   uint8_t* F = kl + frag * 1408;
   *(uint4*)(F + 16 * l) = make_uint4(o[0], o[1], o[2], o[3]);
-  *(uint32_t*)(F + 1024 + 4 * l) = *(const uint32_t*)(mask + row * (K / 16) + 16 * ss + 4 * c);
+  const uint32_t mk = *(const uint32_t*)(mask + row * (K / 16) + 16 * ss + 4 * c);
+  uint32_t codes = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int g = (k < 4) ? 2 * k : 2 * (k - 4) + 1;
+    codes |= pair_index_code((mk >> (4 * g)) & 15u) << (4 * k);
+  }
+  *(uint32_t*)(F + 1024 + 4 * l) = codes;
   *(uint16_t*)(F + 1280 + 2 * l) = *(const uint16_t*)(scale + row * (K / 32) + 8 * ss + 2 * c);
 }
 

@@ -80,14 +80,14 @@ def test_quantize_validation(L):
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     f = L.moesq_quantize_act
     vp = ctypes.c_void_p
-    f.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp]
+    f.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp, vp]
     base = dict(x=FAKE, dt=0, T=8, K=64, ld=64, g=None, k=1, rows=8, gamma=FAKE, off=None, E=0, q=FAKE, s=FAKE)
 
     def call(**kw):
         a = dict(base, **kw)
         return f(None, _p(a["x"]), a["dt"], a["T"], a["K"], a["ld"], _p(a["g"]) if a["g"] else None, a["k"],
                  a["rows"], _p(a["gamma"]) if a["gamma"] else None, _p(a["off"]) if a["off"] else None, a["E"],
-                 _p(a["q"]), _p(a["s"]))
+                 _p(a["q"]), _p(a["s"]), None)
     assert call(K=48, ld=48) == EARG      # K % 32 != 0
     assert call(dt=7) == EARG             # dtype
     assert call(ld=32) == EARG            # ld_x < K
@@ -103,9 +103,9 @@ def test_gemm_and_mlp_validation(L):
                     ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
     vp = ctypes.c_void_p
     g = L.moesq_grouped_gemm
-    g.argtypes = [vp, ctypes.POINTER(CW), vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, ctypes.c_uint32]
+    g.argtypes = [vp, ctypes.POINTER(CW), vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, ctypes.c_uint32]
     W = CW(4, 128, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
-    call = lambda W, y=FAKE, dt=0: g(None, ctypes.byref(W), _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(y),  # noqa
+    call = lambda W, y=FAKE, dt=0: g(None, ctypes.byref(W), _p(FAKE), _p(FAKE), None, _p(FAKE), _p(FAKE), 16, _p(y),  # noqa
                                      dt, 0)
     assert call(W, dt=3) == EARG
     assert call(W, y=0) == EARG
@@ -114,12 +114,12 @@ def test_gemm_and_mlp_validation(L):
     assert call(CW(4, 100, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS     # N % 64 != 0
     assert call(CW(4, 128, 256, 0, 0, 0, FAKE, 0)) == EARG            # no kernel layout
     m = L.moesq_expert_mlp
-    m.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+    m.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                   ctypes.c_int32, vp, ctypes.c_size_t, ctypes.c_uint32]
     W13 = CW(4, 512, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
     W2 = CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
     mc = lambda a, b, ws=FAKE, wsb=1 << 30: m(None, ctypes.byref(a), ctypes.byref(b), _p(FAKE), _p(FAKE),  # noqa
-                                             _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(FAKE), 0,
+                                             None, _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(FAKE), 0,
                                              _p(ws) if ws else None, wsb, 0)
     assert mc(W13, CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # W2.K != I
     assert mc(W13, CW(3, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # expert count mismatch
@@ -165,6 +165,7 @@ def test_workspace_sizes(L):
     ws = lambda kind, T=0, k=0, E=0, K=0, N=0, I=0: L.moesq_workspace_bytes(kind, T, k, E, K, N, I)  # noqa
     a = lambda x: (x + 255) // 256 * 256  # noqa
     rows, I = 1000, 2048
-    assert ws(2, rows, 0, 384, 7168, 0, I) == a(rows * I // 2) + a(rows * I // 32)
-    assert ws(3, rows, 0, 384, 7168, 0, I) == a(rows * I // 2) + a(rows * I // 32) + rows * 2 * I * 4
+    base = a(rows * I // 2) + a(rows * I // 32) + a(rows * I * 2)
+    assert ws(2, rows, 0, 384, 7168, 0, I) == base
+    assert ws(3, rows, 0, 384, 7168, 0, I) == base + rows * 2 * I * 4
     assert ws(4, E=384) == 384 * 4

@@ -88,8 +88,16 @@ def _kernel_layout_reference(packed, mask, scale):
     sh[..., 0::2] = (b0 & 15) | ((b1 & 15) << 4)
     sh[..., 1::2] = (b0 >> 4) | (b1 & 0xF0)
     out[..., :1024] = sh.transpose(0, 1, 3, 4, 2, 5).reshape(E, N // 16, nss, 1024)
-    mk = mask.reshape(E, N // 16, 16, nss, 4, 4).transpose(0, 1, 3, 4, 2, 5)
-    out[..., 1024:1280] = mk.reshape(E, N // 16, nss, 256)
+    # mask nibbles -> pair-index codes i | j << 2, nibble order (g0, g2, g4, g6, g1, g3, g5, g7)
+    code = np.zeros(16, np.uint32)
+    for i, j in ((0, 1), (0, 2), (1, 2), (0, 3), (1, 3), (2, 3)):
+        code[(1 << i) | (1 << j)] = i | (j << 2)
+    mk = mask.reshape(E, N // 16, 16, nss, 4, 4).transpose(0, 1, 3, 4, 2, 5).astype(np.uint32)
+    word = mk[..., 0] | (mk[..., 1] << 8) | (mk[..., 2] << 16) | (mk[..., 3] << 24)
+    nib = [code[(word >> (4 * g)) & 15] for g in range(8)]
+    order = [0, 2, 4, 6, 1, 3, 5, 7]
+    cw = sum(nib[order[kk]] << np.uint32(4 * kk) for kk in range(8)).astype(np.uint32)
+    out[..., 1024:1280] = np.ascontiguousarray(cw.reshape(E, N // 16, nss, 64)).view(np.uint8)
     sc = scale.reshape(E, N // 16, 16, nss, 4, 2).transpose(0, 1, 3, 4, 2, 5)
     out[..., 1280:] = sc.reshape(E, N // 16, nss, 128)
     return out.reshape(-1)
@@ -166,6 +174,28 @@ def test_quantize_dispatch_bitexact(name):
     assert np.array_equal(host(s), so)
 
 
+def _xk_reference(q, s):
+    """The f16 operand copy from its definition: exact dequantized values, each 8-group stored in
+    the order (0, 2, 4, 6, 1, 3, 5, 7)."""
+    v = orc.dequant(q, s)
+    R, K = v.shape
+    g = v.reshape(R, K // 8, 8)[:, :, [0, 2, 4, 6, 1, 3, 5, 7]]
+    return g.reshape(R, K).astype(np.float16)
+
+
+@pytest.mark.parametrize("name", ["c0", "t_zipf"])
+def test_quantize_f16_operand_copy(name):
+    c = single_case(name)
+    say("quantize xk", name)
+    R, k = c["R"], c["k"]
+    rt = mq.moesq_route_permute(dev(c["ids"]), c["E"])
+    q, s, xk = mq.moesq_quantize_act(dev(c["x"]), dev(c["ga"]), gather_slot=rt["sorted_slot"], k=k,
+                                     offsets=rt["offsets"], xk=True)
+    qo, so = orc.dispatch_quantize(c["x"], R["sorted_slot"], k, R["offsets"], c["ga"])
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    assert np.array_equal(host(xk).view(np.uint16), _xk_reference(qo, so).view(np.uint16))
+
+
 def test_quantize_plain_and_bf16_and_zero():
     say("quantize plain / bf16 / zeros")
     x = gen.student_t(3, gen.act_stream(9), 37 * 512).reshape(37, 512)
@@ -200,7 +230,7 @@ def _gemm_inputs(c):
 
 @pytest.mark.parametrize("name,proj,nrows", [("c0", 0, None), ("c1", 0, None), ("t_zipf", 0, None),
                                              ("c2", 0, 384)])
-@pytest.mark.parametrize("flags", ["decode", "prefill"])
+@pytest.mark.parametrize("flags", ["decode", "prefill", "prefill_xk"])
 def test_grouped_gemm_parity(name, proj, nrows, flags):
     c = single_case(name, proj)
     say("gemm", name, proj, flags)
@@ -208,9 +238,11 @@ def test_grouped_gemm_parity(name, proj, nrows, flags):
     off = c["R"]["offsets"]
     rl = None if nrows is None else sample_rows(off, nrows)
     fl = mq.F_FORCE_DECODE if flags == "decode" else mq.F_FORCE_PREFILL
-    y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl)
+    xk = dev(_xk_reference(qo, so)) if flags == "prefill_xk" else None
+    y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl,
+                              xk=xk)
     yb = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.bfloat16,
-                               flags=fl)
+                               flags=fl, xk=xk)
     rows = np.arange(int(off[-1])) if rl is None else rl
     Wo = c["Wo"].ensure(np.searchsorted(off, rows, side="right") - 1)
     ref = orc.grouped_gemm(Wo.as_dict(), qo, so, c["ga"], off, rows)
@@ -290,6 +322,9 @@ def test_mlp_parity_tiny():
     rows = int(R["offsets"][-1])
     y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
                                 flags=mq.F_DUMP_GATEUP)
+    y_xk, _ = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]),
+                                  y_dtype=torch.float32, xk=dev(_xk_reference(qo, so)))
+    assert np.array_equal(host(y_xk), host(y))   # same operands, same kernel order of operations
     hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
     # gate_up GEMM stage
     assert orc.rel_frobenius(host(dump), M["y13"]) <= GEMM_TOL
