@@ -61,6 +61,73 @@ def _src_hash():
     return h.hexdigest()[:16]
 
 
+COPY_BYTES = 1 << 30  # payload of the plain-copy calibration launch
+
+
+def calibrate_copy(torch, iters=5):
+    """A plain device copy of COPY_BYTES, run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to get the
+    counter's reading for a launch whose HBM traffic is known (COPY_BYTES read, COPY_BYTES written)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "iters": iters}))
+
+
+def _pmc_means(csv_path, match):
+    """Mean per-dispatch value (KiB) and dispatch count of every counter in a rocprofv3 counter CSV,
+    per kernel whose name contains `match`."""
+    import csv
+    acc = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            if match not in k:
+                continue
+            key = (k.split("(")[0], r["Counter_Name"])
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in acc.items()}
+
+
+def summarize_pmc(argv):
+    """--summarize-pmc WORKLOAD FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV: scale the GEMM
+    kernels' FETCH_SIZE / WRITE_SIZE by the copy calibration and record bytes per dominant launch in
+    profiles/traffic.json (keyed by workload and kernel, tagged with the kernel source hash)."""
+    wl, fcsv, wcsv, cf, cw = argv
+    fetch = _pmc_means(fcsv, "gemm_")
+    write = _pmc_means(wcsv, "gemm_")
+    # the calibration run's copy launch is the one that reads the most (the fill before it reads nothing)
+    cf_all = {k: v for (k, c), v in _pmc_means(cf, "").items() if c == "FETCH_SIZE"}
+    copy_name = max(cf_all, key=lambda k: cf_all[k][0])
+    cfetch_kib = cf_all[copy_name][0]
+    cwrite_kib = _pmc_means(cw, "")[(copy_name, "WRITE_SIZE")][0]
+    f_fetch = COPY_BYTES / 1024.0 / cfetch_kib
+    f_write = COPY_BYTES / 1024.0 / cwrite_kib
+    per_kernel = {}
+    for (k, c), (v, n) in fetch.items():
+        if c == "FETCH_SIZE":
+            per_kernel.setdefault(k, {})["fetch_bytes"] = v * 1024.0 * f_fetch
+            per_kernel[k]["dispatches"] = n
+    for (k, c), (v, n) in write.items():
+        if c == "WRITE_SIZE":
+            per_kernel.setdefault(k, {})["write_bytes"] = v * 1024.0 * f_write
+    if wl == "c4":
+        key = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
+        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if "prefill" in k)
+    else:
+        key = "gemm_decode_kernel" if any("decode" in k for k in per_kernel) else "gemm_prefill_kernel"
+        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    t = json.load(open(path)) if os.path.exists(path) else {}
+    t["%s:%s" % (wl, key)] = {"bytes_per_launch": round(total), "src_hash": _src_hash(), "copy_kernel": copy_name,
+                              "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
+                              "kernels": {k: {kk: round(vv) for kk, vv in d.items()} for k, d in per_kernel.items()}}
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+    print(json.dumps(t["%s:%s" % (wl, key)]))
+
+
 def _traffic(kernel_key):
     """HBM traffic per launch from a committed rocprofv3 counter summary, if it was taken on the
     current kernel source; else None."""
@@ -262,7 +329,15 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (traffic-counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="host only: write profiles/traffic.json from rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only (no collective or sharded path); "
@@ -270,6 +345,9 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return 0
 
     import gen
     import sparse_precision_grouped_amd as mq

@@ -118,3 +118,25 @@ def sample_rows(offsets, n_target, seed=0):
     extra = rng.choice(total, size=min(total, max(0, n_target - len(rows))), replace=False)
     rows.update(int(r) for r in extra)
     return np.array(sorted(rows), np.int64)
+
+
+def sample_expert_rows(offsets, n_experts=3, per_expert=48, seed=0):
+    """Rows of a few experts (the busiest, the least busy nonempty one, random others); per expert its
+    first rows, its last row (a ragged tile tail) and random rows, at most per_expert each."""
+    offsets = np.asarray(offsets)
+    counts = np.diff(offsets)
+    nz = np.flatnonzero(counts > 0)
+    rng = np.random.default_rng(seed)
+    pick = [int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])]
+    others = [int(e) for e in rng.permutation(nz) if int(e) not in pick]
+    pick += others[:max(0, n_experts - 2)]
+    rows = set()
+    for e in pick:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        cand = list(range(lo, min(hi, lo + 4))) + [hi - 1]
+        extra = rng.choice(hi - lo, size=min(hi - lo, per_expert), replace=False) + lo
+        for r in cand + [int(v) for v in extra]:
+            if len([x for x in rows if lo <= x < hi]) >= per_expert:
+                break
+            rows.add(int(r))
+    return np.array(sorted(rows), np.int64), sorted(pick)

@@ -10,7 +10,8 @@ import torch
 import gen
 import oracle as orc
 
-from gpu_cases import DEV, dev, host, say, sample_rows, single_case
+from gpu_cases import (DEV, OracleWeights, dev, device_weights, host, sample_expert_rows, sample_rows, say,
+                       single_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -254,6 +255,27 @@ def test_grouped_gemm_parity(name, proj, nrows, flags):
     assert orc.rel_frobenius(gotb, bf16_round(ref)) <= GEMM_TOL
 
 
+@pytest.mark.parametrize("proj", [0, 1])
+@pytest.mark.parametrize("flags", ["auto", "prefill"])
+def test_grouped_gemm_parity_c3_full_size(proj, flags):
+    """Kimi-shaped decode projections at full size (E=384; gate_up K=7168 N=4096, down K=2048
+    N=7168, 512 routed rows), in the launch the benchmark uses (auto = weight streaming) and in the
+    tiled kernel; the oracle evaluates every output column of the rows of a few sampled experts."""
+    c = single_case("c3", proj, x_tag=proj)
+    say("gemm c3 full size proj", proj, flags)
+    qo, so = _gemm_inputs(c)
+    off = c["R"]["offsets"]
+    fl = 0 if flags == "auto" else mq.F_FORCE_PREFILL
+    y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl)
+    rows, experts = sample_expert_rows(off, n_experts=10, per_expert=24)
+    say("sampled experts", experts, "rows", rows.size)
+    Wo = c["Wo"].ensure(experts)
+    ref = orc.grouped_gemm(Wo.as_dict(), qo, so, c["ga"], off, rows)
+    err = orc.rel_frobenius(host(y)[rows], ref)
+    say("rel-Frobenius", err)
+    assert err <= GEMM_TOL
+
+
 def test_grouped_gemm_deterministic_and_variants_agree():
     c = single_case("t_zipf")
     say("gemm determinism t_zipf")
@@ -346,3 +368,67 @@ def test_mlp_parity_tiny():
     out = mq.moesq_unpermute_combine(y, dev(R["slot_pos"]), dev(wts), out_dtype=torch.float32)
     ref = orc.combine(M["y2"], R["slot_pos"], wts)
     assert orc.rel_frobenius(host(out), ref) <= 1e-2
+
+
+def test_mlp_parity_c4_full_size():
+    """The Kimi-shaped routed-expert MLP at full size (E=384, H=7168, I=2048, T=8192, top-8, Zipf),
+    in the benchmark's launch configuration (f16 operand copy from the quantizer). Stage by stage
+    on the rows of sampled experts: activation codes (all rows, bit-exact), gate_up (fp32 dump),
+    requantized h, the down GEMM on the oracle's h codes, the end-to-end chain, and the combine."""
+    cfg = gen.CONFIGS["c4"]
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    say("mlp c4 full size: weights")
+    W13, _ = device_weights(cfg, 0, E, I2, H, host_draw=False)
+    W2, _ = device_weights(cfg, 1, E, H, I, host_draw=False)
+    say("mlp c4: inputs")
+    x = gen.activations(cfg, 0, T, H)
+    ids, wts = gen.routing(cfg)
+    R = orc.route(ids, E)
+    off = R["offsets"]
+    rows_all = int(off[-1])
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    gh = np.full(E, cfg.gamma_h, np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, off, ga)
+    say("mlp c4: quantize on the device")
+    rt = mq.moesq_route_permute(dev(ids), E)
+    q, s, xk = mq.moesq_quantize_act(dev(x), dev(ga), gather_slot=rt["sorted_slot"], k=k, offsets=rt["offsets"],
+                                     xk=True)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    say("mlp c4: expert MLP")
+    y, ws = mq.moesq_expert_mlp(W13, W2, q, s, dev(ga), dev(gh), rt["offsets"], y_dtype=torch.float32,
+                                flags=mq.F_DUMP_GATEUP, xk=xk)
+    hq, hs, dump = mq.mlp_workspace_views(ws, rows_all, I, dump=True)
+    rows, experts = sample_expert_rows(off, n_experts=3, per_expert=32)
+    say("mlp c4: oracle on experts", experts, "rows", rows.size)
+    W13o = OracleWeights(cfg, 0, E, I2, H).ensure(experts).as_dict()
+    W2o = OracleWeights(cfg, 1, E, H, I).ensure(experts).as_dict()
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, off, rows)
+    err13 = orc.rel_frobenius(host(dump)[rows], M["y13"])
+    hq_g, hs_g = host(hq)[rows], host(hs)[rows]
+    flips = np.mean(orc.dequant(hq_g, hs_g) != orc.dequant(M["hq"], M["hs"]))
+    say("gate_up rel-Frobenius", err13, "h code flips", flips)
+    assert err13 <= GEMM_TOL
+    assert np.mean(hs_g != M["hs"]) <= 1e-3 and flips <= 2e-3
+    err_chain = orc.rel_frobenius(host(y)[rows], M["y2"])
+    say("chain y2 rel-Frobenius", err_chain)
+    assert err_chain <= 1e-2
+    # down GEMM alone on the oracle's h codes (other rows zero: rows are independent)
+    hq_o = np.zeros((rows_all, I // 2), np.uint8)
+    hs_o = np.zeros((rows_all, I // 32), np.uint8)
+    hq_o[rows], hs_o[rows] = M["hq"], M["hs"]
+    yd = mq.moesq_grouped_gemm(W2, dev(hq_o), dev(hs_o), dev(gh), dev(off), y_dtype=torch.float32)
+    errd = orc.rel_frobenius(host(yd)[rows], M["y2"])
+    say("down rel-Frobenius", errd)
+    assert errd <= GEMM_TOL
+    del y, ws, dump, yd
+    # combine at full size on a generated expert output, sampled tokens
+    say("mlp c4: combine")
+    y2 = gen.normal(5, gen.act_stream(12), rows_all * H).reshape(rows_all, H)
+    yt = torch.from_numpy(y2).to(torch.bfloat16)
+    out = host(mq.moesq_unpermute_combine(yt.to(DEV), rt["slot_pos"], dev(wts), out_dtype=torch.float32))
+    toks = np.sort(np.random.default_rng(1).choice(T, 64, replace=False))
+    sp = R["slot_pos"].reshape(T, k)[toks].ravel()
+    # the sampled tokens as a problem of their own: their k rows each, in (token, slot) order
+    ref = orc.combine(yt[torch.from_numpy(sp)].to(torch.float64).numpy(), np.arange(sp.size, dtype=np.int32),
+                      wts[toks])
+    assert orc.rel_frobenius(out[toks], ref) <= 1e-6
