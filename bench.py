@@ -145,7 +145,7 @@ def _traffic(kernel_key):
 class Workload:
     """Device buffers, graphs and accounting for one named config."""
 
-    def __init__(self, name, rotate, torch, gen, mq):
+    def __init__(self, name, rotate, torch, gen, mq, f16_operand=False):
         self.torch, self.gen, self.mq = torch, gen, mq
         self.cfg = cfg = gen.CONFIGS[name]
         self.name = name
@@ -176,9 +176,10 @@ class Workload:
                                          device=dev)
             sl["q"] = torch.empty((self.rows, cfg.K // 2), dtype=torch.uint8, device=dev)
             sl["s"] = torch.empty((self.rows, cfg.K // 32), dtype=torch.uint8, device=dev)
-            # the tiled (prefill) kernel reads the f16 operand copy written by the quantizer
+            # optional: the quantizer also writes the f16 operand copy that the tiled kernel can stage
+            # straight into LDS (more HBM traffic, fewer instructions in the GEMM)
             sl["xk"] = (torch.empty((self.rows, cfg.K), dtype=torch.float16, device=dev)
-                        if self.tiled else None)
+                        if self.tiled and f16_operand else None)
             if self.kind == "single":
                 sl["y"] = torch.empty((self.rows, cfg.N), dtype=torch.bfloat16, device=dev)
             elif self.kind == "pair":
@@ -225,13 +226,13 @@ class Workload:
         rt = sl["rt"]
         mq.moesq_route_permute(sl["ids"], cfg.E, rt["counts"], rt["offsets"], rt["sorted_slot"], rt["slot_pos"],
                                sl["ws_route"])
-        mq.moesq_quantize_act(sl["x"], sl["ga"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
+        mq.moesq_quantize_act(sl["x"], sl["ga"], slot_pos=rt["slot_pos"], k=cfg.k, offsets=rt["offsets"],
                               q=sl["q"], s=sl["s"], xk=sl["xk"])
         if self.kind == "single":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
         elif self.kind == "pair":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
-            mq.moesq_quantize_act(sl["x2"], sl["ga2"], gather_slot=rt["sorted_slot"], k=cfg.k, offsets=rt["offsets"],
+            mq.moesq_quantize_act(sl["x2"], sl["ga2"], slot_pos=rt["slot_pos"], k=cfg.k, offsets=rt["offsets"],
                                   q=sl["q2"], s=sl["s2"])
             mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"])
         else:
@@ -329,6 +330,8 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--f16-operand", action="store_true",
+                    help="tiled workloads: quantizer writes the f16 activation copy and the GEMM reads it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (traffic-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -353,7 +356,7 @@ def main(argv=None):
     import sparse_precision_grouped_amd as mq
 
     torch.cuda.set_device(0)
-    wl = Workload(args.workload, args.rotate, torch, gen, mq)
+    wl = Workload(args.workload, args.rotate, torch, gen, mq, args.f16_operand)
     wl.capture()
     for i in range(args.warmup):
         wl.graphs[i % wl.R].replay()

@@ -108,9 +108,12 @@ int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_
 /*
  * Dynamic NVFP4 activation quantization (paper Section 3.4 and Appendix D.1: activations are
  * quantized at run time into 32-element blocks; Eq. 3 + Eq. 5 with the given tensor scale), fused
- * with token dispatch: permuted row p reads token row gather_slot[p] / k of x.
+ * with token dispatch (a scatter: every token row of x is read once and its codes are written to each
+ * permuted row the token is routed to).
  *   x           [T][ld_x] fp32 or bf16 (x_dtype), K <= ld_x, K % 32 == 0
- *   gather_slot [rows] or NULL. NULL: rows must equal T and row p reads x row p.
+ *   slot_pos    [T*k] or NULL: permuted row of the j-th routed copy of token t at slot_pos[t*k + j]
+ *               (moesq_route_permute's output; negative = dropped). rows >= T*k, k <= 512; permuted
+ *               rows no slot points to are not written. NULL: rows must equal T and row p is x row p.
  *   gamma       [G] fp32 tensor scales. With offsets != NULL, row p uses gamma[e] where
  *               offsets[e] <= p < offsets[e+1] (G = E, the per-expert input scale of the model
  *               card); with offsets == NULL every row uses gamma[0].
@@ -124,7 +127,7 @@ int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_
  * code, +0 for zero); q = 0 when s == 0. All in IEEE fp32 without fused multiply-add.
  */
 int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
-                       const int32_t *gather_slot, int32_t k, int64_t rows, const float *gamma,
+                       const int32_t *slot_pos, int32_t k, int64_t rows, const float *gamma,
                        const int32_t *offsets, int32_t E, uint8_t *q, uint8_t *s, void *xk);
 
 /*
@@ -138,7 +141,7 @@ int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, 
  *   offsets     [E+1] from moesq_route_permute (device)
  *   y           [rows][N] fp32 or bf16 (round to nearest even). Rows >= offsets[E] are not written.
  * Requires W->kl (MOESQ_ERR_INVALID_ARG if NULL), K % 256 == 0 and N % 64 == 0
- * (MOESQ_ERR_UNSUPPORTED otherwise); E <= 4096.
+ * (MOESQ_ERR_UNSUPPORTED otherwise); E <= 1024.
  */
 int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s, const void *xk,
                        const float *gamma_a, const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype,

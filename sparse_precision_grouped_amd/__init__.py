@@ -179,16 +179,17 @@ def moesq_route_permute(topk_ids, E, counts=None, offsets=None, sorted_slot=None
     return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos)
 
 
-def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=None, rows=None, xk=None):
-    """NVFP4-quantize rows of x [T, K] (fp32/bf16). With gather_slot, permuted row p reads token
-    gather_slot[p] // k and (with offsets) uses gamma[expert of p]. Returns (q [rows,K/2], s [rows,K/32]);
+def moesq_quantize_act(x, gamma, slot_pos=None, k=1, offsets=None, q=None, s=None, rows=None, xk=None):
+    """NVFP4-quantize rows of x [T, K] (fp32/bf16). With slot_pos (from moesq_route_permute), token t's
+    j-th routed copy goes to permuted row slot_pos[t*k + j] and (with offsets) uses gamma[expert of that
+    row]. Returns (q [rows,K/2], s [rows,K/32]);
     with ``xk`` (a [rows, K] float16 tensor, or True to allocate one) also writes the GEMM's f16
     operand copy and returns (q, s, xk)."""
     _dev(x)
     T, K = x.shape
     assert x.stride(1) == 1
     if rows is None:
-        rows = T if gather_slot is None else gather_slot.numel()
+        rows = T if slot_pos is None else slot_pos.numel()
     E = 0 if offsets is None else offsets.numel() - 1
     q = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
@@ -196,7 +197,7 @@ def moesq_quantize_act(x, gamma, gather_slot=None, k=1, offsets=None, q=None, s=
     if xk is True:
         xk = torch.empty((rows, K), dtype=torch.float16, device=x.device)
     _check("moesq_quantize_act",
-           lib().moesq_quantize_act(_stream(), _p(x), _dtype_code(x.dtype), T, K, x.stride(0), _p(gather_slot), k,
+           lib().moesq_quantize_act(_stream(), _p(x), _dtype_code(x.dtype), T, K, x.stride(0), _p(slot_pos), k,
                                     rows, _p(gamma), _p(offsets), E, _p(q), _p(s), _p(xk if want_xk else None)))
     return (q, s, xk) if want_xk else (q, s)
 

@@ -71,22 +71,25 @@ int moesq_route_permute(void* stream, const int32_t* topk_ids, int64_t T, int32_
 }
 
 int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
-                       const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
+                       const int32_t* slot_pos, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
                        int32_t E, uint8_t* q, uint8_t* s, void* xk) {
   if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
   if (T < 0 || rows < 0 || K <= 0 || K % 32 != 0 || ld_x < K) return MOESQ_ERR_INVALID_ARG;
   if (!gamma) return MOESQ_ERR_INVALID_ARG;
-  if (rows > 0 && (!x || !q || !s)) return MOESQ_ERR_INVALID_ARG;
-  if (gather_slot) {
+  if (T > 0 && (!x || !q || !s)) return MOESQ_ERR_INVALID_ARG;
+  if (slot_pos) {
     if (k <= 0) return MOESQ_ERR_INVALID_ARG;
+    if (rows < T * (int64_t)k) return MOESQ_ERR_INVALID_ARG;
+    if (k > 512) return MOESQ_ERR_UNSUPPORTED;
   } else if (rows != T) {
     return MOESQ_ERR_INVALID_ARG;
   }
   if (offsets && E <= 0) return MOESQ_ERR_INVALID_ARG;
   if (offsets && E > 4096) return MOESQ_ERR_UNSUPPORTED;
+  if (rows >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
   if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4) || !aligned(xk, 16)) return MOESQ_ERR_UNSUPPORTED;
-  return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, gather_slot, k, rows, gamma,
-                         offsets, E, q, s, xk);
+  return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, slot_pos, k, gamma, offsets, E,
+                         q, s, xk);
 }
 
 static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,

@@ -20,9 +20,10 @@
 //    mapping. Buffer loads past an expert's last token return zero, which pads partial tiles.
 //  - Decode (few tokens per expert): weight streaming. One workgroup = 16*MF weight rows of one
 //    expert; its 4 waves split K and reduce through LDS in a fixed order (deterministic).
-//  - Prefill: 256 x 64 tiles (4 waves x 4 m-fragments x 16 rows, 4 n-fragments x 16 tokens);
-//    the activation tile of each super-step is decoded once into LDS (f16, de-interleaved) and
-//    shared by the four waves; the weights go from global memory straight to registers.
+//  - Prefill: persistent 512 x 128 tiles (8 waves x 4 m-fragments x 16 rows, 8 n-fragments x 16
+//    tokens); the activation tile of each super-step is staged once into LDS (f16, de-interleaved:
+//    decoded from the NVFP4 codes, or loaded straight from the quantizer's f16 copy) and shared by
+//    the eight waves; the weights go from global memory straight to registers.
 //  - The gate_up GEMM of the MLP fuses SwiGLU and the NVFP4 requantization of h in its epilogue:
 //    a wave owns the gate rows and the matching up rows of 32 intermediate columns, which is one
 //    32-element scale block per token.
@@ -41,11 +42,18 @@ MOESQ_DEV f16x16 concat_x(u32x4 lo, u32x4 hi) {
   return __builtin_bit_cast(f16x16, v);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Store 4 consecutive outputs scaled by alpha: fp32, or bf16 rounded to nearest even by the gfx950
+// packed convert.
 MOESQ_DEV void store4(void* y, int64_t off, f32x4 v, float alpha, int bf16) {
   if (bf16) {
+    const bf16x2 lo = __builtin_convertvector((f32x2){v.x * alpha, v.y * alpha}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){v.z * alpha, v.w * alpha}, bf16x2);
     uint2 o;
-    o.x = f32_to_bf16_bits(v.x * alpha) | (f32_to_bf16_bits(v.y * alpha) << 16);
-    o.y = f32_to_bf16_bits(v.z * alpha) | (f32_to_bf16_bits(v.w * alpha) << 16);
+    o.x = __builtin_bit_cast(uint32_t, lo);
+    o.y = __builtin_bit_cast(uint32_t, hi);
     *(uint2*)((uint16_t*)y + off) = o;
   } else {
     float4 o;
@@ -70,14 +78,16 @@ struct WStage {
 };
 
 // soff[f]: byte offset (wave uniform) of fragment f's first super-step within the expert's layout.
+// The fragment offset goes into the per-lane offset operand: a uniform value that the compiler keeps
+// in a VGPR would otherwise need a readfirstlane loop to reach the scalar offset operand.
 template <int MF>
 MOESQ_DEV void load_w(WStage<MF>& st, rsrc_t rw, const uint32_t (&soff)[MF], int lane, int ss) {
 #pragma unroll
   for (int f = 0; f < MF; f++) {
     const int so = (int)(soff[f] + (uint32_t)ss * kFragBytes);
-    st.pk[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * lane, so, 0));
-    st.mk[f] = __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * lane + 1024, so, 0);
-    st.sw[f] = __builtin_amdgcn_raw_buffer_load_b16(rw, 2 * lane + 1280, so, 0);
+    st.pk[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * lane + so, 0, 0));
+    st.mk[f] = __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * lane + 1024 + so, 0, 0);
+    st.sw[f] = __builtin_amdgcn_raw_buffer_load_b16(rw, 2 * lane + 1280 + so, 0, 0);
   }
 }
 
@@ -237,11 +247,19 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   }
 }
 
-// =========================================================================== prefill kernel =====
-constexpr int kPfTokens = 64;                     // T_N
-constexpr int kPfGroups = 32;                     // 8-element groups per 256-K super-step
-constexpr int kPfRowBytes = kPfGroups * 16 + 16;  // FP4-staging path: decoded groups of one token (+ pad)
-constexpr int kPfTileBytes = kPfTokens * kPfRowBytes;
+// ============================================================================= tiled kernel =====
+// Prefill-sized problems. A workgroup of 8 waves computes 512 weight rows x 128 tokens of one expert
+// (MLP gate_up: 256 gate rows and the matching 256 up rows); a wave owns 64 rows (4 m-fragments)
+// and all 128 tokens (8 n-fragments), so each decoded weight operand feeds 8 MFMAs and each staged
+// activation operand is shared by all 8 waves. Token tiles past an expert's last token skip their
+// empty 16-token fragments.
+constexpr int kTileTok = 128;                          // T_N
+constexpr int kTileNF = kTileTok / 16;                 // n-fragments per wave
+constexpr int kTileThreads = 512;                      // 8 waves
+constexpr int kPfGroups = 32;                          // 8-element groups per 256-K super-step
+constexpr int kPfRowBytes = kPfGroups * 16 + 16;       // FP4 path: decoded groups of one token (+ pad)
+constexpr int kBTileFp4 = kTileTok * kPfRowBytes;      // 67584 B
+constexpr int kBTileF16 = kTileTok * kPfGroups * 16;   // 65536 B
 
 // Activation tile (B) in LDS. FP4-staging path: token row r, group g at r * kPfRowBytes + 16 g.
 // f16 path (direct-to-LDS loads): chunk (r, g) at 16 * (32 r + (g ^ (r & 31))), an XOR swizzle that
@@ -252,9 +270,9 @@ MOESQ_DEV const uint8_t* b_chunk(const uint8_t* Bs, int r, int g) {
   return Bs + r * kPfRowBytes + 16 * g;
 }
 
-// Activation staging of one super-step from NVFP4 codes: thread (lane = token, wave = quarter of the
-// super-step) reads 32 code bytes (8 groups = 64 K) and their two block scales and decodes them to
-// f16 (de-interleaved) into LDS.
+// Activation staging of one super-step from NVFP4 codes: thread (token, quarter of the super-step)
+// reads 32 code bytes (8 groups = 64 K) and their two block scales and decodes them to f16
+// (de-interleaved) into LDS.
 struct PStage {
   u32x4 cw0, cw1;
   uint32_t sc2;
@@ -279,50 +297,65 @@ MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bw) {
   *(u32x4*)(Bw + 112) = decode_x_group(st.cw1.w, s1);
 }
 
+// One K-step (64 K) of the wave's MF x NF fragments. The n-fragments go in blocks of G; a block
+// whose first token lies past the expert's last token (n >= nv, wave uniform) is skipped, so a
+// partial token tile costs about its own size.
+#ifndef MOESQ_TILE_SKIP_G
+#define MOESQ_TILE_SKIP_G 4
+#endif
 template <int S, int MF, int NF, bool XK>
 MOESQ_DEV void lds_step(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const WMeta (&m)[MF], const uint8_t* Bs, int r16,
-                        int c) {
+                        int c, int nv) {
+  constexpr int G = MOESQ_TILE_SKIP_G;
   f16x8 A[MF];
 #pragma unroll
   for (int f = 0; f < MF; f++) A[f] = w_frag(w, m[f], f, S);
   const int g1 = 8 * (c >> 1) + 2 * S + (c & 1);
 #pragma unroll
-  for (int n = 0; n < NF; n++) {
-    const int r = n * 16 + r16;
-    const f16x16 B = concat_x(*(const u32x4*)b_chunk<XK>(Bs, r, g1), *(const u32x4*)b_chunk<XK>(Bs, r, g1 + 16));
+  for (int n0 = 0; n0 < NF; n0 += G) {
+    if (G == NF || n0 < nv) {
 #pragma unroll
-    for (int f = 0; f < MF; f++) acc[f][n] = smfmac_step<S>(A[f], B, acc[f][n], m[f]);
+      for (int n = n0; n < n0 + G; n++) {
+        const int r = n * 16 + r16;
+        const f16x16 B = concat_x(*(const u32x4*)b_chunk<XK>(Bs, r, g1), *(const u32x4*)b_chunk<XK>(Bs, r, g1 + 16));
+#pragma unroll
+        for (int f = 0; f < MF; f++) acc[f][n] = smfmac_step<S>(A[f], B, acc[f][n], m[f]);
+      }
+    }
   }
 }
 
 template <int MF, int NF, bool XK>
-MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const uint8_t* Bs, int r16, int c) {
+MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const uint8_t* Bs, int r16, int c,
+                                 int nv) {
   WMeta m[MF];
 #pragma unroll
   for (int f = 0; f < MF; f++) m[f] = w_meta(w, f);
-  lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c);
-  lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c);
-  lds_step<2, MF, NF, XK>(acc, w, m, Bs, r16, c);
-  lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c);
+  lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+  lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+  lds_step<2, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+  lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
 }
 
-// Per-expert tile counts ceil(n_e / 64) -> exclusive prefix tile_pre[0..E] in LDS (E+1 entries),
-// and the expert offsets copied to off_l[0..E].
+// Per-expert tile counts ceil(n_e / kTileTok) -> exclusive prefix tile_pre[0..E] in LDS (E+1
+// entries), and the expert offsets copied to off_l[0..E]. part: LDS scratch of THREADS ints.
+template <int THREADS>
 MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int32_t* tile_pre, int32_t* off_l,
                                  int32_t* part) {
+  constexpr int PER_LANE = THREADS / 64;
   const int tid = threadIdx.x;
-  for (int i = tid; i <= E; i += 256) off_l[i] = offsets[i];
+  for (int i = tid; i <= E; i += THREADS) off_l[i] = offsets[i];
   __syncthreads();
-  const int per = (E + 255) / 256;
+  const int per = (E + THREADS - 1) / THREADS;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; e++) sum += (off_l[e + 1] - off_l[e] + kPfTokens - 1) / kPfTokens;
+  for (int e = lo; e < hi; e++) sum += (off_l[e + 1] - off_l[e] + kTileTok - 1) / kTileTok;
   part[tid] = sum;
   __syncthreads();
-  if (tid < 64) {  // wave 0 scans the 256 partial sums (4 per lane)
-    int v[4], s = 0;
+  if (tid < 64) {  // wave 0 scans the partial sums (PER_LANE per lane)
+    int v[PER_LANE], s = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) { v[i] = part[4 * tid + i]; s += v[i]; }
+    for (int i = 0; i < PER_LANE; i++) { v[i] = part[PER_LANE * tid + i]; s += v[i]; }
     int incl = s;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -331,33 +364,33 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
     }
     int run = incl - s;
 #pragma unroll
-    for (int i = 0; i < 4; i++) { part[4 * tid + i] = run; run += v[i]; }
+    for (int i = 0; i < PER_LANE; i++) { part[PER_LANE * tid + i] = run; run += v[i]; }
   }
   __syncthreads();
   int run = part[tid];
   for (int e = lo; e < hi; e++) {
     tile_pre[e] = run;
-    run += (off_l[e + 1] - off_l[e] + kPfTokens - 1) / kPfTokens;
+    run += (off_l[e + 1] - off_l[e] + kTileTok - 1) / kTileTok;
   }
   if (hi == E && lo < hi) tile_pre[E] = run;
   __syncthreads();
 }
 
-// One output tile of the persistent schedule and the per-tile operand addressing.
+// One output tile of the persistent schedule and the per-tile operand addressing (all wave uniform).
 template <int MF>
 struct TileCtx {
-  int e, off, ne, tb, rb;
+  int e, off, ne, tb, rb, nv;
   float alpha;
   rsrc_t rw;          // expert's weights (kernel layout)
   uint32_t soff[MF];  // fragment offsets of the wave's m-fragments (super-step 0)
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
 };
 
-// Tile t of the list ordered expert -> token tile -> row block (row block fastest): the 4-wave
-// workgroups of one XCD that run neighbouring tiles share the activation tile in L2.
+// Tile t of the list ordered expert -> token tile -> row block (row block fastest): workgroups of one
+// XCD that run neighbouring tiles share the activation tile in L2.
 template <int MF, bool MLP, bool XK>
 MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, int RB, int t,
-                                int w, int r16) {
+                                int w) {
   TileCtx<MF> c;
   int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] * RB <= t
   while (lo < hi) {
@@ -366,18 +399,19 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   }
   c.e = __builtin_amdgcn_readfirstlane(lo);
   const int local = t - __builtin_amdgcn_readfirstlane(tile_pre[c.e]) * RB;
-  c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kPfTokens);
+  c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kTileTok);
   c.rb = __builtin_amdgcn_readfirstlane(local % RB);
   c.off = __builtin_amdgcn_readfirstlane(off_l[c.e]);
   c.ne = __builtin_amdgcn_readfirstlane(off_l[c.e + 1]) - c.off;
+  c.nv = min(kTileNF, (c.ne - c.tb + 15) / 16);
   const int K = a.K, N = a.N, nss = K / 256;
   const uint32_t ekl = expert_kl_bytes(N, K);
   c.rw = make_rsrc(a.kl + (size_t)c.e * ekl, ekl);
 #pragma unroll
   for (int f = 0; f < MF; f++) {
     int rbf;
-    if (MLP) rbf = ((f < 2 ? 0 : N / 2) + c.rb * 128 + 32 * w + 16 * (f & 1)) / 16;
-    else rbf = min(c.rb * 256 + 64 * w, N - 64) / 16 + f;
+    if (MLP) rbf = ((f < 2 ? 0 : N / 2) + c.rb * 256 + 32 * w + 16 * (f & 1)) / 16;
+    else rbf = min(c.rb * 512 + 64 * w, N - 64) / 16 + f;
     c.soff[f] = __builtin_amdgcn_readfirstlane((uint32_t)rbf * (uint32_t)nss * kFragBytes);
   }
   c.alpha = 1.0f / (a.gscale[c.e] * a.gamma_a[c.e]);
@@ -388,20 +422,34 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
     c.rq = make_rsrc(a.q + (size_t)c.off * (K / 2), (uint32_t)c.ne * (K / 2));
     c.rs = make_rsrc(a.s + (size_t)c.off * (K / 32), (uint32_t)c.ne * (K / 32));
   }
-  (void)r16;
   return c;
+}
+
+// Per-lane parts of the activation addresses. FP4 path: token = lane + 64 (w & 1), quarter w / 2.
+// f16 path: the wave's 8 direct-to-LDS chunk loads j = 0..7 fill chunks q = (8 w + j) * 64 + lane of
+// the swizzled tile, chunk q holding token q / 32, group (q % 32) ^ (token % 32).
+struct BAddr {
+  uint32_t tok, qtr;
+};
+
+MOESQ_DEV BAddr make_baddr(int w, int lane) {
+  BAddr b;
+  b.tok = (uint32_t)(lane + 64 * (w & 1));
+  b.qtr = (uint32_t)(w >> 1);
+  return b;
 }
 
 // Issue the activation operand of super-step ss of tile c: f16 path = 8 direct-to-LDS loads per wave
 // (wave w fills chunks [512 w, 512 w + 512) of the swizzled tile); FP4 path = register loads.
 template <int MF, bool XK>
-MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int w, int lane, int K) {
+MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int w, int lane, const BAddr& ba, int K) {
   if (XK) {
+    const uint32_t ub = (uint32_t)c.tb * (uint32_t)(2 * K) + 512u * ss;
+    const uint32_t h = (uint32_t)lane >> 5, pq = (uint32_t)lane & 31u;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const int q = (8 * w + j) * 64 + lane;
-      const int r = q >> 5, g = (q & 31) ^ (r & 31);
-      const uint32_t vo = (uint32_t)(c.tb + r) * (uint32_t)(2 * K) + 16u * g + 512u * ss;
+      const uint32_t r = 2u * (uint32_t)(8 * w + j) + h;
+      const uint32_t vo = r * (uint32_t)(2 * K) + 16u * (pq ^ (r & 31u)) + ub;
 #if defined(__HIP_DEVICE_COMPILE__)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (__attribute__((address_space(3))) void*)(Bs + (8 * w + j) * 1024),
                                                16, (int)vo, 0, 0, 0);
@@ -410,10 +458,13 @@ MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int
 #endif
     }
   } else {
-    const uint32_t voq = (uint32_t)(c.tb + lane) * (K / 2) + 32u * w;
-    const uint32_t vos = (uint32_t)(c.tb + lane) * (K / 32) + 2u * w;
-    load_p(p, c.rq, c.rs, voq, vos, ss);
+    const uint32_t t = (uint32_t)c.tb + ba.tok;
+    load_p(p, c.rq, c.rs, t * (K / 2) + 32u * ba.qtr, t * (K / 32) + 2u * ba.qtr, ss);
   }
+}
+
+MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) {
+  stage_p(p, Bs + ba.tok * kPfRowBytes + ba.qtr * 128);
 }
 
 // Epilogue of a finished tile.
@@ -422,22 +473,24 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   const int N = a.N;
   const float alpha = c.alpha;
   if (!MLP) {
-    const int n0 = c.rb * 256 + 64 * w;
+    const int n0 = c.rb * 512 + 64 * w;
     if (n0 >= N) return;
 #pragma unroll
     for (int n = 0; n < NF; n++) {
       const int tok = c.tb + n * 16 + r16;
       if (tok >= c.ne) continue;
 #pragma unroll
-      for (int f = 0; f < MF; f++) store4(a.y, (int64_t)(c.off + tok) * N + n0 + 16 * f + 4 * cc, acc[f][n], alpha, a.y_bf16);
+      for (int f = 0; f < MF; f++)
+        store4(a.y, (int64_t)(c.off + tok) * N + n0 + 16 * f + 4 * cc, acc[f][n], alpha, a.y_bf16);
     }
     return;
   }
   const int I = N / 2;
-  const int ib = c.rb * 128 + 32 * w;  // first intermediate column of this wave (one 32-block)
+  const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
   const float gh = a.gamma_h[c.e];
 #pragma unroll
   for (int n = 0; n < NF; n++) {
+    if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
     const bool tv = tok < c.ne;
     float h[8];
@@ -497,31 +550,33 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   }
 }
 
-// Persistent tiled kernel: 256 weight rows (4 waves x 4 m-fragments) x 64 tokens per tile. The grid
-// holds 8*J workgroups; the workgroups of XCD x (blockIdx % 8 == x) take the x-th contiguous eighth
-// of the tile list, slot j handling tiles start + j, + J, ... The super-steps of all the workgroup's
-// tiles form one pipeline: while step i computes, the weights (registers) and activations (LDS) of
-// step i+1 -- possibly the first step of the next tile -- are in flight; one barrier per step.
+// Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the
+// workgroups of XCD x (blockIdx % 8 == x) take the x-th contiguous eighth of the tile list, slot j
+// handling tiles start + j, + J, ... The super-steps of all the workgroup's tiles form one
+// pipeline: while step i computes, the weights (registers) and activations (LDS) of step i+1 --
+// possibly the first step of the next tile -- are in flight; one barrier per step.
 template <bool MLP, bool XK>
-__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
-  constexpr int MF = 4, NF = 4;
+__global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
+  constexpr int MF = 4, NF = kTileNF;
+  constexpr int BBYTES = XK ? kBTileF16 : kBTileFp4;
   extern __shared__ __align__(16) uint8_t dyn[];
-  __shared__ int32_t part[256];
+  __shared__ int32_t part[kTileThreads];
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, cc = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t* Bs0 = dyn;                                    // two activation tiles
-  uint8_t* Bs1 = dyn + kPfTileBytes;
-  int32_t* tile_pre = (int32_t*)(dyn + 2 * kPfTileBytes);  // [E+1]
+  uint8_t* Bs1 = dyn + BBYTES;
+  int32_t* tile_pre = (int32_t*)(dyn + 2 * BBYTES);      // [E+1]
   int32_t* off_l = tile_pre + a.E + 1;                   // [E+1]
-  build_tile_prefix(a.offsets, a.E, tile_pre, off_l, part);
+  build_tile_prefix<kTileThreads>(a.offsets, a.E, tile_pre, off_l, part);
   const int K = a.K, nss = K / 256;
-  const int RB = MLP ? a.N / 256 : (a.N + 255) / 256;   // MLP: 128 gate + 128 up rows per tile
+  const int RB = MLP ? a.N / 512 : (a.N + 511) / 512;   // MLP: 256 gate + 256 up rows per tile
   const int T = tile_pre[a.E] * RB;
   const int J = gridDim.x >> 3, x = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int chunk = (T + 7) / 8;
   const int tend = min(T, (x + 1) * chunk);
   int t = x * chunk + j;
   if (t >= tend) return;
+  const BAddr ba = make_baddr(w, lane);
 
   f32x4 acc[MF][NF];
 #pragma unroll
@@ -529,57 +584,55 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  TileCtx<MF> cur = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t, w, r16);
-  WStage<MF> wa0, wa1;
-  PStage p0, p1;
-  load_w(wa0, cur.rw, cur.soff, lane, 0);
-  issue_b<MF, XK>(cur, 0, Bs0, p0, w, lane, K);
-  if (!XK) stage_p(p0, Bs0 + lane * kPfRowBytes + w * 128);
+  TileCtx<MF> cur = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t, w);
+  WStage<MF> wc, wn;
+  PStage p;
+  load_w(wc, cur.rw, cur.soff, lane, 0);
+  issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
+  if (!XK) stage_b(p, Bs0, ba);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int ss = 0;
-  bool more = true;
-  while (more) {
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-      // coordinates of the next step
-      int ss_n = ss + 1, t_n = t;
-      if (ss_n == nss) {
-        ss_n = 0;
-        t_n = t + J;
-      }
-      const bool has_n = t_n < tend;
-      TileCtx<MF> nxt = cur;
-      if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t_n, w, r16);
-      uint8_t* Bc = half == 0 ? Bs0 : Bs1;
-      uint8_t* Bn = half == 0 ? Bs1 : Bs0;
-      if (has_n) {
-        load_w(half == 0 ? wa1 : wa0, nxt.rw, nxt.soff, lane, ss_n);
-        issue_b<MF, XK>(nxt, ss_n, Bn, half == 0 ? p1 : p0, w, lane, K);
-      }
-      mma_superstep_lds<MF, NF, XK>(acc, half == 0 ? wa0 : wa1, Bc, r16, cc);
-      if (ss == nss - 1) {
-        tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
-#pragma unroll
-        for (int f = 0; f < MF; f++)
-#pragma unroll
-          for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      }
-      if (has_n && !XK) stage_p(half == 0 ? p1 : p0, Bn + lane * kPfRowBytes + w * 128);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (!has_n) {
-        more = false;
-        break;
-      }
-      cur = nxt;
-      t = t_n;
-      ss = ss_n;
+  uint32_t bsel = 0;  // which LDS tile holds the current step
+  while (true) {
+    // coordinates of the next step
+    int ss_n = ss + 1, t_n = t;
+    if (ss_n == nss) {
+      ss_n = 0;
+      t_n = t + J;
     }
+    const bool has_n = t_n < tend;
+    TileCtx<MF> nxt = cur;
+    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t_n, w);
+    uint8_t* Bc = bsel ? Bs1 : Bs0;
+    uint8_t* Bn = bsel ? Bs0 : Bs1;
+    if (has_n) {
+      load_w(wn, nxt.rw, nxt.soff, lane, ss_n);
+      issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
+    }
+    mma_superstep_lds<MF, NF, XK>(acc, wc, Bc, r16, cc, cur.nv);
+    if (ss == nss - 1) {
+      tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
+#pragma unroll
+      for (int f = 0; f < MF; f++)
+#pragma unroll
+        for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    if (has_n && !XK) stage_b(p, Bn, ba);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!has_n) break;
+    wc = wn;
+    cur = nxt;
+    t = t_n;
+    ss = ss_n;
+    bsel ^= 1u;
   }
 }
 
-static size_t prefill_lds_bytes(int E) { return 2 * (size_t)kPfTileBytes + 2 * (size_t)(E + 1) * 4; }
+static size_t tile_lds_bytes(int E, bool xk) {
+  return 2 * (size_t)(xk ? kBTileF16 : kBTileFp4) + 2 * (size_t)(E + 1) * 4;
+}
 
 static int device_cu_count() {
   static int cus[64] = {0};
@@ -619,16 +672,16 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
       default: hipLaunchKernelGGL((gemm_decode_kernel<8, 1>), dim3(a.N / 512, a.E), dim3(256), 0, st, a); break;
     }
   } else {
-    // persistent grid: two 4-wave workgroups per CU, a multiple of the 8 XCDs
-    const int grid = 8 * ((2 * device_cu_count() + 7) / 8);
-    const size_t lds = prefill_lds_bytes(a.E);
+    // persistent grid: one 8-wave workgroup per CU, a multiple of the 8 XCDs
+    const int grid = 8 * ((device_cu_count() + 7) / 8);
     const bool xk = a.xk != nullptr;
+    const size_t lds = tile_lds_bytes(a.E, xk);
     if (a.gamma_h) {
-      if (xk) hipLaunchKernelGGL((gemm_prefill_kernel<true, true>), dim3(grid), dim3(256), lds, st, a);
-      else hipLaunchKernelGGL((gemm_prefill_kernel<true, false>), dim3(grid), dim3(256), lds, st, a);
+      if (xk) hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+      else hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
     } else {
-      if (xk) hipLaunchKernelGGL((gemm_prefill_kernel<false, true>), dim3(grid), dim3(256), lds, st, a);
-      else hipLaunchKernelGGL((gemm_prefill_kernel<false, false>), dim3(grid), dim3(256), lds, st, a);
+      if (xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+      else hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
     }
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;

@@ -9,7 +9,7 @@ namespace moesq {
 
 constexpr int64_t kRouteSingleMax = 8192;  // slots handled by the one-workgroup routing path
 constexpr int32_t kMaxExpertsRoute = 512;
-constexpr int32_t kMaxExpertsGemm = 4096;
+constexpr int32_t kMaxExpertsGemm = 1024;
 
 constexpr int kFragBytes = 1408;  // 16 rows x 256 K of the kernel weight layout
 
@@ -37,8 +37,8 @@ int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32
                  int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status);
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
-                    const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
-                    int32_t E, uint8_t* q, uint8_t* s, void* xk);
+                    const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
+                    uint8_t* q, uint8_t* s, void* xk);
 
 int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
                         float* gamma_out);

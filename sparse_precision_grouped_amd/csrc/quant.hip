@@ -9,89 +9,106 @@
 
 namespace moesq {
 
-// One wave quantizes one 512-element chunk of one permuted row (64 lanes x 8 values); each lane
-// quantizes 8 consecutive values, four lanes per 32-block (block amax by a 4-lane max reduction).
-// The workgroup (4 waves) first copies the expert offsets into LDS so that the expert of a row is
-// found by a binary search in LDS, not by a chain of dependent global loads.
+// Fused dispatch + quantization: one workgroup per token. Its waves take the token's 512-element
+// chunks (wave w: chunks w, w+4, ...), read them once, quantize them (a lane holds 8 consecutive
+// values, four lanes per 32-block, block amax by a 4-lane max reduction) and write the codes to every
+// permuted row the token is routed to. The codes depend on the row's expert only through its tensor
+// scale, so they are recomputed only when that scale changes between consecutive copies.
 constexpr int kQuantMaxE = 4096;
+constexpr int kQuantMaxK = 512;
 
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K,
-                                                       int64_t ld_x, const int32_t* __restrict__ gather, int32_t k,
-                                                       int64_t rows, const float* __restrict__ gamma,
+                                                       int64_t ld_x, const int32_t* __restrict__ slot_pos, int32_t k,
+                                                       const float* __restrict__ gamma,
                                                        const int32_t* __restrict__ offsets, int32_t E,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                        uint8_t* __restrict__ xk) {
   __shared__ int32_t off_l[kQuantMaxE + 1];
-  const int lane = threadIdx.x & 63;
-  const int nchunk = (K + 511) / 512;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t p = wid / nchunk;
-  const int chunk = (int)(wid % nchunk);
+  __shared__ int32_t dst[kQuantMaxK];
+  __shared__ float gam[kQuantMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t = blockIdx.x;
+  const int nk = slot_pos ? k : 1;
   if (offsets) {
-    for (int i = threadIdx.x; i <= E; i += 256) off_l[i] = offsets[i];
+    for (int i = tid; i <= E; i += 256) off_l[i] = offsets[i];
     __syncthreads();
   }
-  if (p >= rows) return;
-  int64_t t = p;
-  if (gather) {
-    if (offsets && p >= off_l[E]) return;  // slot dropped by routing (invalid id)
-    t = gather[p] / k;
-    if (t < 0 || t >= T) return;
-  }
-  float g;
-  if (offsets) {
-    int lo = 0, hi = E - 1;  // largest e with offsets[e] <= p
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off_l[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    g = gamma[lo];
-  } else {
-    g = gamma[0];
-  }
-  const int ch = chunk * 64 + lane;  // 8-value group index within the row
-  const bool valid = ch < K / 8;
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = 0.0f;
-  if (valid) {
-    if (x_bf16) {
-      const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
-      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+  for (int j = tid; j < nk; j += 256) {
+    int32_t p = slot_pos ? slot_pos[t * k + j] : (int32_t)t;
+    float g = gamma[0];
+    if (p >= 0 && offsets) {
+      if (p >= off_l[E]) {
+        p = -1;  // not a routed row
+      } else {
+        int lo = 0, hi = E - 1;  // largest e with offsets[e] <= p
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off_l[mid] <= p) lo = mid; else hi = mid - 1;
+        }
+        g = gamma[lo];
       }
-    } else {
-      const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
-      const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
+    dst[j] = p;
+    gam[j] = g;
   }
-  uint32_t codes, sc;
-  quant8_block4(v, g, codes, sc);
-  if (valid) {
-    *(uint32_t*)(q + p * (K / 2) + 4 * ch) = codes;
-    if ((lane & 3) == 0) s[p * (K / 32) + ch / 4] = (uint8_t)sc;
-    if (xk) {
-      // the same values dequantized (exact in f16), in the GEMM's de-interleaved group order
-      f16x2 sv, unused;
-      e4m3_pair_f16x2(sc, sv, unused);
-      *(u32x4*)(xk + (p * K + 8 * ch) * 2) = decode_x_group(codes, sv);
+  __syncthreads();
+  const int nchunk = (K + 511) / 512;
+  for (int chunk = w; chunk < nchunk; chunk += 4) {
+    const int ch = chunk * 64 + lane;  // 8-value group index within the row
+    const bool valid = ch < K / 8;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    if (valid) {
+      if (x_bf16) {
+        const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
+          v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
+        const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    }
+    bool have = false;
+    float gq = 0.0f;
+    uint32_t codes = 0u, sc = 0u;
+    u32x4 xv = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < nk; j++) {
+      const int32_t p = dst[j];
+      if (p < 0) continue;
+      const float g = gam[j];
+      if (!have || g != gq) {
+        quant8_block4(v, g, codes, sc);
+        if (xk) {
+          // the same values dequantized (exact in f16), in the GEMM's de-interleaved group order
+          f16x2 sv, unused;
+          e4m3_pair_f16x2(sc, sv, unused);
+          xv = decode_x_group(codes, sv);
+        }
+        gq = g;
+        have = true;
+      }
+      if (valid) {
+        *(uint32_t*)(q + (int64_t)p * (K / 2) + 4 * ch) = codes;
+        if ((lane & 3) == 0) s[(int64_t)p * (K / 32) + ch / 4] = (uint8_t)sc;
+        if (xk) *(u32x4*)(xk + ((int64_t)p * K + 8 * ch) * 2) = xv;
+      }
     }
   }
 }
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
-                    const int32_t* gather_slot, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
-                    int32_t E, uint8_t* q, uint8_t* s, void* xk) {
-  if (rows == 0) return MOESQ_OK;
-  const int64_t waves = rows * ((K + 511) / 512);
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x,
-                     gather_slot, k, rows, gamma, offsets, E, q, s, (uint8_t*)xk);
+                    const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
+                    uint8_t* q, uint8_t* s, void* xk) {
+  if (T == 0) return MOESQ_OK;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x, slot_pos, k,
+                     gamma, offsets, E, q, s, (uint8_t*)xk);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

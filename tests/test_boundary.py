@@ -92,7 +92,10 @@ def test_quantize_validation(L):
     assert call(dt=7) == EARG             # dtype
     assert call(ld=32) == EARG            # ld_x < K
     assert call(gamma=0) == EARG
-    assert call(rows=9) == EARG           # no gather: rows must equal T
+    assert call(rows=9) == EARG           # no scatter: rows must equal T
+    assert call(g=FAKE, k=2, rows=15) == EARG    # scatter: rows must hold T*k copies
+    assert call(g=FAKE, k=513, rows=8 * 513) == EUNS
+    assert call(g=FAKE, k=0) == EARG
     assert call(x=FAKE + 4) == EUNS       # misaligned x
 
 

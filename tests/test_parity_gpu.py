@@ -169,7 +169,7 @@ def test_quantize_dispatch_bitexact(name):
     R, k = c["R"], c["k"]
     rt = mq.moesq_route_permute(dev(c["ids"]), c["E"])
     ga = c["ga"] * np.linspace(0.5, 2.0, c["E"]).astype(np.float32)   # distinct per-expert scales
-    q, s = mq.moesq_quantize_act(dev(c["x"]), dev(ga), gather_slot=rt["sorted_slot"], k=k, offsets=rt["offsets"])
+    q, s = mq.moesq_quantize_act(dev(c["x"]), dev(ga), slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"])
     qo, so = orc.dispatch_quantize(c["x"], R["sorted_slot"], k, R["offsets"], ga)
     assert np.array_equal(host(q), qo)
     assert np.array_equal(host(s), so)
@@ -190,7 +190,7 @@ def test_quantize_f16_operand_copy(name):
     say("quantize xk", name)
     R, k = c["R"], c["k"]
     rt = mq.moesq_route_permute(dev(c["ids"]), c["E"])
-    q, s, xk = mq.moesq_quantize_act(dev(c["x"]), dev(c["ga"]), gather_slot=rt["sorted_slot"], k=k,
+    q, s, xk = mq.moesq_quantize_act(dev(c["x"]), dev(c["ga"]), slot_pos=rt["slot_pos"], k=k,
                                      offsets=rt["offsets"], xk=True)
     qo, so = orc.dispatch_quantize(c["x"], R["sorted_slot"], k, R["offsets"], c["ga"])
     assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
@@ -391,7 +391,7 @@ def test_mlp_parity_c4_full_size():
     qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, off, ga)
     say("mlp c4: quantize on the device")
     rt = mq.moesq_route_permute(dev(ids), E)
-    q, s, xk = mq.moesq_quantize_act(dev(x), dev(ga), gather_slot=rt["sorted_slot"], k=k, offsets=rt["offsets"],
+    q, s, xk = mq.moesq_quantize_act(dev(x), dev(ga), slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"],
                                      xk=True)
     assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
     say("mlp c4: expert MLP")
