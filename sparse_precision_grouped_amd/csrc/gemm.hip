@@ -69,6 +69,14 @@ MOESQ_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads and stores issued before it stay in
+// flight (a plain __syncthreads waits for every outstanding memory operation of the wave).
+MOESQ_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // One 256-K super-step of MF A fragments (16 rows each) for one lane.
 template <int MF>
 struct WStage {
@@ -170,23 +178,24 @@ MOESQ_DEV void mma_superstep_x(f32x4 (&acc)[MF], const WStage<MF>& w, const XSta
 MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
 
 // ============================================================================ decode kernel =====
-// Weight streaming for few tokens per expert. Workgroup = 4 waves; a wave owns 16*MF weight rows.
-// KSPLIT = 4: the 4 waves share the same rows and take super-steps ss = w, w+4, ...; their partial
-// sums are added in wave order through LDS (deterministic). KSPLIT = 1: the 4 waves own 4 row
-// blocks and each streams the whole K. Both keep two super-steps of operands in flight per wave
-// (register double buffering). Experts with more than 16 tokens loop over 16-token blocks.
-// grid (N / (16*MF*(4/KSPLIT)), E).
-template <int MF, int KSPLIT>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
-  __shared__ f32x4 red[KSPLIT][MF][64];
+// Weight streaming for few tokens per expert. A workgroup of KS * RG waves covers 16*MF*RG weight rows
+// of one expert: RG row groups of 16*MF rows, each split over KS waves along K (wave kw takes
+// super-steps kw, kw + KS, ...). The KS partial sums of a row group are added in wave order through
+// LDS (deterministic). Each wave keeps two super-steps of operands in flight (register double
+// buffering). Experts with more than 16 tokens loop over 16-token blocks.
+// grid (N / (16*MF*RG), E).
+template <int MF, int KS, int RG>
+__global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
+  __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
   const int off = a.offsets[e];
   const int ne = a.offsets[e + 1] - off;
   if (ne <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = w % KS, rg = w / KS;
   const int K = a.K, N = a.N, nss = K / 256;
-  const int rb0 = blockIdx.x * (MF * (4 / KSPLIT)) + (KSPLIT == 1 ? w * MF : 0);
+  const int rb0 = (blockIdx.x * RG + rg) * MF;
   const uint32_t ekl = expert_kl_bytes(N, K);
   const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
   uint32_t soff[MF];
@@ -196,7 +205,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
   const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
   const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
   const int n0 = rb0 * 16;
-  const int ss0 = KSPLIT == 1 ? 0 : w;
   for (int tb = 0; tb < ne; tb += 16) {
     f32x4 acc[MF];
 #pragma unroll
@@ -208,13 +216,13 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
     const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
     WStage<MF> w0, w1;
     XStage x0, x1;
-    int ss = ss0;
+    int ss = kw;
     if (ss < nss) {
       load_w(w0, rw, soff, lane, ss);
       load_x(x0, rq, rs, voq, vos, ss);
     }
     while (ss < nss) {
-      const int s1 = ss + KSPLIT, s2 = ss + 2 * KSPLIT;
+      const int s1 = ss + KS, s2 = ss + 2 * KS;
       if (s1 < nss) {
         load_w(w1, rw, soff, lane, s1);
         load_x(x1, rq, rs, voq, vos, s1);
@@ -227,19 +235,19 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs a) {
       if (s1 < nss) mma_superstep_x(acc, w1, x1);
       ss = s2;
     }
-    if (KSPLIT == 1) {
+    if (KS == 1) {
       if (tv) {
 #pragma unroll
         for (int f = 0; f < MF; f++) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, acc[f], alpha, a.y_bf16);
       }
     } else {
 #pragma unroll
-      for (int f = 0; f < MF; f++) red[w][f][lane] = acc[f];
+      for (int f = 0; f < MF; f++) red[rg * KS + kw][f][lane] = acc[f];
       __syncthreads();
-      for (int f = w; f < MF; f += 4) {
-        f32x4 sum = red[0][f][lane];
+      for (int f = kw; f < MF; f += KS) {
+        f32x4 sum = red[rg * KS][f][lane];
 #pragma unroll
-        for (int v = 1; v < KSPLIT; v++) sum = sum + red[v][f][lane];
+        for (int v = 1; v < KS; v++) sum = sum + red[rg * KS + v][f][lane];
         if (tv) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
       }
       __syncthreads();
@@ -619,8 +627,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
         for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     if (has_n && !XK) stage_b(p, Bn, ba);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (XK) {
+      __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next step
+      __syncthreads();
+    } else {
+      lds_barrier();  // epilogue stores may still be in flight
+    }
     if (!has_n) break;
     wc = wn;
     cur = nxt;
@@ -646,31 +658,41 @@ static int device_cu_count() {
   return cus[dev];
 }
 
-// Decode variants: MF (rows per wave / 16) and KSPLIT. The default is picked by measurement; the
-// environment variable MOESQ_DECODE_VARIANT (0..3) overrides it for tuning.
+// Decode variants (MF, KS, RG); the default is picked by measurement, the environment variable
+// MOESQ_DECODE_VARIANT overrides it for tuning.
 static int decode_variant_default() {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("MOESQ_DECODE_VARIANT");
     v = e ? atoi(e) : 0;
-    if (v < 0 || v > 3) v = 0;
+    if (v < 0 || v > 7) v = 0;
   }
   return v;
+}
+
+template <int MF, int KS, int RG>
+static bool launch_decode(hipStream_t st, const GemmArgs& a) {
+  constexpr int rows = 16 * MF * RG;
+  if (a.N % rows != 0) return false;
+  hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
+  return true;
 }
 
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
   if (rows == 0) return MOESQ_OK;
   if (variant == 0) {
-    int v = decode_variant_default();
-    // KSPLIT = 1 needs N to be a multiple of the 4-wave row block
-    if ((v == 2 && a.N % 256 != 0) || (v == 3 && a.N % 512 != 0)) v = 0;
-    if (v == 1 && a.N % 128 != 0) v = 0;
-    switch (v) {
-      case 0: hipLaunchKernelGGL((gemm_decode_kernel<4, 4>), dim3(a.N / 64, a.E), dim3(256), 0, st, a); break;
-      case 1: hipLaunchKernelGGL((gemm_decode_kernel<8, 4>), dim3(a.N / 128, a.E), dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((gemm_decode_kernel<4, 1>), dim3(a.N / 256, a.E), dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((gemm_decode_kernel<8, 1>), dim3(a.N / 512, a.E), dim3(256), 0, st, a); break;
+    bool ok = false;
+    switch (decode_variant_default()) {
+      case 1: ok = launch_decode<8, 4, 1>(st, a); break;
+      case 2: ok = launch_decode<4, 1, 4>(st, a); break;
+      case 3: ok = launch_decode<4, 8, 1>(st, a); break;
+      case 4: ok = launch_decode<2, 8, 1>(st, a); break;
+      case 5: ok = launch_decode<2, 4, 1>(st, a); break;
+      case 6: ok = launch_decode<4, 2, 2>(st, a); break;
+      case 7: ok = launch_decode<2, 4, 2>(st, a); break;
+      default: break;
     }
+    if (!ok) launch_decode<4, 4, 1>(st, a);  // N % 64 == 0 always holds
   } else {
     // persistent grid: one 8-wave workgroup per CU, a multiple of the 8 XCDs
     const int grid = 8 * ((device_cu_count() + 7) / 8);

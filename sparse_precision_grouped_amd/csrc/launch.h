@@ -7,7 +7,7 @@
 
 namespace moesq {
 
-constexpr int64_t kRouteSingleMax = 8192;  // slots handled by the one-workgroup routing path
+constexpr int64_t kRouteSingleMax = 2048;  // slots handled by the one-workgroup routing path
 constexpr int32_t kMaxExpertsRoute = 512;
 constexpr int32_t kMaxExpertsGemm = 1024;
 

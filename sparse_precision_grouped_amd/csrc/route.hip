@@ -10,28 +10,25 @@
 
 namespace moesq {
 
-constexpr int kRouteThreads = 1024;  // multi-block path: 16 waves
-constexpr int kRouteChunk = 4096;    // slots per block in the multi-block path
+constexpr int kRouteThreads = 256;   // multi-block path: 4 waves per block
+constexpr int kRouteChunk = 1024;    // slots per block in the multi-block path
 constexpr int kSmallThreads = 256;   // single-workgroup path: 4 waves
 
 // Rank of this lane among the lanes of its wave holding the same key (lower lanes first), and the
-// number of such lanes. Lanes with valid == false take no part. The loop runs once per distinct key.
-MOESQ_DEV void wave_match_rank(int key, bool valid, int& rank, int& count) {
+// number of such lanes. Lanes with valid == false take no part. The set of lanes with the same key is
+// the AND over the key's bits of the ballot of lanes that agree on that bit (keys < 2^bits).
+MOESQ_DEV void wave_match_rank(int key, bool valid, int bits, int& rank, int& count) {
   const int lane = threadIdx.x & 63;
-  uint64_t todo = __ballot(valid);
-  rank = 0;
-  count = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int lk = __shfl(key, leader);
-    const uint64_t same = __ballot(valid && key == lk) & todo;
-    if (valid && key == lk) {
-      rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
-      count = __builtin_popcountll(same);
-    }
-    todo &= ~same;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < bits; b++) {
+    const uint64_t ones = __ballot(valid && ((key >> b) & 1));
+    same &= ((key >> b) & 1) ? ones : ~ones;
   }
+  rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+  count = __builtin_popcountll(same);
 }
+
+MOESQ_DEV int key_bits(int E) { return 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1)); }
 
 // Scatter one round of up to THREADS consecutive slots starting at `base_slot`, given the running
 // per-expert positions pos_base[e] (LDS). Waves are ordered: wave w's slots come after waves
@@ -53,7 +50,7 @@ MOESQ_DEV void scatter_round(const int32_t* __restrict__ ids, int64_t n, int64_t
   for (int i = tid; i < WAVES * E; i += THREADS) wave_tab[i] = 0;
   __syncthreads();
   int rank, count;
-  wave_match_rank(e, valid, rank, count);
+  wave_match_rank(e, valid, key_bits(E), rank, count);
   if (valid && rank == count - 1) wave_tab[w * E + e] = count;  // one writer per (wave, expert)
   __syncthreads();
   // exclusive prefix over waves per expert, then advance pos_base
@@ -142,9 +139,10 @@ __global__ __launch_bounds__(kSmallThreads) void route_single_kernel(const int32
   }
 }
 
-// Multi-block path, step 1: per-chunk histograms hist[chunk][E].
+// Multi-block path, step 1: per-chunk histograms, stored expert-major: hist[e][chunk].
 __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                                   int32_t E, int32_t* __restrict__ hist_g) {
+                                                                   int32_t E, int32_t nchunks,
+                                                                   int32_t* __restrict__ hist_g) {
   extern __shared__ int32_t lds[];
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kRouteThreads) lds[i] = 0;
@@ -156,48 +154,63 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(const int32_t
     if (e >= 0 && e < E) atomicAdd(&lds[e], 1);
   }
   __syncthreads();
-  for (int i = tid; i < E; i += kRouteThreads) hist_g[(int64_t)blockIdx.x * E + i] = lds[i];
+  for (int i = tid; i < E; i += kRouteThreads) hist_g[(int64_t)i * nchunks + blockIdx.x] = lds[i];
 }
 
-// Step 2 (one block): counts, offsets, and per-chunk starting positions base[chunk][E] (in place).
-__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int32_t* __restrict__ hist_g, int32_t nchunks,
-                                                                   int32_t E, int32_t* __restrict__ counts,
-                                                                   int32_t* __restrict__ offsets) {
-  extern __shared__ int32_t lds[];
-  int32_t* tot = lds;          // [E]
-  int32_t* pos = tot + E;      // [E+1]
-  __shared__ int32_t wsum[kRouteThreads / 64];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int run = 0;
-    for (int c = 0; c < nchunks; c++) {
-      const int v = hist_g[(int64_t)c * E + e];
-      hist_g[(int64_t)c * E + e] = run;
-      run += v;
-    }
-    tot[e] = run;
+// Step 2 (one wave per expert): exclusive prefix of the expert's chunk counts in place,
+// hist[e][c] = sum of hist[e][c'] for c' < c, and its total -> tot[e], counts[e]. Lane l holds a
+// contiguous run of chunks.
+__global__ __launch_bounds__(kRouteThreads) void route_chunk_scan_kernel(int32_t* __restrict__ hist_g, int32_t nchunks,
+                                                                        int32_t E, int32_t* __restrict__ tot,
+                                                                        int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  if (e >= E) return;
+  int32_t* h = hist_g + (int64_t)e * nchunks;
+  const int per = (nchunks + 63) / 64;
+  const int c0 = min(nchunks, lane * per), c1 = min(nchunks, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; c++) sum += h[c];
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
   }
-  __syncthreads();
-  block_exclusive_scan<kRouteThreads>(tot, E, pos, wsum);
-  for (int e = tid; e <= E; e += kRouteThreads) {
-    offsets[e] = pos[e];
-    if (e < E) counts[e] = tot[e];
+  int run = incl - sum;
+  for (int c = c0; c < c1; c++) {
+    const int v = h[c];
+    h[c] = run;
+    run += v;
   }
-  for (int e = tid; e < E; e += kRouteThreads)
-    for (int c = 0; c < nchunks; c++) hist_g[(int64_t)c * E + e] += pos[e];
+  if (lane == 63) {
+    tot[e] = incl;
+    counts[e] = incl;
+  }
 }
 
-// Step 3: stable scatter of each chunk from its base positions.
+// Step 3: stable scatter of each chunk. Every block scans the expert totals itself (offsets; block 0
+// also stores them), adds the chunk's prefix, then scatters its slots.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                                      int32_t E, const int32_t* __restrict__ base_g,
+                                                                      int32_t E, int32_t nchunks,
+                                                                      const int32_t* __restrict__ base_g,
+                                                                      const int32_t* __restrict__ tot_g,
+                                                                      int32_t* __restrict__ offsets,
                                                                       int32_t* __restrict__ sorted_slot,
                                                                       int32_t* __restrict__ slot_pos,
                                                                       int32_t* dev_status) {
   extern __shared__ int32_t lds[];
-  int32_t* pos = lds;                // [E]
-  int32_t* wave_tab = pos + E;       // [16 * E]
+  int32_t* tot = lds;                // [E]
+  int32_t* pos = tot + E;            // [E+1]
+  int32_t* wave_tab = pos + E + 1;   // [4 * E]
+  __shared__ int32_t wsum[kRouteThreads / 64];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kRouteThreads) pos[e] = base_g[(int64_t)blockIdx.x * E + e];
+  for (int e = tid; e < E; e += kRouteThreads) tot[e] = tot_g[e];
+  __syncthreads();
+  block_exclusive_scan<kRouteThreads>(tot, E, pos, wsum);
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = pos[e];
+  for (int e = tid; e < E; e += kRouteThreads) pos[e] += base_g[(int64_t)e * nchunks + blockIdx.x];
   __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * kRouteChunk;
   const int64_t hi = min(n, lo + kRouteChunk);
@@ -212,7 +225,7 @@ static size_t route_single_lds(int32_t E) { return sizeof(int32_t) * ((size_t)E 
 size_t route_workspace_bytes(int64_t n, int32_t E) {
   if (n <= kRouteSingleMax) return 0;
   const int64_t chunks = (n + kRouteChunk - 1) / kRouteChunk;
-  return sizeof(int32_t) * (size_t)chunks * (size_t)E;
+  return sizeof(int32_t) * ((size_t)chunks * (size_t)E + (size_t)E);
 }
 
 int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t* counts, int32_t* offsets,
@@ -223,13 +236,15 @@ int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32
     return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
   }
   const int32_t chunks = (int32_t)((n + kRouteChunk - 1) / kRouteChunk);
-  int32_t* hist = (int32_t*)ws;
-  hipLaunchKernelGGL(route_hist_kernel, dim3(chunks), dim3(kRouteThreads), sizeof(int32_t) * E, st, ids, n, E, hist);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), sizeof(int32_t) * ((size_t)E + E + 1), st,
-                     hist, chunks, E, counts, offsets);
+  int32_t* hist = (int32_t*)ws;                     // [E][chunks]
+  int32_t* tot = hist + (size_t)chunks * E;         // [E]
+  hipLaunchKernelGGL(route_hist_kernel, dim3(chunks), dim3(kRouteThreads), sizeof(int32_t) * E, st, ids, n, E, chunks,
+                     hist);
+  hipLaunchKernelGGL(route_chunk_scan_kernel, dim3((E + 3) / 4), dim3(kRouteThreads), 0, st, hist, chunks, E, tot,
+                     counts);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(chunks), dim3(kRouteThreads),
-                     sizeof(int32_t) * ((size_t)E + 16 * (size_t)E), st, ids, n, E, hist, sorted_slot, slot_pos,
-                     dev_status);
+                     sizeof(int32_t) * ((size_t)E + (E + 1) + 4 * (size_t)E), st, ids, n, E, chunks, hist, tot, offsets,
+                     sorted_slot, slot_pos, dev_status);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 
