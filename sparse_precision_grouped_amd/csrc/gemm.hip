@@ -483,13 +483,45 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   if (!MLP) {
     const int n0 = c.rb * 512 + 64 * w;
     if (n0 >= N) return;
+    // Lane (r16, cc) holds columns 16 f + 4 cc .. + 3 of token r16 for every fragment f. A permlane16
+    // swap between lane rows cc = 2i and 2i + 1 gives each lane 8 consecutive columns of one fragment
+    // (even cc: fragment f, columns 16 f + 4 cc ..; odd cc: fragment f + 1, columns 16 (f+1) + 4 (cc-1)
+    // ..), so every store writes 16 (bf16) or 32 (fp32) contiguous bytes.
+    const int odd = cc & 1;
 #pragma unroll
     for (int n = 0; n < NF; n++) {
       const int tok = c.tb + n * 16 + r16;
-      if (tok >= c.ne) continue;
+      const bool tv = tok < c.ne;
+      const int64_t rowo = (int64_t)(c.off + tok) * N + n0;
 #pragma unroll
-      for (int f = 0; f < MF; f++)
-        store4(a.y, (int64_t)(c.off + tok) * N + n0 + 16 * f + 4 * cc, acc[f][n], alpha, a.y_bf16);
+      for (int f = 0; f < MF; f += 2) {
+        const int col = odd ? 16 * (f + 1) + 4 * (cc - 1) : 16 * f + 4 * cc;
+        if (a.y_bf16) {
+          const bf16x2 x0 = __builtin_convertvector((f32x2){acc[f][n].x * alpha, acc[f][n].y * alpha}, bf16x2);
+          const bf16x2 x1 = __builtin_convertvector((f32x2){acc[f][n].z * alpha, acc[f][n].w * alpha}, bf16x2);
+          const bf16x2 y0 = __builtin_convertvector((f32x2){acc[f + 1][n].x * alpha, acc[f + 1][n].y * alpha}, bf16x2);
+          const bf16x2 y1 = __builtin_convertvector((f32x2){acc[f + 1][n].z * alpha, acc[f + 1][n].w * alpha}, bf16x2);
+          const auto s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, y0),
+                                                           false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x1), __builtin_bit_cast(uint32_t, y1),
+                                                           false, false);
+          if (tv) *(u32x4*)((uint16_t*)a.y + rowo + col) = (u32x4){s0[0], s1[0], s0[1], s1[1]};
+        } else {
+          uint32_t xv[4], yv[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[f][n][i] * alpha),
+                                                             __float_as_uint(acc[f + 1][n][i] * alpha), false, false);
+            xv[i] = sw[0];
+            yv[i] = sw[1];
+          }
+          if (tv) {
+            u32x4* dst = (u32x4*)((float*)a.y + rowo + col);
+            dst[0] = (u32x4){xv[0], xv[1], xv[2], xv[3]};
+            dst[1] = (u32x4){yv[0], yv[1], yv[2], yv[3]};
+          }
+        }
+      }
     }
     return;
   }
