@@ -265,18 +265,13 @@ constexpr int kTileTok = 128;                          // T_N
 constexpr int kTileNF = kTileTok / 16;                 // n-fragments per wave
 constexpr int kTileThreads = 512;                      // 8 waves
 constexpr int kPfGroups = 32;                          // 8-element groups per 256-K super-step
-constexpr int kPfRowBytes = kPfGroups * 16 + 16;       // FP4 path: decoded groups of one token (+ pad)
-constexpr int kBTileFp4 = kTileTok * kPfRowBytes;      // 67584 B
-constexpr int kBTileF16 = kTileTok * kPfGroups * 16;   // 65536 B
+constexpr int kBTileBytes = kTileTok * kPfGroups * 16;  // 65536 B: one super-step of f16 activations
 
-// Activation tile (B) in LDS. FP4-staging path: token row r, group g at r * kPfRowBytes + 16 g.
-// f16 path (direct-to-LDS loads): chunk (r, g) at 16 * (32 r + (g ^ (r & 31))), an XOR swizzle that
-// keeps the 16 rows read by one B fragment on distinct banks.
-template <bool XK>
-MOESQ_DEV const uint8_t* b_chunk(const uint8_t* Bs, int r, int g) {
-  if (XK) return Bs + 16 * (32 * r + (g ^ (r & 31)));
-  return Bs + r * kPfRowBytes + 16 * g;
-}
+// Activation tile (B) in LDS, both paths: 16-byte chunk (token r, 8-group g of the super-step) at
+// 16 * (32 r + (g ^ (r & 31))). The XOR swizzle keeps the 16 rows read by one B fragment, and the 16
+// tokens written by one staging store, on distinct banks.
+MOESQ_DEV uint8_t* b_chunk(uint8_t* Bs, int r, int g) { return Bs + 16 * (32 * r + (g ^ (r & 31))); }
+MOESQ_DEV const uint8_t* b_chunk(const uint8_t* Bs, int r, int g) { return Bs + 16 * (32 * r + (g ^ (r & 31))); }
 
 // Activation staging of one super-step from NVFP4 codes: thread (token, quarter of the super-step)
 // reads 32 code bytes (8 groups = 64 K) and their two block scales and decodes them to f16
@@ -292,17 +287,13 @@ MOESQ_DEV void load_p(PStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t v
   st.sc2 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
 }
 
-MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bw) {
+// Decode the staged codes of token `tok`, groups 8 qtr .. 8 qtr + 7, into the swizzled tile.
+MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bs, int tok, int qtr) {
   f16x2 s0, s1;
   e4m3_pair_f16x2(st.sc2, s0, s1);
-  *(u32x4*)(Bw + 0) = decode_x_group(st.cw0.x, s0);
-  *(u32x4*)(Bw + 16) = decode_x_group(st.cw0.y, s0);
-  *(u32x4*)(Bw + 32) = decode_x_group(st.cw0.z, s0);
-  *(u32x4*)(Bw + 48) = decode_x_group(st.cw0.w, s0);
-  *(u32x4*)(Bw + 64) = decode_x_group(st.cw1.x, s1);
-  *(u32x4*)(Bw + 80) = decode_x_group(st.cw1.y, s1);
-  *(u32x4*)(Bw + 96) = decode_x_group(st.cw1.z, s1);
-  *(u32x4*)(Bw + 112) = decode_x_group(st.cw1.w, s1);
+  const uint32_t cw[8] = {st.cw0.x, st.cw0.y, st.cw0.z, st.cw0.w, st.cw1.x, st.cw1.y, st.cw1.z, st.cw1.w};
+#pragma unroll
+  for (int i = 0; i < 8; i++) *(u32x4*)b_chunk(Bs, tok, 8 * qtr + i) = decode_x_group(cw[i], i < 4 ? s0 : s1);
 }
 
 // One K-step (64 K) of the wave's MF x NF fragments. The n-fragments go in blocks of G; a block
@@ -325,7 +316,7 @@ MOESQ_DEV void lds_step(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const WMeta (
 #pragma unroll
       for (int n = n0; n < n0 + G; n++) {
         const int r = n * 16 + r16;
-        const f16x16 B = concat_x(*(const u32x4*)b_chunk<XK>(Bs, r, g1), *(const u32x4*)b_chunk<XK>(Bs, r, g1 + 16));
+        const f16x16 B = concat_x(*(const u32x4*)b_chunk(Bs, r, g1), *(const u32x4*)b_chunk(Bs, r, g1 + 16));
 #pragma unroll
         for (int f = 0; f < MF; f++) acc[f][n] = smfmac_step<S>(A[f], B, acc[f][n], m[f]);
       }
@@ -471,9 +462,7 @@ MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int
   }
 }
 
-MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) {
-  stage_p(p, Bs + ba.tok * kPfRowBytes + ba.qtr * 128);
-}
+MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) { stage_p(p, Bs, (int)ba.tok, (int)ba.qtr); }
 
 // Epilogue of a finished tile.
 template <int MF, int NF, bool MLP>
@@ -598,7 +587,7 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
 template <bool MLP, bool XK>
 __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = kTileNF;
-  constexpr int BBYTES = XK ? kBTileF16 : kBTileFp4;
+  constexpr int BBYTES = kBTileBytes;
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int32_t part[kTileThreads];
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, cc = lane >> 4;
@@ -674,9 +663,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   }
 }
 
-static size_t tile_lds_bytes(int E, bool xk) {
-  return 2 * (size_t)(xk ? kBTileF16 : kBTileFp4) + 2 * (size_t)(E + 1) * 4;
-}
+static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + 2 * (size_t)(E + 1) * 4; }
 
 static int device_cu_count() {
   static int cus[64] = {0};
@@ -729,7 +716,7 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
     // persistent grid: one 8-wave workgroup per CU, a multiple of the 8 XCDs
     const int grid = 8 * ((device_cu_count() + 7) / 8);
     const bool xk = a.xk != nullptr;
-    const size_t lds = tile_lds_bytes(a.E, xk);
+    const size_t lds = tile_lds_bytes(a.E);
     if (a.gamma_h) {
       if (xk) hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
       else hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
