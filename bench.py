@@ -114,9 +114,9 @@ def summarize_pmc(argv):
             per_kernel.setdefault(k, {})["write_bytes"] = v * 1024.0 * f_write
     if wl == "c4":
         key = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
-        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if "prefill" in k)
+        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if "gemm_tile_kernel" in k)
     else:
-        key = "gemm_decode_kernel" if any("decode" in k for k in per_kernel) else "gemm_prefill_kernel"
+        key = "gemm_decode_kernel" if any("decode" in k for k in per_kernel) else "gemm_tile_kernel"
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     t = json.load(open(path)) if os.path.exists(path) else {}
@@ -284,7 +284,7 @@ class Workload:
                          for sl in self.slots])
             return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, "gemm_decode_kernel"
         kept = 0.5 * self.eff_flops_per_step() if self.kind == "mlp" else cfg.N * cfg.K * self.rows
-        kern = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)" if self.kind == "mlp" else "gemm_prefill_kernel"
+        kern = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)" if self.kind == "mlp" else "gemm_tile_kernel"
         return "mfma", kept / 1e12, "TFLOP/s", F16_PEAK_TFLOPS, kern
 
 
