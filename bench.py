@@ -179,7 +179,7 @@ class Workload:
             # optional: the quantizer also writes the f16 operand copy that the tiled kernel can stage
             # straight into LDS (more HBM traffic, fewer instructions in the GEMM)
             sl["xk"] = (torch.empty((self.rows, cfg.K), dtype=torch.float16, device=dev)
-                        if self.tiled and f16_operand else None)
+                        if f16_operand else None)
             if self.kind == "single":
                 sl["y"] = torch.empty((self.rows, cfg.N), dtype=torch.bfloat16, device=dev)
             elif self.kind == "pair":
@@ -190,6 +190,8 @@ class Workload:
                 sl["q2"] = torch.empty((self.rows, cfg.K2 // 2), dtype=torch.uint8, device=dev)
                 sl["s2"] = torch.empty((self.rows, cfg.K2 // 32), dtype=torch.uint8, device=dev)
                 sl["y2"] = torch.empty((self.rows, cfg.N2), dtype=torch.bfloat16, device=dev)
+                sl["xk2"] = (torch.empty((self.rows, cfg.K2), dtype=torch.float16, device=dev)
+                             if f16_operand else None)
             else:
                 I = cfg.N // 2
                 sl["gh"] = torch.full((E,), cfg.gamma_h, dtype=torch.float32, device=dev)
@@ -231,10 +233,11 @@ class Workload:
         if self.kind == "single":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
         elif self.kind == "pair":
-            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"])
+            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
             mq.moesq_quantize_act(sl["x2"], sl["ga2"], slot_pos=rt["slot_pos"], k=cfg.k, offsets=rt["offsets"],
-                                  q=sl["q2"], s=sl["s2"])
-            mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"])
+                                  q=sl["q2"], s=sl["s2"], xk=sl["xk2"])
+            mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"],
+                                  xk=sl["xk2"])
         else:
             mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
                                 y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
@@ -330,8 +333,9 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--f16-operand", action="store_true",
-                    help="tiled workloads: quantizer writes the f16 activation copy and the GEMM reads it")
+    ap.add_argument("--operand", choices=["auto", "nvfp4", "f16"], default="auto",
+                    help="activation operand of the GEMMs: NVFP4 codes decoded in the kernel, or the quantizer's "
+                         "f16 copy; auto = f16 for weight-streaming (decode) workloads, NVFP4 for tiled ones")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (traffic-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -356,7 +360,10 @@ def main(argv=None):
     import sparse_precision_grouped_amd as mq
 
     torch.cuda.set_device(0)
-    wl = Workload(args.workload, args.rotate, torch, gen, mq, args.f16_operand)
+    cfgw = gen.CONFIGS[args.workload]
+    decode_shaped = not cfgw.mlp and cfgw.T * cfgw.k <= 16 * cfgw.E
+    f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped)
+    wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand)
     wl.capture()
     for i in range(args.warmup):
         wl.graphs[i % wl.R].replay()
@@ -399,6 +406,7 @@ def main(argv=None):
             args.workload, cfg.desc, cfg.E, cfg.K, cfg.N, cfg.T, cfg.k, cfg.routing,
             ", then K=%d N=%d" % (cfg.K2, cfg.N2) if cfg.N2 else ""),
             "rows": wl.rows, "weight_copies": wl.R, "graph_replay": True,
+            "activation_operand": "f16 copy" if f16_operand else "nvfp4",
             "step_gbps_algorithmic": round(
                 (gemm_bytes(np.mean([(sl["counts_host"] > 0).sum() for sl in wl.slots]), cfg.N, cfg.K, wl.rows,
                             cfg.E) / t / 1e9) if wl.kind == "single" else 0.0, 1)},

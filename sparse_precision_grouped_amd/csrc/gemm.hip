@@ -175,6 +175,57 @@ MOESQ_DEV void mma_superstep_x(f32x4 (&acc)[MF], const WStage<MF>& w, const XSta
   x_step<3>(acc, w, m, x, a01, a23, b01, b23);
 }
 
+// f16 operand copy (xk) for the decode kernel: the lane's two 8-groups of step s are the 16-byte chunks
+// g and g + 16 of the super-step with g = 8 (c >> 1) + (c & 1) + 2 s (the same K mapping as the NVFP4
+// path), so a step is two 16-byte loads and no decoding.
+struct XKStage {
+  u32x4 lo[4], hi[4];
+};
+
+MOESQ_DEV void load_xk(XKStage& st, rsrc_t rx, uint32_t vox, int ss) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    st.lo[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(vox + 512u * ss + 32u * s), 0, 0));
+    st.hi[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(vox + 512u * ss + 32u * s + 256u), 0, 0));
+  }
+}
+
+template <int S, int MF>
+MOESQ_DEV void xk_step(f32x4 (&acc)[MF], const WStage<MF>& w, const WMeta (&m)[MF], const XKStage& x) {
+  const f16x16 B = concat_x(x.lo[S], x.hi[S]);
+#pragma unroll
+  for (int f = 0; f < MF; f++) acc[f] = smfmac_step<S>(w_frag(w, m[f], f, S), B, acc[f], m[f]);
+}
+
+template <int MF>
+MOESQ_DEV void mma_superstep_xk(f32x4 (&acc)[MF], const WStage<MF>& w, const XKStage& x) {
+  WMeta m[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) m[f] = w_meta(w, f);
+  xk_step<0>(acc, w, m, x);
+  xk_step<1>(acc, w, m, x);
+  xk_step<2>(acc, w, m, x);
+  xk_step<3>(acc, w, m, x);
+}
+
+// The activation stage of the decode kernel: NVFP4 codes (decoded in registers) or the f16 copy.
+template <bool XK>
+struct DStage;
+template <>
+struct DStage<false> {
+  XStage x;
+  MOESQ_DEV void load(rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, uint32_t, int ss) { load_x(x, rq, rs, voq, vos, ss); }
+  template <int MF>
+  MOESQ_DEV void mma(f32x4 (&acc)[MF], const WStage<MF>& w) const { mma_superstep_x(acc, w, x); }
+};
+template <>
+struct DStage<true> {
+  XKStage x;
+  MOESQ_DEV void load(rsrc_t rq, rsrc_t, uint32_t, uint32_t, uint32_t vox, int ss) { load_xk(x, rq, vox, ss); }
+  template <int MF>
+  MOESQ_DEV void mma(f32x4 (&acc)[MF], const WStage<MF>& w) const { mma_superstep_xk(acc, w, x); }
+};
+
 MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
 
 // ============================================================================ decode kernel =====
@@ -184,7 +235,7 @@ MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (
 // LDS (deterministic). Each wave keeps two super-steps of operands in flight (register double
 // buffering). Experts with more than 16 tokens loop over 16-token blocks.
 // grid (N / (16*MF*RG), E).
-template <int MF, int KS, int RG>
+template <int MF, int KS, int RG, bool XK>
 __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
@@ -201,7 +252,8 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
   uint32_t soff[MF];
 #pragma unroll
   for (int f = 0; f < MF; f++) soff[f] = (uint32_t)(rb0 + f) * (uint32_t)nss * kFragBytes;
-  const rsrc_t rq = make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
+  const rsrc_t rq = XK ? make_rsrc((const uint8_t*)a.xk + (size_t)off * K * 2, (uint32_t)ne * K * 2)
+                      : make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
   const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
   const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
   const int n0 = rb0 * 16;
@@ -214,25 +266,26 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
     // byte offsets of the lane's first activation group (step 0) and its block scales
     const uint32_t voq = (uint32_t)tok * (K / 2) + 32u * (c >> 1) + 4u * (c & 1);
     const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
+    const uint32_t vox = (uint32_t)tok * (uint32_t)(2 * K) + 16u * (8u * (c >> 1) + (c & 1));
     WStage<MF> w0, w1;
-    XStage x0, x1;
+    DStage<XK> x0, x1;
     int ss = kw;
     if (ss < nss) {
       load_w(w0, rw, soff, lane, ss);
-      load_x(x0, rq, rs, voq, vos, ss);
+      x0.load(rq, rs, voq, vos, vox, ss);
     }
     while (ss < nss) {
       const int s1 = ss + KS, s2 = ss + 2 * KS;
       if (s1 < nss) {
         load_w(w1, rw, soff, lane, s1);
-        load_x(x1, rq, rs, voq, vos, s1);
+        x1.load(rq, rs, voq, vos, vox, s1);
       }
-      mma_superstep_x(acc, w0, x0);
+      x0.mma(acc, w0);
       if (s2 < nss) {
         load_w(w0, rw, soff, lane, s2);
-        load_x(x0, rq, rs, voq, vos, s2);
+        x0.load(rq, rs, voq, vos, vox, s2);
       }
-      if (s1 < nss) mma_superstep_x(acc, w1, x1);
+      if (s1 < nss) x1.mma(acc, w1);
       ss = s2;
     }
     if (KS == 1) {
@@ -693,7 +746,10 @@ template <int MF, int KS, int RG>
 static bool launch_decode(hipStream_t st, const GemmArgs& a) {
   constexpr int rows = 16 * MF * RG;
   if (a.N % rows != 0) return false;
-  hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
+  if (a.xk)
+    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, true>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, false>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
   return true;
 }
 

@@ -231,15 +231,15 @@ def _gemm_inputs(c):
 
 @pytest.mark.parametrize("name,proj,nrows", [("c0", 0, None), ("c1", 0, None), ("t_zipf", 0, None),
                                              ("c2", 0, 384)])
-@pytest.mark.parametrize("flags", ["decode", "prefill", "prefill_xk"])
+@pytest.mark.parametrize("flags", ["decode", "decode_xk", "prefill", "prefill_xk"])
 def test_grouped_gemm_parity(name, proj, nrows, flags):
     c = single_case(name, proj)
     say("gemm", name, proj, flags)
     qo, so = _gemm_inputs(c)
     off = c["R"]["offsets"]
     rl = None if nrows is None else sample_rows(off, nrows)
-    fl = mq.F_FORCE_DECODE if flags == "decode" else mq.F_FORCE_PREFILL
-    xk = dev(_xk_reference(qo, so)) if flags == "prefill_xk" else None
+    fl = mq.F_FORCE_DECODE if flags.startswith("decode") else mq.F_FORCE_PREFILL
+    xk = dev(_xk_reference(qo, so)) if flags.endswith("_xk") else None
     y = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl,
                               xk=xk)
     yb = mq.moesq_grouped_gemm(c["Wd"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.bfloat16,
