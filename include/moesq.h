@@ -203,12 +203,14 @@ int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t row
 /*
  * Load-time repack (model card: the sparse checkpoint is rebuilt into the kernel's own layout at
  * load time) of pair-bitmask v1 weights into the GEMM's fragment layout, same size (2.75 bits per
- * weight): per expert, per 16-row block, per 256-K super-step a 1408-byte fragment; lane
- * l = 16c + r (row r of the block, K [64c, +64) of the super-step) owns bytes [16l, +16) (its
- * eight 8-groups, the two kept bytes (b0, b1) of each stored as (lo b0 | lo b1 << 4,
- * hi b0 | hi b1 << 4)), [1024 + 4l, +4) (per group the code i | j << 2 of its kept pairs i < j,
- * one nibble each, groups in the order 0, 2, 4, 6, 1, 3, 5, 7) and [1280 + 2l, +2) (scale codes).
- *   kl: moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned. Requires K % 256 == 0, N % 16 == 0.
+ * weight): per expert, per 64-row group, per 256-K super-step a 5632-byte unit holding four 16-row
+ * fragments j = 0..3. Lane l = 16c + r (row r of a fragment, K [64c, +64) of the super-step) owns
+ * bytes [1024 j + 16 l, +16) (its eight 8-groups of fragment j, the two kept bytes (b0, b1) of each
+ * stored as (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4)), [4096 + 16 l + 4 j, +4) (per group the code
+ * i | j << 2 of its kept pairs i < j, one nibble each, groups in the order 0, 2, 4, 6, 1, 3, 5, 7)
+ * and [5120 + 8 l + 2 j, +2) (its two scale codes). A wave reads the four fragments of a unit with
+ * six loads.
+ *   kl: moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned. Requires K % 256 == 0, N % 64 == 0.
  */
 int moesq_prepack_weights(void *stream, const moesq_weights *W, uint8_t *kl, size_t kl_bytes);
 

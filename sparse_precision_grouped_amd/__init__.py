@@ -268,7 +268,7 @@ def moesq_prepack_weights(W):
 
 def moesq_compress_weights(w, out=None, workspace=None, dev_status=None, prepack=True):
     """fp32 weights [E, N, K] -> Weights (paired-4:8 pruning + NVFP4 + pair-bitmask v1), plus the
-    kernel layout when ``prepack`` (and K % 256 == 0)."""
+    kernel layout when ``prepack`` (and K % 256 == 0, N % 64 == 0)."""
     _dev(w)
     assert w.dtype == torch.float32 and w.is_contiguous()
     E, N, K = w.shape
@@ -278,7 +278,7 @@ def moesq_compress_weights(w, out=None, workspace=None, dev_status=None, prepack
     _check("moesq_compress_weights",
            lib().moesq_compress_weights(_stream(), _p(w), E, N, K, _p(out.packed), _p(out.mask), _p(out.scale),
                                         _p(out.gscale), _p(workspace), workspace.numel(), _p(dev_status)))
-    if prepack and K % 256 == 0 and N % 16 == 0:
+    if prepack and K % 256 == 0 and N % 64 == 0:
         out.prepack()
     return out
 

@@ -199,7 +199,7 @@ int moesq_prepack_weights(void* stream, const moesq_weights* W, uint8_t* kl, siz
   if (!W || W->E <= 0 || W->N <= 0 || W->K <= 0 || !W->packed || !W->mask || !W->scale || !kl)
     return MOESQ_ERR_INVALID_ARG;
   if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
-  if (W->K % 256 != 0 || W->N % 16 != 0) return MOESQ_ERR_UNSUPPORTED;
+  if (W->K % 256 != 0 || W->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
   if (kl_bytes < moesq_kernel_layout_bytes(W->E, W->N, W->K)) return MOESQ_ERR_WORKSPACE;
   if (!aligned(kl, 16) || !aligned(W->packed, 16) || !aligned(W->mask, 4) || !aligned(W->scale, 2))
     return MOESQ_ERR_UNSUPPORTED;

@@ -12,10 +12,10 @@
 //    gfx950 FP4->f16 convert and multiplied by the UE4M3 block scale (FP8->f16 convert) in f16:
 //    e2m1 * e4m3 has at most 6 significant bits, so every operand is exact and the only rounding
 //    is the fp32 accumulation. No lookup tables: all decoding is VALU work in registers.
-//  - Weights are read from the kernel layout built at load time (prepack_kernel): per 16 rows x
-//    256 K fragment, lane (row r, chunk c) finds its 16 packed bytes, 4 mask bytes and 2 scale
-//    bytes at fixed offsets, so a wave reads 1408 contiguous bytes per fragment with three buffer
-//    loads (SGPR fragment offset, no per-lane 64-bit address arithmetic). The lane covers K
+//  - Weights are read from the kernel layout built at load time (prepack_kernel): units of four
+//    16-row x 256-K fragments, in which lane (row r, chunk c) finds its 16 packed bytes per
+//    fragment and its index codes and scale codes of all four fragments side by side, so a wave
+//    reads a 5632-byte unit with six buffer loads. The lane covers K
 //    [64c + 16s, +16) at step s of the super-step; the activation (B) operand follows the same K
 //    mapping. Buffer loads past an expert's last token return zero, which pads partial tiles.
 //  - Decode (few tokens per expert): weight streaming. One workgroup = 16*MF weight rows of one
@@ -85,17 +85,46 @@ struct WStage {
   uint32_t sw[MF];
 };
 
-// soff[f]: byte offset (wave uniform) of fragment f's first super-step within the expert's layout.
-// The fragment offset goes into the per-lane offset operand: a uniform value that the compiler keeps
-// in a VGPR would otherwise need a readfirstlane loop to reach the scalar offset operand.
+// Where a wave's MF fragments live in the kernel layout: units of 4 fragments (64 rows) per
+// super-step, kGroupBytes each, super-steps of one 64-row group consecutive. g0/g1: byte offset of
+// the group's super-step 0 within the expert; j0/j1: first fragment used in that group. Without SPLIT
+// the MF (2 or 4) fragments are consecutive from (g0, j0); with SPLIT (MF = 4) fragments 0-1 come
+// from (g0, j0) and 2-3 from (g1, j1), as in the gate_up tile (gate rows, then the matching up rows).
+struct WSrc {
+  uint32_t g0, g1;
+  int j0, j1;
+};
+
+// Two consecutive fragments (j, j + 1) of a unit into slots f, f + 1: two 16-byte packed loads, one
+// 8-byte index-code load and one 4-byte scale load (lane offsets go in the per-lane operand).
 template <int MF>
-MOESQ_DEV void load_w(WStage<MF>& st, rsrc_t rw, const uint32_t (&soff)[MF], int lane, int ss) {
+MOESQ_DEV void load_w_pair(WStage<MF>& st, int f, rsrc_t rw, uint32_t go, int j, int lane) {
+  st.pk[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 1024u * j + 16u * lane), 0, 0));
+  st.pk[f + 1] =
+      __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 1024u * (j + 1) + 16u * lane), 0, 0));
+  const auto m = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(go + 4096u + 16u * lane + 4u * j), 0, 0);
+  st.mk[f] = m[0];
+  st.mk[f + 1] = m[1];
+  const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)(go + 5120u + 8u * lane + 2u * j), 0, 0);
+  st.sw[f] = sc;
+  st.sw[f + 1] = sc >> 16;
+}
+
+template <int MF, bool SPLIT>
+MOESQ_DEV void load_w(WStage<MF>& st, rsrc_t rw, const WSrc& src, int lane, int ss) {
+  static_assert(MF == 2 || MF == 4, "fragments per wave");
+  const uint32_t go = src.g0 + (uint32_t)ss * kGroupBytes;
+  if (MF == 4 && !SPLIT) {
 #pragma unroll
-  for (int f = 0; f < MF; f++) {
-    const int so = (int)(soff[f] + (uint32_t)ss * kFragBytes);
-    st.pk[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * lane + so, 0, 0));
-    st.mk[f] = __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * lane + 1024 + so, 0, 0);
-    st.sw[f] = __builtin_amdgcn_raw_buffer_load_b16(rw, 2 * lane + 1280 + so, 0, 0);
+    for (int j = 0; j < 4; j++)
+      st.pk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 1024u * j + 16u * lane), 0, 0));
+    const u32x4 m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 4096u + 16u * lane), 0, 0));
+    st.mk[0] = m.x; st.mk[1] = m.y; st.mk[2] = m.z; st.mk[3] = m.w;
+    const auto sc = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(go + 5120u + 8u * lane), 0, 0);
+    st.sw[0] = sc[0]; st.sw[1] = sc[0] >> 16; st.sw[2] = sc[1]; st.sw[3] = sc[1] >> 16;
+  } else {
+    load_w_pair(st, 0, rw, go, src.j0, lane);
+    if (MF == 4) load_w_pair(st, 2, rw, src.g1 + (uint32_t)ss * kGroupBytes, src.j1, lane);
   }
 }
 
@@ -249,9 +278,11 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
   const int rb0 = (blockIdx.x * RG + rg) * MF;
   const uint32_t ekl = expert_kl_bytes(N, K);
   const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
-  uint32_t soff[MF];
-#pragma unroll
-  for (int f = 0; f < MF; f++) soff[f] = (uint32_t)(rb0 + f) * (uint32_t)nss * kFragBytes;
+  WSrc src;
+  src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * kGroupBytes;
+  src.j0 = rb0 % 4;
+  src.g1 = 0;
+  src.j1 = 0;
   const rsrc_t rq = XK ? make_rsrc((const uint8_t*)a.xk + (size_t)off * K * 2, (uint32_t)ne * K * 2)
                       : make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
   const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
@@ -271,18 +302,18 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
     DStage<XK> x0, x1;
     int ss = kw;
     if (ss < nss) {
-      load_w(w0, rw, soff, lane, ss);
+      load_w<MF, false>(w0, rw, src, lane, ss);
       x0.load(rq, rs, voq, vos, vox, ss);
     }
     while (ss < nss) {
       const int s1 = ss + KS, s2 = ss + 2 * KS;
       if (s1 < nss) {
-        load_w(w1, rw, soff, lane, s1);
+        load_w<MF, false>(w1, rw, src, lane, s1);
         x1.load(rq, rs, voq, vos, vox, s1);
       }
       x0.mma(acc, w0);
       if (s2 < nss) {
-        load_w(w0, rw, soff, lane, s2);
+        load_w<MF, false>(w0, rw, src, lane, s2);
         x0.load(rq, rs, voq, vos, vox, s2);
       }
       if (s1 < nss) x1.mma(acc, w1);
@@ -434,7 +465,7 @@ struct TileCtx {
   int e, off, ne, tb, rb, nv;
   float alpha;
   rsrc_t rw;          // expert's weights (kernel layout)
-  uint32_t soff[MF];  // fragment offsets of the wave's m-fragments (super-step 0)
+  WSrc src;           // the wave's m-fragments in the kernel layout
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
 };
 
@@ -459,12 +490,18 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   const int K = a.K, N = a.N, nss = K / 256;
   const uint32_t ekl = expert_kl_bytes(N, K);
   c.rw = make_rsrc(a.kl + (size_t)c.e * ekl, ekl);
-#pragma unroll
-  for (int f = 0; f < MF; f++) {
-    int rbf;
-    if (MLP) rbf = ((f < 2 ? 0 : N / 2) + c.rb * 256 + 32 * w + 16 * (f & 1)) / 16;
-    else rbf = min(c.rb * 512 + 64 * w, N - 64) / 16 + f;
-    c.soff[f] = __builtin_amdgcn_readfirstlane((uint32_t)rbf * (uint32_t)nss * kFragBytes);
+  if (MLP) {
+    const int rg = (c.rb * 256 + 32 * w) / 16, ru = (N / 2 + c.rb * 256 + 32 * w) / 16;  // gate / up 16-row blocks
+    c.src.g0 = __builtin_amdgcn_readfirstlane((uint32_t)(rg / 4) * (uint32_t)nss * kGroupBytes);
+    c.src.j0 = __builtin_amdgcn_readfirstlane(rg % 4);
+    c.src.g1 = __builtin_amdgcn_readfirstlane((uint32_t)(ru / 4) * (uint32_t)nss * kGroupBytes);
+    c.src.j1 = __builtin_amdgcn_readfirstlane(ru % 4);
+  } else {
+    const int rbf = min(c.rb * 512 + 64 * w, N - 64) / 16;
+    c.src.g0 = __builtin_amdgcn_readfirstlane((uint32_t)(rbf / 4) * (uint32_t)nss * kGroupBytes);
+    c.src.j0 = 0;
+    c.src.g1 = 0;
+    c.src.j1 = 0;
   }
   c.alpha = 1.0f / (a.gscale[c.e] * a.gamma_a[c.e]);
   if (XK) {
@@ -669,7 +706,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   TileCtx<MF> cur = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t, w);
   WStage<MF> wc, wn;
   PStage p;
-  load_w(wc, cur.rw, cur.soff, lane, 0);
+  load_w<MF, MLP>(wc, cur.rw, cur.src, lane, 0);
   issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
   if (!XK) stage_b(p, Bs0, ba);
   __builtin_amdgcn_s_waitcnt(0);
@@ -689,7 +726,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     if (has_n) {
-      load_w(wn, nxt.rw, nxt.soff, lane, ss_n);
+      load_w<MF, MLP>(wn, nxt.rw, nxt.src, lane, ss_n);
       issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
     }
     mma_superstep_lds<MF, NF, XK>(acc, wc, Bc, r16, cc, cur.nv);
@@ -758,7 +795,6 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
   if (variant == 0) {
     bool ok = false;
     switch (decode_variant_default()) {
-      case 1: ok = launch_decode<8, 4, 1>(st, a); break;
       case 2: ok = launch_decode<4, 1, 4>(st, a); break;
       case 3: ok = launch_decode<4, 8, 1>(st, a); break;
       case 4: ok = launch_decode<2, 8, 1>(st, a); break;

@@ -12,6 +12,7 @@ constexpr int32_t kMaxExpertsRoute = 512;
 constexpr int32_t kMaxExpertsGemm = 1024;
 
 constexpr int kFragBytes = 1408;  // 16 rows x 256 K of the kernel weight layout
+constexpr int kGroupBytes = 4 * kFragBytes;  // 4 fragments (64 rows x 256 K): the layout unit
 
 struct GemmArgs {
   const uint8_t* kl;      // kernel layout [E][N/16][K/256][1408 B]

@@ -317,8 +317,10 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
     const uint32_t h23 = ((hi >> 16) & 0xFFu) | ((hi >> 20) & 0xF0u);
     o[j] = l01 | (h01 << 8) | (l23 << 16) | (h23 << 24);
   }
-  uint8_t* F = kl + frag * 1408;
-  *(uint4*)(F + 16 * l) = make_uint4(o[0], o[1], o[2], o[3]);
+  // group of 4 fragments (64 rows) per super-step: fragment j = rowblk % 4
+  const int j = (int)(rowblk & 3);
+  uint8_t* F = kl + ((rowblk >> 2) * nss + ss) * (int64_t)kGroupBytes;
+  *(uint4*)(F + 1024 * j + 16 * l) = make_uint4(o[0], o[1], o[2], o[3]);
   const uint32_t mk = *(const uint32_t*)(mask + row * (K / 16) + 16 * ss + 4 * c);
   uint32_t codes = 0u;
 #pragma unroll
@@ -326,8 +328,8 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
     const int g = (k < 4) ? 2 * k : 2 * (k - 4) + 1;
     codes |= pair_index_code((mk >> (4 * g)) & 15u) << (4 * k);
   }
-  *(uint32_t*)(F + 1024 + 4 * l) = codes;
-  *(uint16_t*)(F + 1280 + 2 * l) = *(const uint16_t*)(scale + row * (K / 32) + 8 * ss + 2 * c);
+  *(uint32_t*)(F + 4096 + 16 * l + 4 * j) = codes;
+  *(uint16_t*)(F + 5120 + 8 * l + 2 * j) = *(const uint16_t*)(scale + row * (K / 32) + 8 * ss + 2 * c);
 }
 
 int launch_prepack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, const uint8_t* scale, int32_t E,

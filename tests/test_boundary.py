@@ -142,12 +142,13 @@ def test_prepack_validation_and_size(L):
     assert L.moesq_kernel_layout_bytes(384, 4096, 7168) == 384 * 4096 * 7168 * 11 // 32
     f = L.moesq_prepack_weights
     f.argtypes = [vp, ctypes.POINTER(CW), vp, ctypes.c_size_t]
-    W = CW(2, 32, 512, FAKE, FAKE, FAKE, FAKE, 0)
-    need = L.moesq_kernel_layout_bytes(2, 32, 512)
+    W = CW(2, 64, 512, FAKE, FAKE, FAKE, FAKE, 0)
+    need = L.moesq_kernel_layout_bytes(2, 64, 512)
     assert f(None, ctypes.byref(W), None, need) == EARG
     assert f(None, ctypes.byref(W), _p(FAKE), need - 1) == EWS
     assert f(None, ctypes.byref(CW(2, 32, 480, FAKE, FAKE, FAKE, FAKE, 0)), _p(FAKE), 1 << 20) == EUNS
     assert f(None, ctypes.byref(CW(2, 24, 512, FAKE, FAKE, FAKE, FAKE, 0)), _p(FAKE), 1 << 20) == EUNS
+    assert f(None, ctypes.byref(CW(2, 32, 512, FAKE, FAKE, FAKE, FAKE, 0)), _p(FAKE), 1 << 20) == EUNS  # N % 64
 
 
 def test_combine_compress_unpack_validation(L):

@@ -78,17 +78,21 @@ def test_compress_edge_patterns():
 
 def _kernel_layout_reference(packed, mask, scale):
     """The kernel weight layout built with numpy from its definition (a byte permutation plus the
-    per-pair nibble interleave), independent of the device prepack."""
+    per-pair nibble interleave), independent of the device prepack: units of 4 fragments (64 rows)
+    per 256-K super-step; lane l = 16c + r of fragment j owns packed bytes [1024 j + 16 l, +16),
+    index codes [4096 + 16 l + 4 j, +4) and scale codes [5120 + 8 l + 2 j, +2)."""
     E, N, K4 = packed.shape
     K = K4 * 4
     nss = K // 256
-    out = np.zeros((E, N // 16, nss, 1408), np.uint8)
+    G = N // 64
+    out = np.zeros((E, G, nss, 5632), np.uint8)
     pk = packed.reshape(E, N // 16, 16, nss, 4, 16)            # [e, rb, r, ss, c, 16 bytes]
     b0, b1 = pk[..., 0::2], pk[..., 1::2]
     sh = np.empty_like(pk)
     sh[..., 0::2] = (b0 & 15) | ((b1 & 15) << 4)
     sh[..., 1::2] = (b0 >> 4) | (b1 & 0xF0)
-    out[..., :1024] = sh.transpose(0, 1, 3, 4, 2, 5).reshape(E, N // 16, nss, 1024)
+    frag = sh.transpose(0, 1, 3, 4, 2, 5).reshape(E, G, 4, nss, 1024)          # [e, g, j, ss, lane*16]
+    out[..., :4096] = frag.transpose(0, 1, 3, 2, 4).reshape(E, G, nss, 4096)
     # mask nibbles -> pair-index codes i | j << 2, nibble order (g0, g2, g4, g6, g1, g3, g5, g7)
     code = np.zeros(16, np.uint32)
     for i, j in ((0, 1), (0, 2), (1, 2), (0, 3), (1, 3), (2, 3)):
@@ -98,9 +102,11 @@ def _kernel_layout_reference(packed, mask, scale):
     nib = [code[(word >> (4 * g)) & 15] for g in range(8)]
     order = [0, 2, 4, 6, 1, 3, 5, 7]
     cw = sum(nib[order[kk]] << np.uint32(4 * kk) for kk in range(8)).astype(np.uint32)
-    out[..., 1024:1280] = np.ascontiguousarray(cw.reshape(E, N // 16, nss, 64)).view(np.uint8)
-    sc = scale.reshape(E, N // 16, 16, nss, 4, 2).transpose(0, 1, 3, 4, 2, 5)
-    out[..., 1280:] = sc.reshape(E, N // 16, nss, 128)
+    cw = cw.reshape(E, G, 4, nss, 64).transpose(0, 1, 3, 4, 2)                  # [e, g, ss, lane, j]
+    out[..., 4096:5120] = np.ascontiguousarray(cw).view(np.uint8).reshape(E, G, nss, 1024)
+    sc = scale.reshape(E, N // 16, 16, nss, 4, 2).transpose(0, 1, 3, 4, 2, 5)  # [e, rb, ss, c, r, 2]
+    sc = sc.reshape(E, G, 4, nss, 64, 2).transpose(0, 1, 3, 4, 2, 5)           # [e, g, ss, lane, j, 2]
+    out[..., 5120:] = sc.reshape(E, G, nss, 512)
     return out.reshape(-1)
 
 
