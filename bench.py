@@ -324,6 +324,101 @@ def cpu_baseline(wl, orc, gen, max_reps=3):
             "sample": sample + ", median of %d run(s), %.3f s each" % (len(times), t)}
 
 
+# Kernel sweep of the pages' Appendix D.2 (Table 8 layer shapes, per-expert token counts following the
+# ragged pattern {N, 3N/4, N/2, N/4} repeated over the G experts).
+SWEEP_LAYERS = {
+    "kimi_gate_up": (4096, 7168, [32, 64, 128, 256, 512, 1024], [24, 48, 96, 192, 384]),
+    "kimi_down": (7168, 2048, [32, 64, 128, 256, 512, 1024], [24, 48, 96, 192, 384]),
+    "qwen_gate_up": (1536, 2048, [16, 32, 64, 128, 256, 512, 1024], [8, 16, 32, 64, 128]),
+    "qwen_down": (2048, 768, [16, 32, 64, 128, 256, 512, 1024], [8, 16, 32, 64, 128]),
+}
+
+
+def sweep_counts(G, N):
+    pat = [N, 3 * N // 4, N // 2, N // 4]
+    return [pat[g % 4] for g in range(G)]
+
+
+def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto"):
+    """Median graph-replay time of the grouped GEMM (and of quantize + GEMM from bf16 activations)
+    for each (G, N); one JSON line per point."""
+    M, K, Nl, Gl = SWEEP_LAYERS[layer]
+    Nl = Ns or Nl
+    Gl = Gs or Gl
+    Gmax = max(Gl)
+    cfg = dataclasses.replace(gen.CONFIGS["c0"], E=Gmax, N=M, K=K, seed=4242)
+    W = mq.Weights.empty(Gmax, M, K)
+    chunk = max(1, min(Gmax, int(2e9 // (M * K * 4))))
+    buf = torch.empty((chunk, M, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mq.moesq_workspace_bytes(mq.WS_COMPRESS, 0, 0, chunk), dtype=torch.uint8, device="cuda")
+    for e0 in range(0, Gmax, chunk):
+        n = min(chunk, Gmax - e0)
+        for j in range(n):
+            gen.gpu_fill_normal(buf[j], cfg.seed, gen.weight_stream(0, e0 + j), cfg.w_std)
+        sub = mq.Weights(W.packed[e0:e0 + n], W.mask[e0:e0 + n], W.scale[e0:e0 + n], W.gscale[e0:e0 + n])
+        mq.moesq_compress_weights(buf[:n], out=sub, workspace=ws, prepack=False)
+    W.prepack()
+    del buf
+    ekl = W.kl.numel() // Gmax
+    st = torch.cuda.current_stream()
+    for G in Gl:
+        Wg = mq.Weights(W.packed[:G], W.mask[:G], W.scale[:G], W.gscale[:G], W.kl[:G * ekl])
+        for N in Nl:
+            counts = sweep_counts(G, N)
+            rows = int(sum(counts))
+            offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
+            x = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+            gen.gpu_fill_normal(x, cfg.seed, gen.act_stream(7), 1.0)
+            xb = x.to(torch.bfloat16)
+            del x
+            g = mq.moesq_global_scale(xb)
+            ga = g.expand(G).contiguous()
+            decode = rows <= 16 * G if kernel == "auto" else kernel == "decode"
+            flags = mq.F_FORCE_DECODE if decode else mq.F_FORCE_PREFILL
+            xk = torch.empty((rows, K), dtype=torch.float16, device="cuda") if decode else None
+            q = torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda")
+            s = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+            y = torch.empty((rows, M), dtype=torch.bfloat16, device="cuda")
+            mq.moesq_quantize_act(xb, g, q=q, s=s, xk=xk)
+
+            def gemm():
+                mq.moesq_grouped_gemm(Wg, q, s, ga, offsets, y=y, xk=xk, flags=flags)
+
+            def quant_gemm():
+                mq.moesq_quantize_act(xb, g, q=q, s=s, xk=xk)
+                mq.moesq_grouped_gemm(Wg, q, s, ga, offsets, y=y, xk=xk, flags=flags)
+
+            out = {"layer": layer, "M": M, "K": K, "G": G, "N": N, "rows": rows,
+                   "kernel": "decode" if decode else "tiled"}
+            for name, fn in (("gemm", gemm), ("quant_gemm", quant_gemm)):
+                side = torch.cuda.Stream()
+                side.wait_stream(st)
+                with torch.cuda.stream(side):
+                    fn()
+                st.wait_stream(side)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    fn()
+                for _ in range(3):
+                    graph.replay()
+                ts = []
+                for _ in range(reps):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(st)
+                    graph.replay()
+                    b.record(st)
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                t = float(np.median(ts)) * 1e-3
+                out[name + "_us"] = round(t * 1e6, 2)
+                if name == "gemm":
+                    out["tflops_eff"] = round(tflops_eff(M, K, rows, t), 1)
+                    out["weight_GBs"] = round(G * weight_bytes(M, K) / t / 1e9, 1)
+            print(json.dumps(out), flush=True)
+            del q, s, y, xk, xb
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +431,10 @@ def main(argv=None):
     ap.add_argument("--operand", choices=["auto", "nvfp4", "f16"], default="auto",
                     help="activation operand of the GEMMs: NVFP4 codes decoded in the kernel, or the quantizer's "
                          "f16 copy; auto = f16 for weight-streaming (decode) workloads, NVFP4 for tiled ones")
+    ap.add_argument("--sweep", choices=sorted(SWEEP_LAYERS) + ["all"],
+                    help="the pages' G x N kernel sweep on one layer shape (one JSON line per point)")
+    ap.add_argument("--sweep-kernel", choices=["auto", "decode", "tiled"], default="auto")
+    ap.add_argument("--sweep-n", type=int, nargs="*", help="restrict the sweep's per-expert token counts")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (traffic-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -358,6 +457,12 @@ def main(argv=None):
 
     import gen
     import sparse_precision_grouped_amd as mq
+
+    if args.sweep:
+        torch.cuda.set_device(0)
+        for layer in (sorted(SWEEP_LAYERS) if args.sweep == "all" else [args.sweep]):
+            run_sweep(layer, torch, gen, mq, Ns=args.sweep_n, kernel=args.sweep_kernel)
+        return 0
 
     torch.cuda.set_device(0)
     cfgw = gen.CONFIGS[args.workload]
