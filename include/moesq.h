@@ -214,6 +214,26 @@ int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t row
  */
 int moesq_prepack_weights(void *stream, const moesq_weights *W, uint8_t *kl, size_t kl_bytes);
 
+/*
+ * Dense NVFP4 control (paper Appendix D.2 compares the sparse kernel with a dense NVFP4 grouped GEMM):
+ * the same kernels on unpruned weights, so that the two differ only in sparsity. Dense weights of
+ * expert e: codes [E][N][K/2] (two E2M1 codes per byte, lower K in the low nibble), UE4M3 block
+ * scales [E][N][K/32], tensor scale gscale [E] (Eq. 5); moesq_quantize_act with gamma = gscale[e]
+ * produces codes and scales from fp32 rows.
+ * moesq_prepack_dense_weights builds the dense kernel layout (moesq_dense_layout_bytes(E, N, K) =
+ * E * N * K * 9 / 16 bytes, 4.5 bits per weight: per 64-row group and 256-K super-step a 9216-byte
+ * unit; lane l of fragment j owns 32 code bytes at 2048 j + 32 l and 4 scale bytes at 8192 + 16 l + 4 j,
+ * the scale bytes stored once per lane pair that reads them). Requires K % 256 == 0, N % 64 == 0.
+ * moesq_dense_grouped_gemm: as moesq_grouped_gemm with W->kl = the dense layout and W->gscale
+ * (W->packed, W->mask, W->scale are not read).
+ */
+size_t moesq_dense_layout_bytes(int32_t E, int32_t N, int32_t K);
+int moesq_prepack_dense_weights(void *stream, int32_t E, int32_t N, int32_t K, const uint8_t *codes,
+                                const uint8_t *scales, uint8_t *kl, size_t kl_bytes);
+int moesq_dense_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, const uint8_t *s, const void *xk,
+                             const float *gamma_a, const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype,
+                             uint32_t flags);
+
 /* Bytes of the kernel layout of E experts of [N][K] weights: E * N * K * 11 / 32. */
 size_t moesq_kernel_layout_bytes(int32_t E, int32_t N, int32_t K);
 

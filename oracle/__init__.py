@@ -278,6 +278,42 @@ def expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, row_list=None):
     return dict(y13=y13, h=h, hq=hq_rows, hs=hs_rows, y2=y2, rows=rl)
 
 
+# --- dense NVFP4 control (paper Appendix D.2: the sparse kernel is compared with a dense NVFP4
+# grouped GEMM; here the same format without pruning) ----------------------------------------------
+def compress_dense(w):
+    """Unpruned NVFP4 of fp32 weights [E, N, K]: per expert the Eq. 5 tensor scale over the whole
+    [N, K] tensor, then the Eq. 3/5 row quantizer with that scale. Returns codes [E, N, K/2],
+    scale [E, N, K/32], gscale [E]."""
+    w = _c(w, np.float32)
+    E, N, K = w.shape
+    codes = np.empty((E, N, K // 2), np.uint8)
+    scale = np.empty((E, N, K // 32), np.uint8)
+    gscale = np.empty(E, np.float32)
+    for e in range(E):
+        gscale[e] = global_scale_of(w[e])
+        codes[e], scale[e] = quantize_rows(w[e], gscale[e])
+    return dict(codes=codes, scale=scale, gscale=gscale, E=E, N=N, K=K)
+
+
+def dense_grouped_gemm(Wd, q, s, gamma_a, offsets, row_list=None):
+    """Rows of Y (double) for the dense control: Y[p] = (deq(q[p], s[p]) / gamma_a[e]) .
+    (deq(codes_e, scale_e) / gscale_e)^T for the expert e owning row p; the product by numpy matmul
+    in double."""
+    offsets = np.asarray(offsets, np.int64)
+    E = Wd["E"]
+    rows = int(offsets[-1])
+    rl = np.arange(rows, dtype=np.int64) if row_list is None else np.asarray(row_list, np.int64)
+    gamma_a = np.broadcast_to(np.asarray(gamma_a, np.float32), (E,))
+    ex = expert_of_rows(offsets, rl)
+    y = np.zeros((rl.size, Wd["N"]), np.float64)
+    for e in np.unique(ex):
+        sel = np.flatnonzero(ex == e)
+        w = dequant(Wd["codes"][e], Wd["scale"][e]) / np.float64(Wd["gscale"][e])
+        x = dequant(np.asarray(q)[rl[sel]], np.asarray(s)[rl[sel]]) / np.float64(gamma_a[e])
+        y[sel] = x @ w.T
+    return y
+
+
 # --- metrics -------------------------------------------------------------------------------
 def rel_frobenius(a, ref):
     """||a - ref||_F / ||ref||_F in double."""

@@ -65,6 +65,10 @@ def lib():
         L.moesq_prepack_weights.argtypes = [vp, W, vp, sz]
         L.moesq_kernel_layout_bytes.argtypes = [i32, i32, i32]
         L.moesq_kernel_layout_bytes.restype = sz
+        L.moesq_dense_layout_bytes.argtypes = [i32, i32, i32]
+        L.moesq_dense_layout_bytes.restype = sz
+        L.moesq_prepack_dense_weights.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz]
+        L.moesq_dense_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, vp, i64, vp, i32, u32]
         L.moesq_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32]
         L.moesq_workspace_bytes.restype = sz
         L.moesq_status_str.argtypes = [i32]
@@ -300,3 +304,60 @@ def moesq_unpack_weights(W, dense=None, dev_status=None):
     c = W.cstruct()
     _check("moesq_unpack_weights", lib().moesq_unpack_weights(_stream(), ctypes.byref(c), _p(dense), _p(dev_status)))
     return dense
+
+
+# ---------------------------------------------------------------- dense NVFP4 control ----------
+class DenseWeights:
+    """Unpruned NVFP4 weights of one projection for E experts (the dense control of the sparse
+    kernels): codes [E,N,K/2] u8 (two E2M1 codes per byte, lower K in the low nibble), scale
+    [E,N,K/32] u8 (UE4M3), gscale [E] f32, and kl, the dense kernel layout."""
+
+    def __init__(self, codes, scale, gscale, kl=None):
+        E, N, K2 = codes.shape
+        self.E, self.N, self.K = E, N, K2 * 2
+        assert scale.shape == (E, N, self.K // 32) and gscale.shape == (E,)
+        self.codes, self.scale, self.gscale, self.kl = codes, scale, gscale, kl
+
+    def prepack(self):
+        nb = lib().moesq_dense_layout_bytes(self.E, self.N, self.K)
+        if self.kl is None or self.kl.numel() < nb:
+            self.kl = torch.empty(nb, dtype=torch.uint8, device=self.codes.device)
+        _check("moesq_prepack_dense_weights",
+               lib().moesq_prepack_dense_weights(_stream(), self.E, self.N, self.K, _p(self.codes), _p(self.scale),
+                                                 _p(self.kl), nb))
+        return self
+
+    def cstruct(self):
+        return _CWeights(self.E, self.N, self.K, None, None, None, self.gscale.data_ptr(),
+                         None if self.kl is None else self.kl.data_ptr())
+
+    def nbytes(self):
+        return self.codes.numel() + self.scale.numel()
+
+
+def compress_dense_weights(w, prepack=True):
+    """fp32 weights [E, N, K] -> DenseWeights: per expert the Eq. 5 tensor scale over the whole
+    [N, K] tensor, then row-wise NVFP4 quantization with that scale (no pruning)."""
+    _dev(w)
+    E, N, K = w.shape
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
+    gscale = torch.empty((E,), dtype=torch.float32, device=w.device)
+    for e in range(E):
+        moesq_global_scale(w[e], out=gscale[e:e + 1])
+        moesq_quantize_act(w[e], gscale[e:e + 1], q=codes[e], s=scale[e])
+    out = DenseWeights(codes, scale, gscale)
+    if prepack and K % 256 == 0 and N % 64 == 0:
+        out.prepack()
+    return out
+
+
+def moesq_dense_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):
+    rows = q.shape[0]
+    if y is None:
+        y = torch.empty((rows, W.N), dtype=y_dtype, device=q.device)
+    c = W.cstruct()
+    _check("moesq_dense_grouped_gemm",
+           lib().moesq_dense_grouped_gemm(_stream(), ctypes.byref(c), _p(q), _p(s), _p(xk), _p(gamma_a), _p(offsets),
+                                          rows, _p(y), _dtype_code(y.dtype), flags))
+    return y

@@ -206,6 +206,38 @@ int moesq_prepack_weights(void* stream, const moesq_weights* W, uint8_t* kl, siz
   return launch_prepack((hipStream_t)stream, W->packed, W->mask, W->scale, W->E, W->N, W->K, kl);
 }
 
+size_t moesq_dense_layout_bytes(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)E * (size_t)N * (size_t)K / 16 * 9;
+}
+
+int moesq_prepack_dense_weights(void* stream, int32_t E, int32_t N, int32_t K, const uint8_t* codes,
+                                const uint8_t* scales, uint8_t* kl, size_t kl_bytes) {
+  if (E <= 0 || N <= 0 || K <= 0 || !codes || !scales || !kl) return MOESQ_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
+  if (K % 256 != 0 || N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
+  if (kl_bytes < moesq_dense_layout_bytes(E, N, K)) return MOESQ_ERR_WORKSPACE;
+  if (!aligned(kl, 16) || !aligned(codes, 4)) return MOESQ_ERR_UNSUPPORTED;
+  return launch_prepack_dense((hipStream_t)stream, codes, scales, E, N, K, kl);
+}
+
+int moesq_dense_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,
+                             const float* gamma_a, const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype,
+                             uint32_t flags) {
+  if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  const int rc = gemm_common(W, q, s, xk, gamma_a, offsets, rows, y);
+  if (rc != MOESQ_OK) return rc;
+  if ((int64_t)W->N * W->K / 16 * 9 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  GemmArgs a{};
+  a.kl = W->kl; a.gscale = W->gscale;
+  a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
+  a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
+  int variant = rows <= (int64_t)16 * W->E ? 0 : 1;
+  if (flags & MOESQ_F_FORCE_DECODE) variant = 0;
+  if (flags & MOESQ_F_FORCE_PREFILL) variant = 1;
+  return launch_dense_gemm((hipStream_t)stream, a, rows, variant);
+}
+
 int moesq_unpack_weights(void* stream, const moesq_weights* W, uint8_t* dense_nvfp4, int32_t* dev_status) {
   if (!W || W->E <= 0 || W->N <= 0 || W->K <= 0 || W->K % 32 != 0 || !W->packed || !W->mask || !dense_nvfp4)
     return MOESQ_ERR_INVALID_ARG;

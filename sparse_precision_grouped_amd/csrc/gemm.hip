@@ -244,18 +244,144 @@ template <>
 struct DStage<false> {
   XStage x;
   MOESQ_DEV void load(rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t vos, uint32_t, int ss) { load_x(x, rq, rs, voq, vos, ss); }
-  template <int MF>
-  MOESQ_DEV void mma(f32x4 (&acc)[MF], const WStage<MF>& w) const { mma_superstep_x(acc, w, x); }
 };
 template <>
 struct DStage<true> {
   XKStage x;
   MOESQ_DEV void load(rsrc_t rq, rsrc_t, uint32_t, uint32_t, uint32_t vox, int ss) { load_xk(x, rq, vox, ss); }
-  template <int MF>
-  MOESQ_DEV void mma(f32x4 (&acc)[MF], const WStage<MF>& w) const { mma_superstep_xk(acc, w, x); }
 };
 
 MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
+
+// ============================================================== dense NVFP4 control operand =====
+// The dense control (unpruned NVFP4, one UE4M3 scale per 32 K) runs the same kernels with the dense
+// v_mfma_f32_16x16x32_f16: per 64-K step and 16-row fragment, two MFMAs over the 8-groups g (lo) and
+// g + 16 (hi) that the sparse step covers with one 2:4 MFMA. Layout (moesq_prepack_dense_weights):
+// per expert, 64-row group and 256-K super-step a kDenseUnitBytes unit; fragment j's lane l owns the
+// 32 bytes [2048 j + 32 l, +32) = code words (S0 lo, S0 hi, S1 lo, S1 hi, S2 lo, S2 hi, S3 lo, S3 hi),
+// each 8-group with its nibbles in the operand order (0, 2, 4, 6, 1, 3, 5, 7), and the 4 bytes
+// [8192 + 16 l + 4 j, +4) = block-scale codes (steps 0-1 lo, 0-1 hi, 2-3 lo, 2-3 hi).
+constexpr int kDenseUnitBytes = 9216;
+
+template <int MF>
+struct DWStage {
+  u32x4 c0[MF], c1[MF];  // code words of steps 0-1 and 2-3
+  uint32_t sc[MF];       // scale codes
+};
+
+template <int MF>
+MOESQ_DEV void load_dw(DWStage<MF>& st, rsrc_t rw, uint32_t g0, int j0, int lane, int ss) {
+  static_assert(MF == 2 || MF == 4, "fragments per wave");
+  const uint32_t go = g0 + (uint32_t)ss * kDenseUnitBytes;
+#pragma unroll
+  for (int f = 0; f < MF; f++) {
+    const uint32_t o = go + 2048u * (j0 + f) + 32u * lane;
+    st.c0[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0));
+    st.c1[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(o + 16u), 0, 0));
+  }
+  if (MF == 4) {
+    const u32x4 m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 8192u + 16u * lane), 0, 0));
+    st.sc[0] = m.x; st.sc[1] = m.y; st.sc[2] = m.z; st.sc[3] = m.w;
+  } else {
+    const auto m = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(go + 8192u + 16u * lane + 4u * j0), 0, 0);
+    st.sc[0] = m[0]; st.sc[1] = m[1];
+  }
+}
+
+// One dense A operand (8 f16) from a code word in operand nibble order, scaled by sc.
+MOESQ_DEV f16x8 dense_frag(uint32_t wd, f16x2 sc) {
+  u32x4 o;
+  o.x = f16x2_bits(MOESQ_CVT_FP4(wd, 0) * sc);
+  o.y = f16x2_bits(MOESQ_CVT_FP4(wd, 1) * sc);
+  o.z = f16x2_bits(MOESQ_CVT_FP4(wd, 2) * sc);
+  o.w = f16x2_bits(MOESQ_CVT_FP4(wd, 3) * sc);
+  return __builtin_bit_cast(f16x8, o);
+}
+
+struct DMeta {
+  f16x2 lo01, hi01, lo23, hi23;
+};
+
+template <int MF>
+MOESQ_DEV DMeta dense_meta(const DWStage<MF>& w, int f) {
+  DMeta m;
+  e4m3_pair_f16x2(w.sc[f], m.lo01, m.hi01);
+  e4m3_pair_f16x2(w.sc[f] >> 16, m.lo23, m.hi23);
+  return m;
+}
+
+// Step S of fragment f against the activation operand halves (blo: 8-group g, bhi: g + 16).
+template <int S, int MF>
+MOESQ_DEV f32x4 dense_step(const DWStage<MF>& w, const DMeta& m, int f, u32x4 blo, u32x4 bhi, f32x4 acc) {
+  const u32x4 cw = S < 2 ? w.c0[f] : w.c1[f];
+  const uint32_t wlo = (S & 1) ? cw.z : cw.x, whi = (S & 1) ? cw.w : cw.y;
+  const f16x8 alo = dense_frag(wlo, S < 2 ? m.lo01 : m.lo23);
+  const f16x8 ahi = dense_frag(whi, S < 2 ? m.hi01 : m.hi23);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, __builtin_bit_cast(f16x8, blo), acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, __builtin_bit_cast(f16x8, bhi), acc, 0, 0, 0);
+}
+
+template <int S, int MF>
+MOESQ_DEV void dense_x_step(f32x4 (&acc)[MF], const DWStage<MF>& w, const DMeta (&m)[MF], const XStage& x,
+                            f16x2 a01, f16x2 a23, f16x2 b01, f16x2 b23) {
+  const u32x4 blo = decode_x_group(x.bc[2 * S], S < 2 ? a01 : a23);
+  const u32x4 bhi = decode_x_group(x.bc[2 * S + 1], S < 2 ? b01 : b23);
+#pragma unroll
+  for (int f = 0; f < MF; f++) acc[f] = dense_step<S>(w, m[f], f, blo, bhi, acc[f]);
+}
+
+template <int MF>
+MOESQ_DEV void dense_superstep_x(f32x4 (&acc)[MF], const DWStage<MF>& w, const XStage& x) {
+  DMeta m[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) m[f] = dense_meta(w, f);
+  f16x2 a01, a23, b01, b23;
+  e4m3_pair_f16x2(x.bs0, a01, a23);
+  e4m3_pair_f16x2(x.bs1, b01, b23);
+  dense_x_step<0>(acc, w, m, x, a01, a23, b01, b23);
+  dense_x_step<1>(acc, w, m, x, a01, a23, b01, b23);
+  dense_x_step<2>(acc, w, m, x, a01, a23, b01, b23);
+  dense_x_step<3>(acc, w, m, x, a01, a23, b01, b23);
+}
+
+template <int MF>
+MOESQ_DEV void dense_superstep_xk(f32x4 (&acc)[MF], const DWStage<MF>& w, const XKStage& x) {
+  DMeta m[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) m[f] = dense_meta(w, f);
+#pragma unroll
+  for (int f = 0; f < MF; f++) {
+    acc[f] = dense_step<0>(w, m[f], f, x.lo[0], x.hi[0], acc[f]);
+    acc[f] = dense_step<1>(w, m[f], f, x.lo[1], x.hi[1], acc[f]);
+    acc[f] = dense_step<2>(w, m[f], f, x.lo[2], x.hi[2], acc[f]);
+    acc[f] = dense_step<3>(w, m[f], f, x.lo[3], x.hi[3], acc[f]);
+  }
+}
+
+MOESQ_DEV uint32_t expert_dense_bytes(int N, int K) { return (uint32_t)(N / 64) * (uint32_t)(K / 256) * kDenseUnitBytes; }
+
+// Weight stage of the decode kernel: the sparse layout (WStage) or the dense control (DWStage).
+template <int MF, bool DENSE>
+struct WS;
+template <int MF>
+struct WS<MF, false> {
+  WStage<MF> w;
+  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w<MF, false>(w, rw, src, lane, ss); }
+};
+template <int MF>
+struct WS<MF, true> {
+  DWStage<MF> w;
+  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
+};
+
+template <int MF>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false>& w, const DStage<false>& x) { mma_superstep_x(acc, w.w, x.x); }
+template <int MF>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false>& w, const DStage<true>& x) { mma_superstep_xk(acc, w.w, x.x); }
+template <int MF>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<false>& x) { dense_superstep_x(acc, w.w, x.x); }
+template <int MF>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<true>& x) { dense_superstep_xk(acc, w.w, x.x); }
 
 // ============================================================================ decode kernel =====
 // Weight streaming for few tokens per expert. A workgroup of KS * RG waves covers 16*MF*RG weight rows
@@ -264,7 +390,7 @@ MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (
 // LDS (deterministic). Each wave keeps two super-steps of operands in flight (register double
 // buffering). Experts with more than 16 tokens loop over 16-token blocks.
 // grid (N / (16*MF*RG), E).
-template <int MF, int KS, int RG, bool XK>
+template <int MF, int KS, int RG, bool XK, bool DENSE>
 __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
@@ -276,10 +402,10 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
   const int kw = w % KS, rg = w / KS;
   const int K = a.K, N = a.N, nss = K / 256;
   const int rb0 = (blockIdx.x * RG + rg) * MF;
-  const uint32_t ekl = expert_kl_bytes(N, K);
+  const uint32_t ekl = DENSE ? expert_dense_bytes(N, K) : expert_kl_bytes(N, K);
   const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
   WSrc src;
-  src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * kGroupBytes;
+  src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * (DENSE ? kDenseUnitBytes : kGroupBytes);
   src.j0 = rb0 % 4;
   src.g1 = 0;
   src.j1 = 0;
@@ -298,25 +424,25 @@ __global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
     const uint32_t voq = (uint32_t)tok * (K / 2) + 32u * (c >> 1) + 4u * (c & 1);
     const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
     const uint32_t vox = (uint32_t)tok * (uint32_t)(2 * K) + 16u * (8u * (c >> 1) + (c & 1));
-    WStage<MF> w0, w1;
+    WS<MF, DENSE> w0, w1;
     DStage<XK> x0, x1;
     int ss = kw;
     if (ss < nss) {
-      load_w<MF, false>(w0, rw, src, lane, ss);
+      w0.load(rw, src, lane, ss);
       x0.load(rq, rs, voq, vos, vox, ss);
     }
     while (ss < nss) {
       const int s1 = ss + KS, s2 = ss + 2 * KS;
       if (s1 < nss) {
-        load_w<MF, false>(w1, rw, src, lane, s1);
+        w1.load(rw, src, lane, s1);
         x1.load(rq, rs, voq, vos, vox, s1);
       }
-      x0.mma(acc, w0);
+      stage_mma(acc, w0, x0);
       if (s2 < nss) {
-        load_w<MF, false>(w0, rw, src, lane, s2);
+        w0.load(rw, src, lane, s2);
         x0.load(rq, rs, voq, vos, vox, s2);
       }
-      if (s1 < nss) x1.mma(acc, w1);
+      if (s1 < nss) stage_mma(acc, w1, x1);
       ss = s2;
     }
     if (KS == 1) {
@@ -420,6 +546,71 @@ MOESQ_DEV void mma_superstep_lds(f32x4 (&acc)[MF][NF], const WStage<MF>& w, cons
   lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
 }
 
+// Dense control: step S in two halves (8-groups g and g + 16), each a decoded A operand per fragment
+// against the staged activations, one dense MFMA per (fragment, n-fragment).
+template <int S, int MF, int NF>
+MOESQ_DEV void dense_lds_step(f32x4 (&acc)[MF][NF], const DWStage<MF>& w, const DMeta (&m)[MF], const uint8_t* Bs,
+                              int r16, int c, int nv) {
+  constexpr int G = MOESQ_TILE_SKIP_G;
+  const int g1 = 8 * (c >> 1) + 2 * S + (c & 1);
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    f16x8 A[MF];
+#pragma unroll
+    for (int f = 0; f < MF; f++) {
+      const u32x4 cw = S < 2 ? w.c0[f] : w.c1[f];
+      const uint32_t wd = h == 0 ? ((S & 1) ? cw.z : cw.x) : ((S & 1) ? cw.w : cw.y);
+      const f16x2 sc = h == 0 ? (S < 2 ? m[f].lo01 : m[f].lo23) : (S < 2 ? m[f].hi01 : m[f].hi23);
+      A[f] = dense_frag(wd, sc);
+    }
+#pragma unroll
+    for (int n0 = 0; n0 < NF; n0 += G) {
+      if (G == NF || n0 < nv) {
+#pragma unroll
+        for (int n = n0; n < n0 + G; n++) {
+          const f16x8 B = __builtin_bit_cast(f16x8, *(const u32x4*)b_chunk(Bs, n * 16 + r16, g1 + 16 * h));
+#pragma unroll
+          for (int f = 0; f < MF; f++) acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[f], B, acc[f][n], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <int MF, int NF>
+MOESQ_DEV void dense_superstep_lds(f32x4 (&acc)[MF][NF], const DWStage<MF>& w, const uint8_t* Bs, int r16, int c,
+                                   int nv) {
+  DMeta m[MF];
+#pragma unroll
+  for (int f = 0; f < MF; f++) m[f] = dense_meta(w, f);
+  dense_lds_step<0, MF, NF>(acc, w, m, Bs, r16, c, nv);
+  dense_lds_step<1, MF, NF>(acc, w, m, Bs, r16, c, nv);
+  dense_lds_step<2, MF, NF>(acc, w, m, Bs, r16, c, nv);
+  dense_lds_step<3, MF, NF>(acc, w, m, Bs, r16, c, nv);
+}
+
+// Weight stage of the tiled kernel: the sparse layout or the dense control.
+template <int MF, bool MLP, bool DENSE>
+struct TWS;
+template <int MF, bool MLP>
+struct TWS<MF, MLP, false> {
+  WStage<MF> w;
+  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w<MF, MLP>(w, rw, src, lane, ss); }
+  template <int NF, bool XK>
+  MOESQ_DEV void mma(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) const {
+    mma_superstep_lds<MF, NF, XK>(acc, w, Bs, r16, c, nv);
+  }
+};
+template <int MF, bool MLP>
+struct TWS<MF, MLP, true> {
+  DWStage<MF> w;
+  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
+  template <int NF, bool XK>
+  MOESQ_DEV void mma(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) const {
+    dense_superstep_lds<MF, NF>(acc, w, Bs, r16, c, nv);
+  }
+};
+
 // Per-expert tile counts ceil(n_e / kTileTok) -> exclusive prefix tile_pre[0..E] in LDS (E+1
 // entries), and the expert offsets copied to off_l[0..E]. part: LDS scratch of THREADS ints.
 template <int THREADS>
@@ -471,7 +662,7 @@ struct TileCtx {
 
 // Tile t of the list ordered expert -> token tile -> row block (row block fastest): workgroups of one
 // XCD that run neighbouring tiles share the activation tile in L2.
-template <int MF, bool MLP, bool XK>
+template <int MF, bool MLP, bool XK, bool DENSE>
 MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, int RB, int t,
                                 int w) {
   TileCtx<MF> c;
@@ -488,7 +679,7 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   c.ne = __builtin_amdgcn_readfirstlane(off_l[c.e + 1]) - c.off;
   c.nv = min(kTileNF, (c.ne - c.tb + 15) / 16);
   const int K = a.K, N = a.N, nss = K / 256;
-  const uint32_t ekl = expert_kl_bytes(N, K);
+  const uint32_t ekl = DENSE ? expert_dense_bytes(N, K) : expert_kl_bytes(N, K);
   c.rw = make_rsrc(a.kl + (size_t)c.e * ekl, ekl);
   if (MLP) {
     const int rg = (c.rb * 256 + 32 * w) / 16, ru = (N / 2 + c.rb * 256 + 32 * w) / 16;  // gate / up 16-row blocks
@@ -498,7 +689,8 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
     c.src.j1 = __builtin_amdgcn_readfirstlane(ru % 4);
   } else {
     const int rbf = min(c.rb * 512 + 64 * w, N - 64) / 16;
-    c.src.g0 = __builtin_amdgcn_readfirstlane((uint32_t)(rbf / 4) * (uint32_t)nss * kGroupBytes);
+    c.src.g0 = __builtin_amdgcn_readfirstlane((uint32_t)(rbf / 4) * (uint32_t)nss *
+                                              (uint32_t)(DENSE ? kDenseUnitBytes : kGroupBytes));
     c.src.j0 = 0;
     c.src.g1 = 0;
     c.src.j1 = 0;
@@ -674,7 +866,7 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
 // handling tiles start + j, + J, ... The super-steps of all the workgroup's tiles form one
 // pipeline: while step i computes, the weights (registers) and activations (LDS) of step i+1 --
 // possibly the first step of the next tile -- are in flight; one barrier per step.
-template <bool MLP, bool XK>
+template <bool MLP, bool XK, bool DENSE = false>
 __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = kTileNF;
   constexpr int BBYTES = kBTileBytes;
@@ -703,10 +895,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  TileCtx<MF> cur = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t, w);
-  WStage<MF> wc, wn;
+  TileCtx<MF> cur = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, RB, t, w);
+  TWS<MF, MLP, DENSE> wc, wn;
   PStage p;
-  load_w<MF, MLP>(wc, cur.rw, cur.src, lane, 0);
+  wc.load(cur.rw, cur.src, lane, 0);
   issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
   if (!XK) stage_b(p, Bs0, ba);
   __builtin_amdgcn_s_waitcnt(0);
@@ -722,14 +914,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     }
     const bool has_n = t_n < tend;
     TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK>(a, tile_pre, off_l, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     if (has_n) {
-      load_w<MF, MLP>(wn, nxt.rw, nxt.src, lane, ss_n);
+      wn.load(nxt.rw, nxt.src, lane, ss_n);
       issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
     }
-    mma_superstep_lds<MF, NF, XK>(acc, wc, Bc, r16, cc, cur.nv);
+    wc.template mma<NF, XK>(acc, Bc, r16, cc, cur.nv);
     if (ss == nss - 1) {
       tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
 #pragma unroll
@@ -779,14 +971,16 @@ static int decode_variant_default() {
   return v;
 }
 
-template <int MF, int KS, int RG>
+template <int MF, int KS, int RG, bool DENSE = false>
 static bool launch_decode(hipStream_t st, const GemmArgs& a) {
   constexpr int rows = 16 * MF * RG;
   if (a.N % rows != 0) return false;
   if (a.xk)
-    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, true>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, true, DENSE>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, false>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MF, KS, RG, false, DENSE>), dim3(a.N / rows, a.E), dim3(64 * KS * RG), 0,
+                       st, a);
   return true;
 }
 
@@ -816,6 +1010,20 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
       if (xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
       else hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
     }
+  }
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// Dense control: variant 0 = weight streaming, otherwise the tiled kernel (no MLP epilogue).
+int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
+  if (rows == 0) return MOESQ_OK;
+  if (variant == 0) {
+    launch_decode<4, 4, 1, true>(st, a);
+  } else {
+    const int grid = 8 * ((device_cu_count() + 7) / 8);
+    const size_t lds = tile_lds_bytes(a.E);
+    if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+    else hipLaunchKernelGGL((gemm_tile_kernel<false, false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }

@@ -41,6 +41,10 @@ int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32
                     const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
                     uint8_t* q, uint8_t* s, void* xk);
 
+int launch_prepack_dense(hipStream_t st, const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                         uint8_t* kl);
+int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
+
 int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
                         float* gamma_out);
 

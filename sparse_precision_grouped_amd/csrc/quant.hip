@@ -341,6 +341,62 @@ int launch_prepack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, c
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 
+// Dense NVFP4 control layout (the unpruned counterpart of prepack_kernel's layout): per expert,
+// 64-row group and 256-K super-step a 9216-byte unit. Fragment j's lane l = 16c + r owns the 32 bytes
+// [2048 j + 32 l, +32): the code words of its 8-groups g(S, h) = 8 (c>>1) + 2 S + (c&1) + 16 h in the
+// order (S0 h0, S0 h1, S1 h0, ..., S3 h1), each word's nibbles reordered to (0, 2, 4, 6, 1, 3, 5, 7);
+// and the 4 bytes [8192 + 16 l + 4 j, +4): the scale codes of blocks 2q, 4+2q, 2q+1, 5+2q (q = c>>1)
+// of the super-step.
+constexpr int kDenseUnit = 9216;
+
+MOESQ_DEV uint32_t operand_nibble_order(uint32_t w) {
+  uint32_t o = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int src = i < 4 ? 2 * i : 2 * (i - 4) + 1;
+    o |= ((w >> (4 * src)) & 15u) << (4 * i);
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(256) void prepack_dense_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales, int32_t N, int32_t K,
+                                                            int64_t nfrag, uint8_t* __restrict__ kl) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nfrag * 64) return;
+  const int64_t frag = i >> 6;
+  const int l = (int)(i & 63), r = l & 15, c = l >> 4, q = c >> 1;
+  const int nss = K / 256;
+  const int64_t ss = frag % nss;
+  const int64_t rowblk = frag / nss;   // e * (N/16) + rb
+  const int64_t row = rowblk * 16 + r;
+  const int j = (int)(rowblk & 3);
+  uint8_t* U = kl + ((rowblk >> 2) * nss + ss) * (int64_t)kDenseUnit;
+  const uint8_t* src = codes + row * (K / 2) + 128 * ss;
+  uint32_t o[8];
+#pragma unroll
+  for (int S = 0; S < 4; S++)
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int g = 8 * q + 2 * S + (c & 1) + 16 * h;
+      o[2 * S + h] = operand_nibble_order(*(const uint32_t*)(src + 4 * g));
+    }
+  *(uint4*)(U + 2048 * j + 32 * l) = make_uint4(o[0], o[1], o[2], o[3]);
+  *(uint4*)(U + 2048 * j + 32 * l + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  const uint8_t* b = scales + row * (K / 32) + 8 * ss;
+  *(uint32_t*)(U + 8192 + 16 * l + 4 * j) =
+      (uint32_t)b[2 * q] | ((uint32_t)b[4 + 2 * q] << 8) | ((uint32_t)b[2 * q + 1] << 16) | ((uint32_t)b[5 + 2 * q] << 24);
+}
+
+int launch_prepack_dense(hipStream_t st, const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                         uint8_t* kl) {
+  const int64_t nfrag = (int64_t)E * (N / 16) * (K / 256);
+  if (nfrag == 0) return MOESQ_OK;
+  hipLaunchKernelGGL(prepack_dense_kernel, dim3((unsigned)((nfrag * 64 + 255) / 256)), dim3(256), 0, st, codes, scales,
+                     N, K, nfrag, kl);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
 // ------------------------------------------------------------------ tensor scale (Eq. 5) ---------
 // amax of a [rows][K] tensor (leading dimension ld) accumulated as float bits in out[0], then
 // replaced in place by gamma = 448 / (amax / 6).

@@ -384,3 +384,46 @@ def test_mlp_chain_matches_step_by_step(orc):
     assert np.array_equal(M["y2"], y2)
     # the requantized h is close to h (NVFP4 relative error)
     assert orc.rel_frobenius(orc.dequant(hq, hs) / np.float64(gh[0]), h) < 0.12
+
+
+# ---------------------------------------------------------------- dense NVFP4 control ------
+def test_dense_gemm_on_unpacked_sparse_weights_equals_sparse_gemm(orc):
+    """The dense control computes the same product as the sparse GEMM when its weights are the
+    sparse weights written out densely (model card round trip: unpack gives dense NVFP4 bytes)."""
+    cfg = gen.CONFIGS["c0"]
+    w = np.stack([gen.weights_expert(cfg, 0, e, cfg.N, cfg.K) for e in range(cfg.E)])
+    W = orc.compress(w)
+    Wd = dict(codes=orc.unpack(W["packed"], W["mask"]), scale=W["scale"], gscale=W["gscale"], E=cfg.E, N=cfg.N,
+              K=cfg.K)
+    x = gen.activations(cfg, 0, cfg.T, cfg.K)
+    ids, _ = gen.routing(cfg)
+    R = orc.route(ids, cfg.E)
+    ga = np.full(cfg.E, orc.global_scale_of(x), np.float32) * np.linspace(0.5, 2.0, cfg.E).astype(np.float32)
+    q, s = orc.dispatch_quantize(x, R["sorted_slot"], cfg.k, R["offsets"], ga)
+    ys = orc.grouped_gemm(W, q, s, ga, R["offsets"])
+    yd = orc.dense_grouped_gemm(Wd, q, s, ga, R["offsets"])
+    assert orc.rel_frobenius(yd, ys) < 1e-12
+
+
+def test_dense_compress_and_one_hot_column(orc):
+    """Dense compression keeps every weight (no pruning): the block holding the tensor amax gets the
+    largest scale code 448 (Eq. 5), the reconstruction error is the quantizer's, and a one-hot
+    activation reads back one dequantized weight column."""
+    rng = np.random.default_rng(5)
+    E, N, K = 2, 64, 256
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    Wd = orc.compress_dense(w)
+    for e in range(E):
+        r, c = np.unravel_index(np.argmax(np.abs(w[e])), w[e].shape)
+        assert Wd["scale"][e, r, c // 32] == 0x7E
+        deq = orc.dequant(Wd["codes"][e], Wd["scale"][e]) / np.float64(Wd["gscale"][e])
+        assert np.count_nonzero(deq) > 0.9 * N * K                  # dense: no paired-4:8 zeros
+        assert orc.rel_frobenius(deq, w[e]) < 0.12
+    # one token routed to expert 1 whose activation is 1.0 at K index 37 and 0 elsewhere
+    x = np.zeros((1, K), np.float32)
+    x[0, 37] = 1.0
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    q, s = orc.quantize_rows(x, ga[0])
+    y = orc.dense_grouped_gemm(Wd, q, s, ga, np.array([0, 0, 1]))
+    col = orc.dequant(Wd["codes"][1], Wd["scale"][1])[:, 37] / np.float64(Wd["gscale"][1])
+    assert np.allclose(y[0], col, rtol=1e-12, atol=0)

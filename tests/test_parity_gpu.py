@@ -438,3 +438,105 @@ def test_mlp_parity_c4_full_size():
     ref = orc.combine(yt[torch.from_numpy(sp)].to(torch.float64).numpy(), np.arange(sp.size, dtype=np.int32),
                       wts[toks])
     assert orc.rel_frobenius(out[toks], ref) <= 1e-6
+
+
+# ---------------------------------------------------------------- dense NVFP4 control ----------
+def _dense_layout_reference(codes, scale):
+    """The dense control's kernel layout built with numpy from its definition: per 64-row group and
+    256-K super-step a 9216-byte unit; lane l = 16c + r of fragment j owns 32 code bytes at
+    2048 j + 32 l (words of 8-groups g(S, h) = 8 (c>>1) + 2 S + (c&1) + 16 h in the order S0h0, S0h1,
+    ..., S3h1, nibbles reordered to 0,2,4,6,1,3,5,7) and 4 scale bytes at 8192 + 16 l + 4 j (blocks
+    2q, 4+2q, 2q+1, 5+2q of the super-step, q = c>>1)."""
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    nss, G = K // 256, N // 64
+    words = np.ascontiguousarray(codes.reshape(E, N, nss, 32, 4)).view(np.uint32)[..., 0]   # [e, row, ss, group]
+    order = [0, 2, 4, 6, 1, 3, 5, 7]
+    reo = np.zeros_like(words)
+    for i, src in enumerate(order):
+        reo |= ((words >> np.uint32(4 * src)) & np.uint32(15)) << np.uint32(4 * i)
+    out = np.zeros((E, G, nss, 9216), np.uint8)
+    rows = reo.reshape(E, G, 4, 16, nss, 32)            # [e, g, j, r, ss, group]
+    sc = scale.reshape(E, G, 4, 16, nss, 8)             # [e, g, j, r, ss, block]
+    for c in range(4):
+        q = c >> 1
+        for S in range(4):
+            for h in range(2):
+                grp = 8 * q + 2 * S + (c & 1) + 16 * h
+                wv = rows[..., grp].transpose(0, 1, 4, 2, 3)                                # [e, g, ss, j, r]
+                for j in range(4):
+                    off = 2048 * j + 32 * (16 * c) + 4 * (2 * S + h)
+                    byt = np.ascontiguousarray(wv[:, :, :, j, :]).view(np.uint8).reshape(E, G, nss, 16, 4)
+                    for r in range(16):
+                        out[:, :, :, off + 32 * r: off + 32 * r + 4] = byt[:, :, :, r, :]
+        blocks = [2 * q, 4 + 2 * q, 2 * q + 1, 5 + 2 * q]
+        for j in range(4):
+            for r in range(16):
+                l = 16 * c + r
+                for b, blk in enumerate(blocks):
+                    out[:, :, :, 8192 + 16 * l + 4 * j + b] = sc[:, :, j, r, :, blk]
+    return out.reshape(-1)
+
+
+def _dense_case(name):
+    key = ("dense", name)
+    if key in _dense_cache:
+        return _dense_cache[key]
+    c = single_case(name)
+    cfg, E, N, K = c["cfg"], c["E"], c["N"], c["K"]
+    w = np.stack([gen.weights_expert(cfg, 0, e, N, K) for e in range(E)])
+    Wo = orc.compress_dense(w)
+    Wg = mq.compress_dense_weights(dev(w))
+    out = dict(c, Wdo=Wo, Wdg=Wg)
+    _dense_cache[key] = out
+    return out
+
+
+_dense_cache = {}
+
+
+@pytest.mark.parametrize("name", ["c0", "t_zipf"])
+def test_dense_compress_and_layout(name):
+    c = _dense_case(name)
+    say("dense compress + layout", name)
+    Wg, Wo = c["Wdg"], c["Wdo"]
+    assert np.array_equal(host(Wg.codes), Wo["codes"])
+    assert np.array_equal(host(Wg.scale), Wo["scale"])
+    assert np.array_equal(host(Wg.gscale), Wo["gscale"])
+    assert np.array_equal(host(Wg.kl), _dense_layout_reference(Wo["codes"], Wo["scale"]))
+
+
+@pytest.mark.parametrize("name,nrows", [("c0", None), ("t_zipf", None), ("c1", None), ("c2", 256)])
+@pytest.mark.parametrize("flags", ["decode", "decode_xk", "prefill", "prefill_xk"])
+def test_dense_gemm_parity(name, nrows, flags):
+    c = _dense_case(name)
+    say("dense gemm", name, flags)
+    qo, so = _gemm_inputs(c)
+    off = c["R"]["offsets"]
+    rl = None if nrows is None else sample_rows(off, nrows)
+    fl = mq.F_FORCE_DECODE if flags.startswith("decode") else mq.F_FORCE_PREFILL
+    xk = dev(_xk_reference(qo, so)) if flags.endswith("_xk") else None
+    y = mq.moesq_dense_grouped_gemm(c["Wdg"], dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32,
+                                    flags=fl, xk=xk)
+    rows = np.arange(int(off[-1])) if rl is None else rl
+    ref = orc.dense_grouped_gemm(c["Wdo"], qo, so, c["ga"], off, rows)
+    err = orc.rel_frobenius(host(y)[rows], ref)
+    say("rel-Frobenius", err)
+    assert err <= GEMM_TOL
+
+
+def test_dense_kernel_on_unpacked_sparse_weights_matches_sparse_kernel():
+    """The dense control on the sparse weights written out densely gives the sparse kernel's result
+    (same values; only the MFMA instruction and summation order differ)."""
+    c = single_case("t_zipf")
+    say("dense vs sparse kernels t_zipf")
+    qo, so = _gemm_inputs(c)
+    off = c["R"]["offsets"]
+    Wd = c["Wd"]
+    dense = mq.moesq_unpack_weights(Wd)
+    Wdd = mq.DenseWeights(dense, Wd.scale, Wd.gscale).prepack()
+    for fl in (mq.F_FORCE_DECODE, mq.F_FORCE_PREFILL):
+        ys = host(mq.moesq_grouped_gemm(Wd, dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32, flags=fl))
+        yd = host(mq.moesq_dense_grouped_gemm(Wdd, dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32,
+                                              flags=fl))
+        assert orc.rel_frobenius(yd, ys) <= 1e-5
