@@ -339,7 +339,7 @@ def sweep_counts(G, N):
     return [pat[g % 4] for g in range(G)]
 
 
-def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto"):
+def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto", dense=False):
     """Median graph-replay time of the grouped GEMM (and of quantize + GEMM from bf16 activations)
     for each (G, N); one JSON line per point."""
     M, K, Nl, Gl = SWEEP_LAYERS[layer]
@@ -358,12 +358,26 @@ def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto"):
         sub = mq.Weights(W.packed[e0:e0 + n], W.mask[e0:e0 + n], W.scale[e0:e0 + n], W.gscale[e0:e0 + n])
         mq.moesq_compress_weights(buf[:n], out=sub, workspace=ws, prepack=False)
     W.prepack()
+    Wd = None
+    if dense:
+        # the dense control: the same weights quantized without pruning
+        Wd = mq.DenseWeights(torch.empty((Gmax, M, K // 2), dtype=torch.uint8, device="cuda"),
+                             torch.empty((Gmax, M, K // 32), dtype=torch.uint8, device="cuda"),
+                             torch.empty((Gmax,), dtype=torch.float32, device="cuda"))
+        for e in range(Gmax):
+            gen.gpu_fill_normal(buf[0], cfg.seed, gen.weight_stream(0, e), cfg.w_std)
+            mq.moesq_global_scale(buf[0], out=Wd.gscale[e:e + 1])
+            mq.moesq_quantize_act(buf[0], Wd.gscale[e:e + 1], q=Wd.codes[e], s=Wd.scale[e])
+        Wd.prepack()
     del buf
     ekl = W.kl.numel() // Gmax
+    dkl = Wd.kl.numel() // Gmax if dense else 0
     st = torch.cuda.current_stream()
+    first = True
     for G in Gl:
         Wg = mq.Weights(W.packed[:G], W.mask[:G], W.scale[:G], W.gscale[:G], W.kl[:G * ekl])
-        for N in Nl:
+        Wdg = mq.DenseWeights(Wd.codes[:G], Wd.scale[:G], Wd.gscale[:G], Wd.kl[:G * dkl]) if dense else None
+        for N in (Nl[:1] + Nl) if first else Nl:  # the first point twice: clocks and caches settle
             counts = sweep_counts(G, N)
             rows = int(sum(counts))
             offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device="cuda")
@@ -388,9 +402,13 @@ def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto"):
                 mq.moesq_quantize_act(xb, g, q=q, s=s, xk=xk)
                 mq.moesq_grouped_gemm(Wg, q, s, ga, offsets, y=y, xk=xk, flags=flags)
 
+            def dense_gemm():
+                mq.moesq_dense_grouped_gemm(Wdg, q, s, ga, offsets, y=y, xk=xk, flags=flags)
+
             out = {"layer": layer, "M": M, "K": K, "G": G, "N": N, "rows": rows,
                    "kernel": "decode" if decode else "tiled"}
-            for name, fn in (("gemm", gemm), ("quant_gemm", quant_gemm)):
+            runs = [("gemm", gemm), ("quant_gemm", quant_gemm)] + ([("dense_gemm", dense_gemm)] if dense else [])
+            for name, fn in runs:
                 side = torch.cuda.Stream()
                 side.wait_stream(st)
                 with torch.cuda.stream(side):
@@ -415,7 +433,12 @@ def run_sweep(layer, torch, gen, mq, reps=20, Ns=None, Gs=None, kernel="auto"):
                 if name == "gemm":
                     out["tflops_eff"] = round(tflops_eff(M, K, rows, t), 1)
                     out["weight_GBs"] = round(G * weight_bytes(M, K) / t / 1e9, 1)
-            print(json.dumps(out), flush=True)
+                if name == "dense_gemm":
+                    out["dense_tflops_eff"] = round(tflops_eff(M, K, rows, t), 1)
+                    out["speedup_vs_dense"] = round(out["dense_gemm_us"] / out["gemm_us"], 3)
+            if not first:
+                print(json.dumps(out), flush=True)
+            first = False
             del q, s, y, xk, xb
 
 
@@ -435,6 +458,8 @@ def main(argv=None):
                     help="the pages' G x N kernel sweep on one layer shape (one JSON line per point)")
     ap.add_argument("--sweep-kernel", choices=["auto", "decode", "tiled"], default="auto")
     ap.add_argument("--sweep-n", type=int, nargs="*", help="restrict the sweep's per-expert token counts")
+    ap.add_argument("--sweep-dense", action="store_true",
+                    help="also time the dense NVFP4 control on the same weights (speedup of the sparse kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (traffic-counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -461,7 +486,7 @@ def main(argv=None):
     if args.sweep:
         torch.cuda.set_device(0)
         for layer in (sorted(SWEEP_LAYERS) if args.sweep == "all" else [args.sweep]):
-            run_sweep(layer, torch, gen, mq, Ns=args.sweep_n, kernel=args.sweep_kernel)
+            run_sweep(layer, torch, gen, mq, Ns=args.sweep_n, kernel=args.sweep_kernel, dense=args.sweep_dense)
         return 0
 
     torch.cuda.set_device(0)
