@@ -17,6 +17,27 @@ namespace moesq {
 constexpr int kQuantMaxE = 4096;
 constexpr int kQuantMaxK = 512;
 
+MOESQ_DEV void load_chunk(const void* __restrict__ x, int x_bf16, int64_t t, int64_t ld_x, int ch, bool valid,
+                          float v[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = 0.0f;
+  if (!valid) return;
+  if (x_bf16) {
+    const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
+    }
+  } else {
+    const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
+    const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K,
                                                        int64_t ld_x, const int32_t* __restrict__ slot_pos, int32_t k,
                                                        const float* __restrict__ gamma,
@@ -29,12 +50,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t = blockIdx.x;
   const int nk = slot_pos ? k : 1;
+  const int nchunk = (K + 511) / 512;
+  // the independent loads first: this wave's first chunk of the row, the token's destinations, the
+  // expert offsets
+  float v[8];
+  load_chunk(x, x_bf16, t, ld_x, w * 64 + lane, w < nchunk && w * 64 + lane < K / 8, v);
+  int32_t p0 = tid < nk ? (slot_pos ? slot_pos[t * k + tid] : (int32_t)t) : -1;
   if (offsets) {
     for (int i = tid; i <= E; i += 256) off_l[i] = offsets[i];
     __syncthreads();
   }
   for (int j = tid; j < nk; j += 256) {
-    int32_t p = slot_pos ? slot_pos[t * k + j] : (int32_t)t;
+    int32_t p = j == tid ? p0 : (slot_pos ? slot_pos[t * k + j] : (int32_t)t);
     float g = gamma[0];
     if (p >= 0 && offsets) {
       if (p >= off_l[E]) {
@@ -52,29 +79,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     gam[j] = g;
   }
   __syncthreads();
-  const int nchunk = (K + 511) / 512;
   for (int chunk = w; chunk < nchunk; chunk += 4) {
     const int ch = chunk * 64 + lane;  // 8-value group index within the row
     const bool valid = ch < K / 8;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    if (valid) {
-      if (x_bf16) {
-        const uint4 raw = *(const uint4*)((const uint16_t*)x + t * ld_x + 8 * ch);
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          v[2 * i] = bf16_bits_to_f32(wd[i] & 0xFFFFu);
-          v[2 * i + 1] = bf16_bits_to_f32(wd[i] >> 16);
-        }
-      } else {
-        const float4 a = *(const float4*)((const float*)x + t * ld_x + 8 * ch);
-        const float4 b = *(const float4*)((const float*)x + t * ld_x + 8 * ch + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-      }
-    }
+    if (chunk != w) load_chunk(x, x_bf16, t, ld_x, ch, valid, v);
     bool have = false;
     float gq = 0.0f;
     uint32_t codes = 0u, sc = 0u;

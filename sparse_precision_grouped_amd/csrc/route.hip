@@ -36,12 +36,12 @@ MOESQ_DEV int key_bits(int E) { return 32 - __builtin_clz((unsigned)(E > 1 ? E -
 template <int THREADS>
 MOESQ_DEV void scatter_round(const int32_t* __restrict__ ids, int64_t n, int64_t base_slot, int32_t E,
                              int32_t* pos_base, int32_t* wave_tab, int32_t* __restrict__ sorted_slot,
-                             int32_t* __restrict__ slot_pos, int32_t* dev_status) {
+                             int32_t* __restrict__ slot_pos, int32_t* dev_status, int e_pre = -2) {
   constexpr int WAVES = THREADS / 64;
   const int tid = threadIdx.x, w = tid >> 6;
   const int64_t f = base_slot + tid;
   int e = -1;
-  if (f < n) e = ids[f];
+  if (f < n) e = e_pre != -2 ? e_pre : ids[f];
   const bool valid = (f < n) && e >= 0 && e < E;
   if (f < n && !valid) {
     slot_pos[f] = -1;
@@ -120,21 +120,30 @@ __global__ __launch_bounds__(kSmallThreads) void route_single_kernel(const int32
   int32_t* pos = hist + E;                    // [E+1]
   int32_t* wave_tab = pos + E + 1;            // [4 * E]
   __shared__ int32_t wsum[kSmallThreads / 64];
+  constexpr int R = kRouteSingleMax / kSmallThreads;  // slots per thread, kept in registers
   const int tid = threadIdx.x;
+  int ev[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int64_t f = tid + (int64_t)r * kSmallThreads;
+    ev[r] = f < n ? ids[f] : -1;
+  }
   for (int i = tid; i < E; i += kSmallThreads) hist[i] = 0;
   __syncthreads();
-  for (int64_t f = tid; f < n; f += kSmallThreads) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-  }
+#pragma unroll
+  for (int r = 0; r < R; r++)
+    if (ev[r] >= 0 && ev[r] < E) atomicAdd(&hist[ev[r]], 1);
   __syncthreads();
   block_exclusive_scan<kSmallThreads>(hist, E, pos, wsum);
   for (int i = tid; i <= E; i += kSmallThreads) {
     offsets[i] = pos[i];
     if (i < E) counts[i] = hist[i];
   }
-  for (int64_t b = 0; b < n; b += kSmallThreads) {
-    scatter_round<kSmallThreads>(ids, n, b, E, pos, wave_tab, sorted_slot, slot_pos, dev_status);
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    if ((int64_t)r * kSmallThreads >= n) break;
+    scatter_round<kSmallThreads>(ids, n, (int64_t)r * kSmallThreads, E, pos, wave_tab, sorted_slot, slot_pos,
+                                 dev_status, ev[r]);
     __syncthreads();
   }
 }
