@@ -131,6 +131,26 @@ int moesq_quantize_act(void *stream, const void *x, int32_t x_dtype, int64_t T, 
                        const int32_t *offsets, int32_t E, uint8_t *q, uint8_t *s, void *xk);
 
 /*
+ * Dispatch in one call (paper Appendix D.1: routing metadata and the quantized activations are
+ * produced on the device before the grouped GEMM): moesq_route_permute followed by
+ * moesq_quantize_act(x, slot_pos, k, rows = T*k, gamma, offsets, E). Every output (counts, offsets,
+ * sorted_slot, slot_pos, q, s, xk, *dev_status) is byte-identical to that pair of calls. For
+ * decode-sized batches (T*k <= 2048, k <= 32) it is a single kernel launch in which each token's
+ * workgroup ranks all T*k ids itself; otherwise it enqueues the two steps.
+ *   topk_ids [T][k] int32 (device); E <= 512; gamma [E] per-expert tensor scales (device).
+ *   x, x_dtype, K, ld_x, q [T*k][K/2], s [T*k][K/32], xk: as moesq_quantize_act.
+ *   counts, offsets, sorted_slot, slot_pos, workspace, dev_status: as moesq_route_permute
+ *   (workspace = moesq_workspace_bytes(MOESQ_WS_ROUTE, T, k, E, 0, 0, 0) bytes; unused, and may be
+ *   NULL, on the single-launch path).
+ * Errors: the union of the two calls' argument checks, returned before anything is enqueued.
+ */
+int moesq_route_quantize(void *stream, const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                         const void *x, int32_t x_dtype, int32_t K, int64_t ld_x, const float *gamma,
+                         int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
+                         void *workspace, size_t workspace_bytes, uint8_t *q, uint8_t *s, void *xk,
+                         int32_t *dev_status);
+
+/*
  * Grouped sparse GEMM (paper Section 2: Y_e = X_e W_e^T in one launch for variable per-expert token
  * counts; Section 3.4: sparse operand W on the left, Y_e^T = W_e X_e^T; block scales applied in the
  * product, alpha_e = 1/(gamma_w,e * gamma_a,e) applied to the fp32 accumulator).

@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = [
-    "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm",
+    "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_route_quantize",
+    "moesq_grouped_gemm",
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
     "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
     "moesq_prepack_weights", "moesq_kernel_layout_bytes",
@@ -56,6 +57,8 @@ def lib():
         W = ctypes.POINTER(_CWeights)
         L.moesq_route_permute.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_quantize_act.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp, vp]
+        L.moesq_route_quantize.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp,
+                                           vp, vp, vp]
         L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, vp, i64, vp, i32, u32]
         L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
         L.moesq_unpermute_combine.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
@@ -74,7 +77,7 @@ def lib():
         L.moesq_status_str.argtypes = [i32]
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
-        for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_grouped_gemm", "moesq_expert_mlp",
+        for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_route_quantize", "moesq_grouped_gemm", "moesq_expert_mlp",
                      "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale",
                      "moesq_prepack_weights"):
             getattr(L, name).restype = ctypes.c_int
@@ -204,6 +207,40 @@ def moesq_quantize_act(x, gamma, slot_pos=None, k=1, offsets=None, q=None, s=Non
            lib().moesq_quantize_act(_stream(), _p(x), _dtype_code(x.dtype), T, K, x.stride(0), _p(slot_pos), k,
                                     rows, _p(gamma), _p(offsets), E, _p(q), _p(s), _p(xk if want_xk else None)))
     return (q, s, xk) if want_xk else (q, s)
+
+
+def moesq_route_quantize(topk_ids, E, x, gamma, rt=None, q=None, s=None, xk=None, workspace=None,
+                         dev_status=None):
+    """Routing + scatter quantization in one call (one kernel launch for decode-sized batches).
+    topk_ids [T, k] int32, x [T, K] fp32/bf16, gamma [E] fp32. ``rt`` is a dict of routing outputs as
+    returned by moesq_route_permute (allocated when None); ``xk`` as in moesq_quantize_act.
+    Returns (rt, q, s) or (rt, q, s, xk)."""
+    _dev(topk_ids)
+    _dev(x)
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and x.stride(1) == 1
+    T, k = topk_ids.shape
+    K = x.shape[1]
+    dev = x.device
+    i32 = torch.int32
+    if rt is None:
+        rt = dict(counts=torch.empty(E, dtype=i32, device=dev), offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                  sorted_slot=torch.empty(T * k, dtype=i32, device=dev),
+                  slot_pos=torch.empty(T * k, dtype=i32, device=dev))
+    q = torch.empty((T * k, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((T * k, K // 32), dtype=torch.uint8, device=dev) if s is None else s
+    want_xk = xk is not None
+    if xk is True:
+        xk = torch.empty((T * k, K), dtype=torch.float16, device=dev)
+    need = moesq_workspace_bytes(WS_ROUTE, T, k, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("moesq_route_quantize",
+           lib().moesq_route_quantize(_stream(), _p(topk_ids), T, k, E, _p(x), _dtype_code(x.dtype), K, x.stride(0),
+                                      _p(gamma), _p(rt["counts"]), _p(rt["offsets"]), _p(rt["sorted_slot"]),
+                                      _p(rt["slot_pos"]), _p(workspace), wsb, _p(q), _p(s),
+                                      _p(xk if want_xk else None), _p(dev_status)))
+    return (rt, q, s, xk) if want_xk else (rt, q, s)
 
 
 def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):

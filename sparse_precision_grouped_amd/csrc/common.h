@@ -142,3 +142,40 @@ MOESQ_DEV uint32_t f32_to_bf16_bits(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 MOESQ_DEV float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// ---------------------------------------------------------------- block scan -------------------
+// Exclusive scan of vals[0..E) (LDS) into out[0..E] (LDS, out[E] = total) by a block of THREADS:
+// each thread sums a contiguous range, wave shuffles scan the per-thread sums, one LDS exchange
+// combines the waves.
+template <int THREADS>
+MOESQ_DEV void block_exclusive_scan(const int32_t* vals, int32_t E, int32_t* out, int32_t* wsum) {
+  constexpr int WAVES = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (E + THREADS - 1) / THREADS;
+  const int lo = min(E, tid * per), hi = min(E, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; i++) sum += vals[i];
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int v = 0; v < WAVES; v++) before += (v < w) ? wsum[v] : 0;
+  int run = before + incl - sum;
+  for (int i = lo; i < hi; i++) {
+    out[i] = run;
+    run += vals[i];
+  }
+  if (tid == THREADS - 1) {
+    int tot = 0;
+#pragma unroll
+    for (int v = 0; v < WAVES; v++) tot += wsum[v];
+    out[E] = tot;
+  }
+  __syncthreads();
+}

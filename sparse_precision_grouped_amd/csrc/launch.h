@@ -9,6 +9,7 @@ namespace moesq {
 
 constexpr int64_t kRouteSingleMax = 2048;  // slots handled by the one-workgroup routing path
 constexpr int32_t kMaxExpertsRoute = 512;
+constexpr int32_t kFusedRouteMaxK = 32;    // top-k handled by the fused route + quantize kernel
 constexpr int32_t kMaxExpertsGemm = 1024;
 
 constexpr int kFragBytes = 1408;  // 16 rows x 256 K of the kernel weight layout
@@ -40,6 +41,13 @@ int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
                     const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
                     uint8_t* q, uint8_t* s, void* xk);
+// Routing + scatter quantization: one fused launch when route_quantize_fused(T, k, E), else the
+// routing kernels followed by the quantizer (ws = the routing workspace).
+bool route_quantize_fused(int64_t T, int32_t k, int32_t E);
+int launch_route_quantize(hipStream_t st, const int32_t* ids, int64_t T, int32_t k, int32_t E, const void* x,
+                          bool x_bf16, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status,
+                          uint8_t* q, uint8_t* s, void* xk);
 
 int launch_prepack_dense(hipStream_t st, const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
                          uint8_t* kl);

@@ -38,6 +38,45 @@ MOESQ_DEV void load_chunk(const void* __restrict__ x, int x_bf16, int64_t t, int
   }
 }
 
+// Quantize token t's row (this wave's first chunk already in v) and write the codes to the nk
+// permuted rows dst[0..nk) (LDS; negative = skipped), each with its expert's tensor scale gam[j].
+MOESQ_DEV void quantize_token_copies(const void* __restrict__ x, int x_bf16, int64_t t, int32_t K, int64_t ld_x,
+                                     float v[8], int nk, const int32_t* dst, const float* gam,
+                                     uint8_t* __restrict__ q, uint8_t* __restrict__ s, uint8_t* __restrict__ xk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nchunk = (K + 511) / 512;
+  for (int chunk = w; chunk < nchunk; chunk += 4) {
+    const int ch = chunk * 64 + lane;  // 8-value group index within the row
+    const bool valid = ch < K / 8;
+    if (chunk != w) load_chunk(x, x_bf16, t, ld_x, ch, valid, v);
+    bool have = false;
+    float gq = 0.0f;
+    uint32_t codes = 0u, sc = 0u;
+    u32x4 xv = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < nk; j++) {
+      const int32_t p = dst[j];
+      if (p < 0) continue;
+      const float g = gam[j];
+      if (!have || g != gq) {
+        quant8_block4(v, g, codes, sc);
+        if (xk) {
+          // the same values dequantized (exact in f16), in the GEMM's de-interleaved group order
+          f16x2 sv, unused;
+          e4m3_pair_f16x2(sc, sv, unused);
+          xv = decode_x_group(codes, sv);
+        }
+        gq = g;
+        have = true;
+      }
+      if (valid) {
+        *(uint32_t*)(q + (int64_t)p * (K / 2) + 4 * ch) = codes;
+        if ((lane & 3) == 0) s[(int64_t)p * (K / 32) + ch / 4] = (uint8_t)sc;
+        if (xk) *(u32x4*)(xk + ((int64_t)p * K + 8 * ch) * 2) = xv;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K,
                                                        int64_t ld_x, const int32_t* __restrict__ slot_pos, int32_t k,
                                                        const float* __restrict__ gamma,
@@ -79,36 +118,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     gam[j] = g;
   }
   __syncthreads();
-  for (int chunk = w; chunk < nchunk; chunk += 4) {
-    const int ch = chunk * 64 + lane;  // 8-value group index within the row
-    const bool valid = ch < K / 8;
-    if (chunk != w) load_chunk(x, x_bf16, t, ld_x, ch, valid, v);
-    bool have = false;
-    float gq = 0.0f;
-    uint32_t codes = 0u, sc = 0u;
-    u32x4 xv = {0u, 0u, 0u, 0u};
-    for (int j = 0; j < nk; j++) {
-      const int32_t p = dst[j];
-      if (p < 0) continue;
-      const float g = gam[j];
-      if (!have || g != gq) {
-        quant8_block4(v, g, codes, sc);
-        if (xk) {
-          // the same values dequantized (exact in f16), in the GEMM's de-interleaved group order
-          f16x2 sv, unused;
-          e4m3_pair_f16x2(sc, sv, unused);
-          xv = decode_x_group(codes, sv);
-        }
-        gq = g;
-        have = true;
-      }
-      if (valid) {
-        *(uint32_t*)(q + (int64_t)p * (K / 2) + 4 * ch) = codes;
-        if ((lane & 3) == 0) s[(int64_t)p * (K / 32) + ch / 4] = (uint8_t)sc;
-        if (xk) *(u32x4*)(xk + ((int64_t)p * K + 8 * ch) * 2) = xv;
-      }
-    }
-  }
+  quantize_token_copies(x, x_bf16, t, K, ld_x, v, nk, dst, gam, q, s, xk);
 }
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
@@ -117,6 +127,109 @@ int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32
   if (T == 0) return MOESQ_OK;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x, slot_pos, k,
                      gamma, offsets, E, q, s, (uint8_t*)xk);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// Routing fused into the quantizer for decode-sized batches (T*k <= kRouteSingleMax, k <=
+// kFusedRouteMaxK): every workgroup (one per token) reads all T*k ids, builds the expert histogram
+// and its exclusive prefix in LDS, and places only its own token's k copies: row = offsets[e] +
+// the number of earlier slots with expert e, counted with wave ballots. The results equal those of
+// the routing kernels followed by quantize_kernel, with one launch and no dependent read of
+// slot_pos / offsets from global memory.
+__global__ __launch_bounds__(256) void route_quantize_kernel(
+    const int32_t* __restrict__ ids, int32_t k, int32_t E, const void* __restrict__ x, int x_bf16, int32_t K,
+    int64_t ld_x, const float* __restrict__ gamma, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos, int32_t* dev_status, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ s, uint8_t* __restrict__ xk) {
+  __shared__ int32_t hist[kMaxExpertsRoute];
+  __shared__ int32_t pos[kMaxExpertsRoute + 1];
+  __shared__ int32_t wsum[4];
+  __shared__ int32_t mine[kFusedRouteMaxK];
+  __shared__ int32_t rank[kFusedRouteMaxK];
+  __shared__ int32_t dst[kFusedRouteMaxK];
+  __shared__ float gam[kFusedRouteMaxK];
+  constexpr int R = kRouteSingleMax / 256;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t = blockIdx.x;
+  const int64_t n = (int64_t)gridDim.x * k;
+  const int64_t f0 = t * k;  // this token's first slot
+  const int nchunk = (K + 511) / 512;
+  float v[8];
+  load_chunk(x, x_bf16, t, ld_x, w * 64 + lane, w < nchunk && w * 64 + lane < K / 8, v);
+  int ev[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int64_t f = tid + (int64_t)r * 256;
+    ev[r] = f < n ? ids[f] : -1;
+  }
+  int e_my = -1;
+  float g_my = 0.0f;
+  if (tid < k) {
+    e_my = ids[f0 + tid];
+    if (e_my < 0 || e_my >= E) e_my = -1;
+    else g_my = gamma[e_my];
+  }
+  for (int i = tid; i < E; i += 256) hist[i] = 0;
+  if (tid < k) {
+    mine[tid] = e_my;
+    rank[tid] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; r++)
+    if (ev[r] >= 0 && ev[r] < E) atomicAdd(&hist[ev[r]], 1);
+  __syncthreads();
+  block_exclusive_scan<256>(hist, E, pos, wsum);
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= E; i += 256) {
+      offsets[i] = pos[i];
+      if (i < E) counts[i] = hist[i];
+    }
+  }
+  // rank of copy j = number of slots f < f0 + j routed to the same expert; only rounds holding
+  // such slots take part
+  const int nr = (int)((f0 + k + 255) / 256);
+  for (int j = 0; j < k; j++) {
+    const int ej = mine[j];  // uniform over the workgroup
+    if (ej < 0) continue;
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < R; r++)
+      if (r < nr) c += __builtin_popcountll(__ballot(ev[r] == ej && tid + (int64_t)r * 256 < f0 + j));
+    if (lane == 0 && c) atomicAdd(&rank[j], c);
+  }
+  __syncthreads();
+  if (tid < k) {
+    int32_t p = -1;
+    if (e_my >= 0) {
+      p = pos[e_my] + rank[tid];
+      sorted_slot[p] = (int32_t)(f0 + tid);
+    } else if (dev_status) {
+      *dev_status = MOESQ_ERR_INVALID_ARG;
+    }
+    slot_pos[f0 + tid] = p;
+    dst[tid] = p;
+    gam[tid] = g_my;
+  }
+  __syncthreads();
+  quantize_token_copies(x, x_bf16, t, K, ld_x, v, k, dst, gam, q, s, xk);
+}
+
+bool route_quantize_fused(int64_t T, int32_t k, int32_t E) {
+  return T > 0 && T * k <= kRouteSingleMax && k <= kFusedRouteMaxK && E <= kMaxExpertsRoute;
+}
+
+int launch_route_quantize(hipStream_t st, const int32_t* ids, int64_t T, int32_t k, int32_t E, const void* x,
+                          bool x_bf16, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status,
+                          uint8_t* q, uint8_t* s, void* xk) {
+  if (!route_quantize_fused(T, k, E)) {
+    const int rc = launch_route(st, ids, T * k, E, counts, offsets, sorted_slot, slot_pos, ws, dev_status);
+    if (rc != MOESQ_OK) return rc;
+    return launch_quantize(st, x, x_bf16, T, K, ld_x, slot_pos, k, gamma, offsets, E, q, s, xk);
+  }
+  hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, ids, k, E, x, (int)x_bf16, K, ld_x,
+                     gamma, counts, offsets, sorted_slot, slot_pos, dev_status, q, s, (uint8_t*)xk);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

@@ -218,6 +218,96 @@ def test_quantize_plain_and_bf16_and_zero():
     assert np.array_equal(host(q2), qo2) and np.array_equal(host(s2), so2)
 
 
+def _route_quantize_check(ids, x, E, ga, xk=False, bf16=False):
+    """moesq_route_quantize against the oracle's routing + dispatch quantizer, and byte for byte
+    against the two separate calls it replaces."""
+    ids = ids.astype(np.int32)
+    T, k = ids.shape
+    xd = dev(x)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        x = xd.float().cpu().numpy()
+    out = mq.moesq_route_quantize(dev(ids), E, xd, dev(ga), xk=True if xk else None)
+    rt, q, s = out[:3]
+    R = orc.route(ids, E)
+    for key in ("counts", "offsets", "sorted_slot", "slot_pos"):
+        assert np.array_equal(host(rt[key]), R[key]), key
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    rt2 = mq.moesq_route_permute(dev(ids), E)
+    q2, s2, xk2 = mq.moesq_quantize_act(xd, dev(ga), slot_pos=rt2["slot_pos"], k=k, offsets=rt2["offsets"], xk=True)
+    assert np.array_equal(host(q), host(q2)) and np.array_equal(host(s), host(s2))
+    if xk:
+        assert np.array_equal(host(out[3]).view(np.uint16), host(xk2).view(np.uint16))
+        assert np.array_equal(host(out[3]).view(np.uint16), _xk_reference(qo, so).view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "t_zipf", "t_mlp"])
+def test_route_quantize_bitexact(name):
+    c = single_case(name)
+    say("route+quantize", name, "T*k", c["ids"].size)
+    ga = c["ga"] * np.linspace(0.5, 2.0, c["E"]).astype(np.float32)   # distinct per-expert scales
+    _route_quantize_check(c["ids"], c["x"], c["E"], ga, xk=True)
+
+
+def test_route_quantize_edges():
+    """The single-launch limit (T*k = 2048) and one past it (two launches), k = 1 and k = 32, one
+    expert, ragged K (not a multiple of 512), bf16 input, skewed routing, and an empty batch."""
+    rng = np.random.default_rng(17)
+
+    def case(T, k, E, K, zipf=False, bf16=False):
+        say("route+quantize edge T", T, "k", k, "E", E, "K", K)
+        if zipf:
+            ids, _ = gen.route_zipf(5, T, E, k, 1.2, 0)
+        else:
+            ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        x = gen.student_t(11, gen.act_stream(T + K), T * K).reshape(T, K)
+        ga = (np.float32(orc.global_scale_of(x)) * np.linspace(0.7, 1.3, E)).astype(np.float32)
+        _route_quantize_check(ids, x, E, ga, xk=(K % 256 == 0), bf16=bf16)
+
+    case(256, 8, 128, 2048)            # T*k = 2048: the fused kernel's limit
+    case(257, 8, 128, 2048)            # one token more: routing kernels + quantizer
+    case(2, 32, 64, 7168)              # k = 32, K = 14 chunks of 512
+    case(40, 1, 1, 96)                 # one expert, ragged K
+    case(64, 8, 512, 1024, zipf=True)  # the routing path's largest E, skewed counts
+    case(24, 6, 60, 2048, bf16=True)
+    case(300, 40, 64, 64)              # k = 40 > 32: routing kernels + quantizer
+    # empty batch: offsets and counts still written (zeros)
+    cnt = torch.full((8,), 5, dtype=torch.int32, device=DEV)
+    off = torch.full((9,), 5, dtype=torch.int32, device=DEV)
+    empty = lambda *shape: torch.empty(shape, dtype=torch.int32, device=DEV)  # noqa: E731
+    rt = dict(counts=cnt, offsets=off, sorted_slot=empty(0), slot_pos=empty(0))
+    mq.moesq_route_quantize(empty(0, 2), 8, torch.zeros((0, 64), device=DEV), dev(np.ones(8, np.float32)), rt=rt)
+    assert not host(cnt).any() and not host(off).any()
+
+
+def test_route_quantize_invalid_ids():
+    """Ids outside [0, E): both paths drop the slot (slot_pos = -1), report MOESQ_ERR_INVALID_ARG and
+    write the valid copies to the same rows."""
+    say("route+quantize invalid ids")
+    ids = np.array([[0, 1], [5, 2], [1, -1], [3, 0]], np.int32)
+    E, K = 4, 64
+    x = gen.student_t(12, gen.act_stream(1), 4 * K).reshape(4, K)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q = torch.zeros((8, K // 2), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((8, K // 32), dtype=torch.uint8, device=DEV)
+    rt, q, s = mq.moesq_route_quantize(dev(ids), E, dev(x), dev(ga), q=q, s=s, dev_status=st)
+    assert int(host(st)[0]) == mq.ERR_INVALID_ARG
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rt2 = mq.moesq_route_permute(dev(ids), E, dev_status=st2)
+    q2 = torch.zeros_like(q)
+    s2 = torch.zeros_like(s)
+    mq.moesq_quantize_act(dev(x), dev(ga), slot_pos=rt2["slot_pos"], k=2, offsets=rt2["offsets"], q=q2, s=s2)
+    assert int(host(st2)[0]) == mq.ERR_INVALID_ARG
+    n_ok = int(host(rt2["offsets"])[-1])
+    assert n_ok == 6
+    for key in ("counts", "offsets", "slot_pos"):
+        assert np.array_equal(host(rt[key]), host(rt2[key])), key
+    assert np.array_equal(host(rt["sorted_slot"])[:n_ok], host(rt2["sorted_slot"])[:n_ok])
+    assert np.array_equal(host(q), host(q2)) and np.array_equal(host(s), host(s2))
+
+
 def test_global_scale_bitexact():
     say("global scale")
     for x in (gen.student_t(4, gen.act_stream(2), 300 * 256).reshape(300, 256),
@@ -540,3 +630,62 @@ def test_dense_kernel_on_unpacked_sparse_weights_matches_sparse_kernel():
         yd = host(mq.moesq_dense_grouped_gemm(Wdd, dev(qo), dev(so), dev(c["ga"]), dev(off), y_dtype=torch.float32,
                                               flags=fl))
         assert orc.rel_frobenius(yd, ys) <= 1e-5
+
+
+# ---------------------------------------------------------------- graph replay -----------------
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replays_match_eager_step(fused):
+    """The benchmark times HIP-graph replays of a whole step. Capture the t_mlp chain (route ->
+    scatter-quantize -> MLP -> combine; routing and quantization as two calls or as one) once,
+    replay it several times with eager work and synchronization in between, and compare every
+    replay with the eager result, bit for bit."""
+    cfg = gen.CONFIGS["t_mlp"]
+    say("graph replay t_mlp fused", fused)
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    x = dev(gen.activations(cfg, 0, T, H))
+    ids, wts = gen.routing(cfg)
+    ids_d, wts_d = dev(ids), dev(wts)
+    ga = mq.moesq_global_scale(x).expand(E).contiguous()
+    gh = torch.full((E,), cfg.gamma_h, dtype=torch.float32, device=DEV)
+    rows = T * k
+    rt = mq.moesq_route_permute(ids_d, E)
+    q = torch.empty((rows, H // 2), dtype=torch.uint8, device=DEV)
+    s = torch.empty((rows, H // 32), dtype=torch.uint8, device=DEV)
+    ws = mq.mlp_workspace(rows, I, False, DEV)
+    y2 = torch.empty((rows, H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        if fused:
+            mq.moesq_route_quantize(ids_d, E, x, ga, rt=rt, q=q, s=s)
+        else:
+            mq.moesq_route_permute(ids_d, E, rt["counts"], rt["offsets"], rt["sorted_slot"], rt["slot_pos"])
+            mq.moesq_quantize_act(x, ga, slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"], q=q, s=s)
+        mq.moesq_expert_mlp(W13, W2, q, s, ga, gh, rt["offsets"], y=y2, workspace=ws)
+        mq.moesq_unpermute_combine(y2, rt["slot_pos"], wts_d, out=out)
+
+    step()
+    ref = host(out.view(torch.int16)).copy()
+    ref_q = host(q).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        q.zero_()
+        rt["slot_pos"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out.view(torch.int16)), ref), i
+        assert np.array_equal(host(q), ref_q), i
+        _ = torch.ones(1024, device=DEV).sum()          # unrelated eager work between replays
