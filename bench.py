@@ -2,12 +2,14 @@
 """Benchmark of the paired-4:8 sparse NVFP4 MoE expert path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input, inputs resident in HBM:
-  single-projection workloads (c0, c1, c2): route/permute -> dispatch+quantize -> grouped GEMM;
-  decode layer (c3): route/permute -> quantize -> gate_up GEMM -> quantize -> down GEMM;
+  single-projection workloads (c0, c1, c2): route/permute + dispatch quantize -> grouped GEMM;
+  decode layer (c3): route/permute + quantize -> gate_up GEMM -> quantize -> down GEMM;
   MLP (c4): route/permute -> quantize -> gate_up GEMM + SwiGLU + requantize -> down GEMM -> combine.
-Each step is captured once in a HIP graph (one graph per rotation slot) and replayed. Weights and
-input batches rotate over several copies so that repeated steps do not find the weights in the
-last-level cache when the weight set would fit there (c1: 8 copies, about 1.1 GB).
+Weights and input batches rotate over R copies so that repeated steps do not find the weights in the
+last-level cache when the weight set would fit there (c1: 8 copies, about 1.1 GB). The R consecutive
+steps of one rotation are captured as one HIP graph, the way a decode server captures a sequence of
+MoE layers, so a graph launch is paid once per R steps; K timed steps are K // R replays of that
+graph plus single-step graphs for the remainder.
 
 Metric (paper Appendix D.2): TFLOP/s_eff = 2 * M * K * sum_e N_e / t with M the output rows and N_e
 the tokens of expert e, summed over the step's GEMMs. The roofline object reports the dominant
@@ -16,7 +18,7 @@ quantized activations, bf16 outputs) or algorithmic flops (prefill: the kept pro
 of the dense-equivalent count) per launch, divided by its mean duration measured with HIP events
 on the launch stream.
 
-Prints one JSON line. --gpus N > 1 exits: this build has no multi-GPU path.
+Prints one JSON line. --gpus N > 1 exits: the path runs on one GPU (no collective or sharded path).
 """
 import argparse
 import dataclasses
@@ -116,7 +118,7 @@ def summarize_pmc(argv):
         key = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if "gemm_tile_kernel" in k)
     else:
-        key = "gemm_decode_kernel" if any("decode" in k for k in per_kernel) else "gemm_tile_kernel"
+        key = "gemm_decode_kernel" if any("gemm_decode_kernel" in k for k in per_kernel) else "gemm_tile_kernel"
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     t = json.load(open(path)) if os.path.exists(path) else {}
@@ -229,15 +231,14 @@ class Workload:
         # routing + dispatch quantization (one launch for decode-sized batches)
         mq.moesq_route_quantize(sl["ids"], cfg.E, sl["x"], sl["ga"], rt=rt, q=sl["q"], s=sl["s"], xk=sl["xk"],
                                 workspace=sl["ws_route"])
-        if self.kind == "single":
+        if self.kind != "mlp":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
-        elif self.kind == "pair":
-            mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
+        if self.kind == "pair":
             mq.moesq_quantize_act(sl["x2"], sl["ga2"], slot_pos=rt["slot_pos"], k=cfg.k, offsets=rt["offsets"],
                                   q=sl["q2"], s=sl["s2"], xk=sl["xk2"])
             mq.moesq_grouped_gemm(self.W2c[r], sl["q2"], sl["s2"], sl["ga2"], rt["offsets"], y=sl["y2"],
                                   xk=sl["xk2"])
-        else:
+        if self.kind == "mlp":
             mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
                                 y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
             mq.moesq_unpermute_combine(sl["y2"], rt["slot_pos"], sl["wts"], out=sl["out"])
@@ -266,7 +267,18 @@ class Workload:
             with torch.cuda.graph(g):
                 self.step(r)
             self.graphs.append(g)
+        self.chain = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.chain):
+            for r in range(self.R):
+                self.step(r)
         torch.cuda.synchronize()
+
+    def run(self, n):
+        """Enqueue n consecutive steps: the R-step graph n // R times, then single-step graphs."""
+        for _ in range(n // self.R):
+            self.chain.replay()
+        for r in range(n % self.R):
+            self.graphs[r].replay()
 
     # ---- accounting ----
     def eff_flops_per_step(self):
@@ -470,7 +482,7 @@ def main(argv=None):
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (no collective or sharded path); "
+        print("bench.py: the path runs on one GPU only (no collective or sharded path); "
               "rerun with --gpus 1", file=sys.stderr)
         return 2
 
@@ -494,12 +506,10 @@ def main(argv=None):
     f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped)
     wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand)
     wl.capture()
-    for i in range(args.warmup):
-        wl.graphs[i % wl.R].replay()
+    wl.run(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        wl.graphs[i % wl.R].replay()
+    wl.run(args.steps)
     torch.cuda.synchronize()
     t = (time.perf_counter() - t0) / args.steps
     value = wl.eff_flops_per_step() / t / 1e12
@@ -542,7 +552,7 @@ def main(argv=None):
         "config": {"workload": "%s: %s (E=%d, K=%d, N=%d, T=%d, top-%d, %s routing%s)" % (
             args.workload, cfg.desc, cfg.E, cfg.K, cfg.N, cfg.T, cfg.k, cfg.routing,
             ", then K=%d N=%d" % (cfg.K2, cfg.N2) if cfg.N2 else ""),
-            "rows": wl.rows, "weight_copies": wl.R, "graph_replay": True,
+            "rows": wl.rows, "weight_copies": wl.R, "graph_replay": "%d steps per graph" % wl.R,
             "activation_operand": "f16 copy" if f16_operand else "nvfp4",
             "step_gbps_algorithmic": step_gbps},
         "roofline": roofline, "cpu_baseline": cpu,

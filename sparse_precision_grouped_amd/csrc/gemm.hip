@@ -390,8 +390,10 @@ MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<t
 // LDS (deterministic). Each wave keeps two super-steps of operands in flight (register double
 // buffering). Experts with more than 16 tokens loop over 16-token blocks.
 // grid (N / (16*MF*RG), E).
+// Weight streaming here is bound by the bytes a CU keeps in flight, so the register budget is capped
+// at 168 VGPRs for 3 waves per SIMD (no spills; the dense f16-operand control needs more and keeps 2).
 template <int MF, int KS, int RG, bool XK, bool DENSE>
-__global__ __launch_bounds__(64 * KS * RG) void gemm_decode_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(DENSE && XK ? 1 : 3, DENSE && XK ? 8 : 3))) void gemm_decode_kernel(GemmArgs a) {
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
   const int off = a.offsets[e];
