@@ -4,7 +4,8 @@
 A step is one pass of the whole path over one batch of synthetic input, inputs resident in HBM:
   single-projection workloads (c0, c1, c2): route/permute + dispatch quantize -> grouped GEMM;
   decode layer (c3): route/permute + quantize -> gate_up GEMM -> quantize -> down GEMM;
-  MLP (c4): route/permute -> quantize -> gate_up GEMM + SwiGLU + requantize -> down GEMM -> combine.
+  MLP (c4 prefill, c3_mlp decode from bf16 tokens): route/permute + quantize -> gate_up GEMM + SwiGLU +
+    requantize -> down GEMM -> combine.
 Weights and input batches rotate over R copies so that repeated steps do not find the weights in the
 last-level cache when the weight set would fit there (c1: 8 copies, about 1.1 GB). The R consecutive
 steps of one rotation are captured as one HIP graph, the way a decode server captures a sequence of
@@ -169,6 +170,8 @@ class Workload:
             cr = dataclasses.replace(cfg, seed=cfg.seed + 7919 * r)
             ids, wts = gen.routing(cr)
             x = torch.from_numpy(gen.activations(cr, 0, T, cfg.K)).to(dev)
+            if cfg.x_bf16:
+                x = x.to(torch.bfloat16)
             sl = dict(ids=torch.from_numpy(ids).to(dev), wts=torch.from_numpy(wts).to(dev), x=x,
                       counts_host=np.bincount(ids.ravel(), minlength=E))
             g = mq.moesq_global_scale(x)
@@ -292,7 +295,16 @@ class Workload:
     def roofline_units(self):
         """(bound, algorithmic units per dominant launch averaged over the slots, unit, peak, kernel)."""
         cfg = self.cfg
-        decode = self.kind != "mlp" and self.rows <= 16 * cfg.E
+        decode = self.rows <= 16 * cfg.E
+        if decode and self.kind == "mlp":
+            # both weight-streaming GEMMs: the two projections' weights of the experts with tokens, the
+            # routed rows' NVFP4 codes, the intermediate h codes written once and read once, bf16 outputs
+            I = cfg.N // 2
+            b = np.mean([gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N, cfg.K, self.rows, cfg.E,
+                                    out_bytes=(I / 2 + I / 32) / cfg.N) +
+                         gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N2, cfg.K2, self.rows, cfg.E)
+                         for sl in self.slots])
+            return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
         if decode:
             b = np.mean([gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N, cfg.K, self.rows, cfg.E)
                          for sl in self.slots])
@@ -469,13 +481,14 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "c3_mlp"])
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--operand", choices=["auto", "nvfp4", "f16"], default="auto",
                     help="activation operand of the GEMMs: NVFP4 codes decoded in the kernel, or the quantizer's "
-                         "f16 copy; auto = f16 for weight-streaming (decode) workloads, NVFP4 for tiled ones")
+                         "f16 copy; auto = f16 for single-projection weight-streaming (decode) workloads, NVFP4 "
+                         "otherwise")
     ap.add_argument("--sweep", choices=sorted(SWEEP_LAYERS) + ["all"],
                     help="the pages' G x N kernel sweep on one layer shape (one JSON line per point)")
     ap.add_argument("--sweep-kernel", choices=["auto", "decode", "tiled"], default="auto")
@@ -513,6 +526,8 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     cfgw = gen.CONFIGS[args.workload]
+    # the f16 copy pays off in the single-projection weight-streaming kernel; the MLP kernels keep the
+    # NVFP4 codes (the MLP epilogue's registers leave the f16-operand form at 2 waves per SIMD)
     decode_shaped = not cfgw.mlp and cfgw.T * cfgw.k <= 16 * cfgw.E
     f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped)
     wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand)

@@ -1,8 +1,10 @@
 """Workload recipes: shapes, distributions and seeds of the synthetic inputs.
 
-The five named workloads follow the layer shapes the pages benchmark (Qwen3-30B-A3B
+The five named workloads c0-c4 follow the layer shapes the pages benchmark (Qwen3-30B-A3B
 gate_up 1536x2048, Kimi-K2.5 gate_up 4096x7168 and down 7168x2048, Appendix D.2 Table 8)
-with seeded synthetic tokens and weights; the extra small cases exist for parity tests.
+with seeded synthetic tokens and weights; c3_mlp is the decode-size layer on the c3 shapes timed
+from bf16 tokens to bf16 outputs (Table 11 times such layers); the extra small cases exist for
+parity tests.
 """
 from dataclasses import dataclass, field
 
@@ -26,6 +28,7 @@ class Config:
     N2: int = 0
     K2: int = 0
     mlp: bool = False      # gate_up -> SiLU(gate)*up -> requant -> down -> combine
+    x_bf16: bool = False   # tokens handed over in bf16 (else fp32)
     gamma_h: float = 0.0   # static tensor scale of the intermediate h (MLP only): 448 / (amax_h / 6) for a
                            # calibrated amax_h (t_mlp: 2.0, c4: 64.0)
     desc: str = ""
@@ -46,6 +49,11 @@ CONFIGS = {
                  N2=7168, K2=2048, desc="Kimi-K2.5 gate_up + down, decode"),
     "c4": Config("c4", E=384, K=7168, N=4096, T=8192, k=8, routing="zipf", act_dist="student_t", seed=1238,
                  N2=7168, K2=2048, mlp=True, gamma_h=42.0, desc="Kimi-K2.5 routed-expert MLP, prefill"),
+    # the decode-size routed-expert MLP on the c3 shapes, bf16 tokens in and out (gamma_h: the c4
+    # calibration, same weight and token distributions)
+    "c3_mlp": Config("c3_mlp", E=384, K=7168, N=4096, T=64, k=8, routing="uniform", act_dist="student_t",
+                     seed=1239, N2=7168, K2=2048, mlp=True, gamma_h=42.0, x_bf16=True,
+                     desc="Kimi-K2.5 routed-expert MLP, decode"),
     # small cases for parity tests
     "t_mlp": Config("t_mlp", E=4, K=256, N=512, T=64, k=2, routing="uniform", act_dist="student_t", seed=77,
                     N2=256, K2=256, mlp=True, gamma_h=1344.0, desc="tiny MLP (H=256, I=256)"),

@@ -179,6 +179,9 @@ int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, c
  *   region starting on a 256-byte boundary, h_q [rows][I/2], h_s [rows][I/32] and h_k [rows][I] (the
  *   f16 copy of the requantized h read by the down GEMM). With MOESQ_F_DUMP_GATEUP the size is
  *   moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and the fp32 gate_up outputs [rows][2I] follow.
+ * Kernels: with rows <= 16 E both GEMMs stream the weights (the gate_up epilogue computes SwiGLU and
+ * the requantization per 32 intermediate columns), otherwise both are tiled; MOESQ_F_FORCE_DECODE /
+ * MOESQ_F_FORCE_PREFILL pick one. Both produce the same results up to fp32 accumulation order.
  * Requires H % 256 == 0, I % 256 == 0.
  */
 int moesq_expert_mlp(void *stream, const moesq_weights *W13, const moesq_weights *W2, const uint8_t *q,

@@ -174,13 +174,17 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
   a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0;
   a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk; a.dump = dumpp;
-  rc = launch_gemm_variant((hipStream_t)stream, a, rows, 1);
+  // few tokens per expert: both GEMMs stream the weights; otherwise both are tiled
+  int variant = rows <= (int64_t)16 * W13->E ? 0 : 1;
+  if (flags & MOESQ_F_FORCE_DECODE) variant = 0;
+  if (flags & MOESQ_F_FORCE_PREFILL) variant = 1;
+  rc = launch_gemm_variant((hipStream_t)stream, a, rows, variant);
   if (rc != MOESQ_OK) return rc;
   GemmArgs b{};
   b.kl = W2->kl; b.gscale = W2->gscale;
   b.q = hq; b.s = hs; b.xk = hk; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
   b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16;
-  return launch_gemm_variant((hipStream_t)stream, b, rows, 1);
+  return launch_gemm_variant((hipStream_t)stream, b, rows, variant);
 }
 
 int moesq_unpermute_combine(void* stream, const void* y_sorted, int32_t y_dtype, const int32_t* slot_pos,

@@ -361,27 +361,89 @@ MOESQ_DEV void dense_superstep_xk(f32x4 (&acc)[MF], const DWStage<MF>& w, const 
 MOESQ_DEV uint32_t expert_dense_bytes(int N, int K) { return (uint32_t)(N / 64) * (uint32_t)(K / 256) * kDenseUnitBytes; }
 
 // Weight stage of the decode kernel: the sparse layout (WStage) or the dense control (DWStage).
-template <int MF, bool DENSE>
+template <int MF, bool DENSE, bool SPLIT = false>
 struct WS;
-template <int MF>
-struct WS<MF, false> {
+template <int MF, bool SPLIT>
+struct WS<MF, false, SPLIT> {
   WStage<MF> w;
-  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w<MF, false>(w, rw, src, lane, ss); }
+  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w<MF, SPLIT>(w, rw, src, lane, ss); }
 };
 template <int MF>
-struct WS<MF, true> {
+struct WS<MF, true, false> {
   DWStage<MF> w;
   MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
 };
 
-template <int MF>
-MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false>& w, const DStage<false>& x) { mma_superstep_x(acc, w.w, x.x); }
-template <int MF>
-MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false>& w, const DStage<true>& x) { mma_superstep_xk(acc, w.w, x.x); }
+template <int MF, bool SPLIT>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false, SPLIT>& w, const DStage<false>& x) { mma_superstep_x(acc, w.w, x.x); }
+template <int MF, bool SPLIT>
+MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, false, SPLIT>& w, const DStage<true>& x) { mma_superstep_xk(acc, w.w, x.x); }
 template <int MF>
 MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<false>& x) { dense_superstep_x(acc, w.w, x.x); }
 template <int MF>
 MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<true>& x) { dense_superstep_xk(acc, w.w, x.x); }
+
+// MLP gate_up epilogue for one token (permuted row p; tv: the row is a real token): g0, g1 are the two
+// gate fragments and u0, u1 the matching up fragments of the 32 intermediate columns [ib, ib + 32);
+// lane (r16, cc) holds columns 16 f + 4 cc .. + 3 of fragment f. h = SiLU(g) * u in fp32 (the optional
+// fp32 dump keeps g and u), then the NVFP4 requantization of the 32-block with the expert's gamma_h
+// (amax over the 4 lanes cc = 0..3: xor 16, 32), and the h codes, block scale and optional f16 copy.
+MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float gh, f32x4 g0,
+                                  f32x4 g1, f32x4 u0, f32x4 u1) {
+  const int N = a.N, I = N / 2;
+  const f32x4 gg[2] = {g0, g1}, uu[2] = {u0, u1};
+  float h[8];
+#pragma unroll
+  for (int f = 0; f < 2; f++) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float g = gg[f][r] * alpha;
+      const float u = uu[f][r] * alpha;
+      h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
+    }
+    if (tv && a.dump) {
+      const int64_t rowo = p * N;
+      float4 gv, uv;
+      gv.x = gg[f][0] * alpha; gv.y = gg[f][1] * alpha; gv.z = gg[f][2] * alpha; gv.w = gg[f][3] * alpha;
+      uv.x = uu[f][0] * alpha; uv.y = uu[f][1] * alpha; uv.z = uu[f][2] * alpha; uv.w = uu[f][3] * alpha;
+      *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
+      *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
+    }
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
+  am = __builtin_fmaxf(am, __shfl_xor(am, 16));
+  am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+  const float t = gh * am;
+  const float uq = t / 6.0f;
+  const uint32_t sc = e4m3_encode(uq);
+  const float sv = e4m3_value(sc) / gh;
+  if (tv) {
+    f16x2 s01, s01b;
+    e4m3_pair_f16x2(sc, s01, s01b);
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+      uint32_t codes = 0u;
+      if (sv != 0.0f) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) codes |= e2m1_encode(h[4 * f + r] / sv) << (4 * r);
+      }
+      const int i0 = ib + 16 * f + 4 * cc;  // 4 consecutive intermediate columns: half (cc & 1) of an 8-group
+      *(uint16_t*)(a.h_q + p * (I / 2) + i0 / 2) = (uint16_t)codes;
+      if (a.h_k) {
+        // f16 copy in the de-interleaved group order (a0,a2,a4,a6,a1,a3,a5,a7): this lane holds
+        // a[4h..4h+3] (h = cc & 1) and writes words h ((a4h, a4h+2)) and 2 + h ((a4h+1, a4h+3)).
+        const uint32_t v01 = f16x2_bits(MOESQ_CVT_FP4(codes, 0) * s01);  // (v0, v1)
+        const uint32_t v23 = f16x2_bits(MOESQ_CVT_FP4(codes, 1) * s01);  // (v2, v3)
+        uint8_t* grp = (uint8_t*)a.h_k + (p * I + (i0 & ~7)) * 2;
+        *(uint32_t*)(grp + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x05040100u);
+        *(uint32_t*)(grp + 8 + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x07060302u);
+      }
+    }
+    if (cc == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
+  }
+}
 
 // ============================================================================ decode kernel =====
 // Weight streaming for few tokens per expert. A workgroup of KS * RG waves covers 16*MF*RG weight rows
@@ -390,10 +452,16 @@ MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<t
 // LDS (deterministic). Each wave keeps two super-steps of operands in flight (register double
 // buffering). Experts with more than 16 tokens loop over 16-token blocks.
 // grid (N / (16*MF*RG), E).
+// MLP (the gate_up GEMM of the routed-expert MLP, N = 2I): workgroup x takes gate rows [32 x, +32) and
+// the matching up rows [I + 32 x, +32) (fragments 0-1 and 2-3), so after the K reduction one wave holds
+// the gate and up sums of 32 intermediate columns, one 32-block per token: SwiGLU and the NVFP4
+// requantization of h run in the same epilogue as the tiled kernel's.
 // Weight streaming here is bound by the bytes a CU keeps in flight, so the register budget is capped
-// at 168 VGPRs for 3 waves per SIMD (no spills; the dense f16-operand control needs more and keeps 2).
-template <int MF, int KS, int RG, bool XK, bool DENSE>
-__global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(DENSE && XK ? 1 : 3, DENSE && XK ? 8 : 3))) void gemm_decode_kernel(GemmArgs a) {
+// at 168 VGPRs for 3 waves per SIMD (no spills; the f16-operand forms of the dense control and of the
+// MLP epilogue need more and keep 2).
+template <int MF, int KS, int RG, bool XK, bool DENSE, bool MLP = false>
+__global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((DENSE || MLP) && XK ? 1 : 3, (DENSE || MLP) && XK ? 8 : 3))) void gemm_decode_kernel(GemmArgs a) {
+  static_assert(!MLP || (MF == 4 && RG == 1 && KS > 1 && !DENSE), "MLP epilogue: 32 gate + 32 up rows per workgroup");
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
   const int off = a.offsets[e];
@@ -407,10 +475,18 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(DE
   const uint32_t ekl = DENSE ? expert_dense_bytes(N, K) : expert_kl_bytes(N, K);
   const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
   WSrc src;
-  src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * (DENSE ? kDenseUnitBytes : kGroupBytes);
-  src.j0 = rb0 % 4;
-  src.g1 = 0;
-  src.j1 = 0;
+  if (MLP) {
+    const int rgate = 2 * blockIdx.x, rup = N / 32 + 2 * blockIdx.x;  // 16-row blocks of the gate / up rows
+    src.g0 = (uint32_t)(rgate / 4) * (uint32_t)nss * kGroupBytes;
+    src.j0 = rgate % 4;
+    src.g1 = (uint32_t)(rup / 4) * (uint32_t)nss * kGroupBytes;
+    src.j1 = rup % 4;
+  } else {
+    src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * (DENSE ? kDenseUnitBytes : kGroupBytes);
+    src.j0 = rb0 % 4;
+    src.g1 = 0;
+    src.j1 = 0;
+  }
   const rsrc_t rq = XK ? make_rsrc((const uint8_t*)a.xk + (size_t)off * K * 2, (uint32_t)ne * K * 2)
                       : make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
   const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
@@ -426,7 +502,7 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(DE
     const uint32_t voq = (uint32_t)tok * (K / 2) + 32u * (c >> 1) + 4u * (c & 1);
     const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
     const uint32_t vox = (uint32_t)tok * (uint32_t)(2 * K) + 16u * (8u * (c >> 1) + (c & 1));
-    WS<MF, DENSE> w0, w1;
+    WS<MF, DENSE, MLP> w0, w1;
     DStage<XK> x0, x1;
     int ss = kw;
     if (ss < nss) {
@@ -456,11 +532,24 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(DE
 #pragma unroll
       for (int f = 0; f < MF; f++) red[rg * KS + kw][f][lane] = acc[f];
       __syncthreads();
-      for (int f = kw; f < MF; f += KS) {
-        f32x4 sum = red[rg * KS][f][lane];
+      if (MLP) {
+        if (kw == 0) {
+          f32x4 sum[4];
 #pragma unroll
-        for (int v = 1; v < KS; v++) sum = sum + red[rg * KS + v][f][lane];
-        if (tv) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
+          for (int f = 0; f < 4; f++) {
+            sum[f] = red[0][f][lane];
+#pragma unroll
+            for (int v = 1; v < KS; v++) sum[f] = sum[f] + red[v][f][lane];
+          }
+          mlp_epilogue_token(a, off + tok, tv, 32 * blockIdx.x, c, alpha, a.gamma_h[e], sum[0], sum[1], sum[2], sum[3]);
+        }
+      } else {
+        for (int f = kw; f < MF; f += KS) {
+          f32x4 sum = red[rg * KS][f][lane];
+#pragma unroll
+          for (int v = 1; v < KS; v++) sum = sum + red[rg * KS + v][f][lane];
+          if (tv) store4(a.y, (int64_t)(off + tok) * N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
+        }
       }
       __syncthreads();
     }
@@ -656,7 +745,7 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
 template <int MF>
 struct TileCtx {
   int e, off, ne, tb, rb, nv;
-  float alpha;
+  float alpha, gh;
   rsrc_t rw;          // expert's weights (kernel layout)
   WSrc src;           // the wave's m-fragments in the kernel layout
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
@@ -698,6 +787,7 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
     c.src.j1 = 0;
   }
   c.alpha = 1.0f / (a.gscale[c.e] * a.gamma_a[c.e]);
+  c.gh = MLP ? a.gamma_h[c.e] : 0.0f;
   if (XK) {
     c.rq = make_rsrc((const uint8_t*)a.xk + (size_t)c.off * K * 2, (uint32_t)c.ne * K * 2);
     c.rs = c.rq;
@@ -798,68 +888,12 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
     }
     return;
   }
-  const int I = N / 2;
   const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
-  const float gh = a.gamma_h[c.e];
 #pragma unroll
   for (int n = 0; n < NF; n++) {
     if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
-    const bool tv = tok < c.ne;
-    float h[8];
-#pragma unroll
-    for (int f = 0; f < 2; f++) {
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const float g = acc[f][n][r] * alpha;
-        const float u = acc[f + 2][n][r] * alpha;
-        h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
-      }
-      if (tv && a.dump) {
-        const int64_t rowo = (int64_t)(c.off + tok) * N;
-        float4 gv, uv;
-        gv.x = acc[f][n][0] * alpha; gv.y = acc[f][n][1] * alpha; gv.z = acc[f][n][2] * alpha; gv.w = acc[f][n][3] * alpha;
-        uv.x = acc[f + 2][n][0] * alpha; uv.y = acc[f + 2][n][1] * alpha; uv.z = acc[f + 2][n][2] * alpha;
-        uv.w = acc[f + 2][n][3] * alpha;
-        *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
-        *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
-      }
-    }
-    // requantize: the 32-block of this token is spread over the 4 lanes cc = 0..3 (xor 16, 32)
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
-    am = __builtin_fmaxf(am, __shfl_xor(am, 16));
-    am = __builtin_fmaxf(am, __shfl_xor(am, 32));
-    const float t = gh * am;
-    const float uq = t / 6.0f;
-    const uint32_t sc = e4m3_encode(uq);
-    const float sv = e4m3_value(sc) / gh;
-    if (tv) {
-      const int64_t p = c.off + tok;
-      f16x2 s01, s01b;
-      e4m3_pair_f16x2(sc, s01, s01b);
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-        uint32_t codes = 0u;
-        if (sv != 0.0f) {
-#pragma unroll
-          for (int r = 0; r < 4; r++) codes |= e2m1_encode(h[4 * f + r] / sv) << (4 * r);
-        }
-        const int i0 = ib + 16 * f + 4 * cc;  // 4 consecutive intermediate columns: half (cc & 1) of an 8-group
-        *(uint16_t*)(a.h_q + p * (I / 2) + i0 / 2) = (uint16_t)codes;
-        if (a.h_k) {
-          // f16 copy in the de-interleaved group order (a0,a2,a4,a6,a1,a3,a5,a7): this lane holds
-          // a[4h..4h+3] (h = cc & 1) and writes words h ((a4h, a4h+2)) and 2 + h ((a4h+1, a4h+3)).
-          const uint32_t v01 = f16x2_bits(MOESQ_CVT_FP4(codes, 0) * s01);  // (v0, v1)
-          const uint32_t v23 = f16x2_bits(MOESQ_CVT_FP4(codes, 1) * s01);  // (v2, v3)
-          uint8_t* grp = (uint8_t*)a.h_k + (p * I + (i0 & ~7)) * 2;
-          *(uint32_t*)(grp + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x05040100u);
-          *(uint32_t*)(grp + 8 + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x07060302u);
-        }
-      }
-      if (cc == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
-    }
+    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, c.gh, acc[0][n], acc[1][n], acc[2][n], acc[3][n]);
   }
 }
 
@@ -988,7 +1022,13 @@ static bool launch_decode(hipStream_t st, const GemmArgs& a) {
 
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
   if (rows == 0) return MOESQ_OK;
-  if (variant == 0) {
+  if (variant == 0 && a.gamma_h) {
+    // MLP gate_up by weight streaming: 32 gate + 32 up rows per workgroup
+    if (a.xk)
+      hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, true>), dim3(a.N / 64, a.E), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, false, false, true>), dim3(a.N / 64, a.E), dim3(256), 0, st, a);
+  } else if (variant == 0) {
     bool ok = false;
     switch (decode_variant_default()) {
       case 2: ok = launch_decode<4, 1, 4>(st, a); break;

@@ -65,7 +65,7 @@ int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, in
 
 // Grouped GEMM: picks the decode (weight-streaming) or the prefill (tiled) kernel from rows / E.
 int launch_gemm(hipStream_t st, const GemmArgs& a, int64_t rows);
-// variant 0 = decode (weight streaming), 1 = prefill (tiled); the MLP epilogue needs variant 1.
+// variant 0 = decode (weight streaming; with gamma_h the MLP gate_up epilogue), 1 = prefill (tiled).
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
 
 int launch_combine(hipStream_t st, const void* y, bool y_bf16, const int32_t* slot_pos, const float* w, int64_t T,

@@ -422,9 +422,13 @@ def test_combine_parity(ydt):
 
 
 # ---------------------------------------------------------------- MLP --------------------------
-def test_mlp_parity_tiny():
+@pytest.mark.parametrize("kernel", ["tiled", "streaming"])
+def test_mlp_parity_tiny(kernel):
+    """The routed-expert MLP on both kernel families (t_mlp has 32 rows per expert: tiled by default;
+    MOESQ_F_FORCE_DECODE runs both GEMMs by weight streaming with the SwiGLU + requant epilogue)."""
     cfg = gen.CONFIGS["t_mlp"]
-    say("mlp t_mlp")
+    say("mlp t_mlp", kernel)
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else 0
     E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
     w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
     w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
@@ -439,9 +443,9 @@ def test_mlp_parity_tiny():
     M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"])
     rows = int(R["offsets"][-1])
     y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
-                                flags=mq.F_DUMP_GATEUP)
+                                flags=mq.F_DUMP_GATEUP | kf)
     y_xk, _ = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]),
-                                  y_dtype=torch.float32, xk=dev(_xk_reference(qo, so)))
+                                  y_dtype=torch.float32, xk=dev(_xk_reference(qo, so)), flags=kf)
     assert np.array_equal(host(y_xk), host(y))   # same operands, same kernel order of operations
     hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
     # gate_up GEMM stage
@@ -459,25 +463,32 @@ def test_mlp_parity_tiny():
     say("mlp y2 rel-Frobenius", err, "h code mismatches", int(diff.sum()))
     assert err <= 1e-2
     # down GEMM alone on the oracle's h codes: identical operands
-    yd = mq.moesq_grouped_gemm(W2, dev(M["hq"]), dev(M["hs"]), dev(gh), dev(R["offsets"]), y_dtype=torch.float32)
+    yd = mq.moesq_grouped_gemm(W2, dev(M["hq"]), dev(M["hs"]), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
+                               flags=kf)
     assert orc.rel_frobenius(host(yd), M["y2"]) <= GEMM_TOL
     out = mq.moesq_unpermute_combine(y, dev(R["slot_pos"]), dev(wts), out_dtype=torch.float32)
     ref = orc.combine(M["y2"], R["slot_pos"], wts)
     assert orc.rel_frobenius(host(out), ref) <= 1e-2
 
 
-def test_mlp_parity_c4_full_size():
-    """The Kimi-shaped routed-expert MLP at full size (E=384, H=7168, I=2048, T=8192, top-8, Zipf),
-    in the benchmark's launch configuration (f16 operand copy from the quantizer). Stage by stage
-    on the rows of sampled experts: activation codes (all rows, bit-exact), gate_up (fp32 dump),
-    requantized h, the down GEMM on the oracle's h codes, the end-to-end chain, and the combine."""
-    cfg = gen.CONFIGS["c4"]
+@pytest.mark.parametrize("name", ["c4", "c3_mlp"])
+def test_mlp_parity_full_size(name):
+    """The Kimi-shaped routed-expert MLP at full size (E=384, H=7168, I=2048, top-8): c4 (T=8192, Zipf,
+    tiled kernels) and c3_mlp (T=64, uniform, bf16 tokens, weight-streaming kernels), with the f16
+    operand copy from the quantizer. Stage by stage on the rows of sampled experts: activation codes
+    (all rows, bit-exact), gate_up (fp32 dump), requantized h, the down GEMM on the oracle's h codes,
+    the end-to-end chain, and the combine."""
+    cfg = gen.CONFIGS[name]
     E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
-    say("mlp c4 full size: weights")
+    say("mlp", name, "full size: weights")
     W13, _ = device_weights(cfg, 0, E, I2, H, host_draw=False)
     W2, _ = device_weights(cfg, 1, E, H, I, host_draw=False)
-    say("mlp c4: inputs")
+    say("mlp", name, ": inputs")
     x = gen.activations(cfg, 0, T, H)
+    xd = dev(x)
+    if cfg.x_bf16:  # the oracle quantizes the same bf16 values
+        xd = xd.to(torch.bfloat16)
+        x = xd.float().cpu().numpy()
     ids, wts = gen.routing(cfg)
     R = orc.route(ids, E)
     off = R["offsets"]
@@ -485,17 +496,16 @@ def test_mlp_parity_c4_full_size():
     ga = np.full(E, orc.global_scale_of(x), np.float32)
     gh = np.full(E, cfg.gamma_h, np.float32)
     qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, off, ga)
-    say("mlp c4: quantize on the device")
+    say("mlp", name, ": quantize on the device")
     rt = mq.moesq_route_permute(dev(ids), E)
-    q, s, xk = mq.moesq_quantize_act(dev(x), dev(ga), slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"],
-                                     xk=True)
+    q, s, xk = mq.moesq_quantize_act(xd, dev(ga), slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"], xk=True)
     assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
-    say("mlp c4: expert MLP")
+    say("mlp", name, ": expert MLP")
     y, ws = mq.moesq_expert_mlp(W13, W2, q, s, dev(ga), dev(gh), rt["offsets"], y_dtype=torch.float32,
                                 flags=mq.F_DUMP_GATEUP, xk=xk)
     hq, hs, dump = mq.mlp_workspace_views(ws, rows_all, I, dump=True)
     rows, experts = sample_expert_rows(off, n_experts=3, per_expert=32)
-    say("mlp c4: oracle on experts", experts, "rows", rows.size)
+    say("mlp", name, ": oracle on experts", experts, "rows", rows.size)
     W13o = OracleWeights(cfg, 0, E, I2, H).ensure(experts).as_dict()
     W2o = OracleWeights(cfg, 1, E, H, I).ensure(experts).as_dict()
     M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, off, rows)
@@ -518,7 +528,7 @@ def test_mlp_parity_c4_full_size():
     assert errd <= GEMM_TOL
     del y, ws, dump, yd
     # combine at full size on a generated expert output, sampled tokens
-    say("mlp c4: combine")
+    say("mlp", name, ": combine")
     y2 = gen.normal(5, gen.act_stream(12), rows_all * H).reshape(rows_all, H)
     yt = torch.from_numpy(y2).to(torch.bfloat16)
     out = host(mq.moesq_unpermute_combine(yt.to(DEV), rt["slot_pos"], dev(wts), out_dtype=torch.float32))
