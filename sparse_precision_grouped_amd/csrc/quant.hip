@@ -143,6 +143,7 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
     uint8_t* __restrict__ s, uint8_t* __restrict__ xk) {
   __shared__ int32_t hist[kMaxExpertsRoute];
   __shared__ int32_t pos[kMaxExpertsRoute + 1];
+  __shared__ float gam_all[kMaxExpertsRoute];  // all tensor scales: no load that waits on an id
   __shared__ int32_t wsum[4];
   __shared__ int32_t mine[kFusedRouteMaxK];
   __shared__ int32_t rank[kFusedRouteMaxK];
@@ -163,13 +164,14 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
     ev[r] = f < n ? ids[f] : -1;
   }
   int e_my = -1;
-  float g_my = 0.0f;
   if (tid < k) {
     e_my = ids[f0 + tid];
     if (e_my < 0 || e_my >= E) e_my = -1;
-    else g_my = gamma[e_my];
   }
-  for (int i = tid; i < E; i += 256) hist[i] = 0;
+  for (int i = tid; i < E; i += 256) {
+    hist[i] = 0;
+    gam_all[i] = gamma[i];
+  }
   if (tid < k) {
     mine[tid] = e_my;
     rank[tid] = 0;
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
     }
     slot_pos[f0 + tid] = p;
     dst[tid] = p;
-    gam[tid] = g_my;
+    gam[tid] = e_my >= 0 ? gam_all[e_my] : 0.0f;
   }
   __syncthreads();
   quantize_token_copies(x, x_bf16, t, K, ld_x, v, k, dst, gam, q, s, xk);
