@@ -70,7 +70,12 @@ extern "C" {
  *   mask   [E][N][K/16] 4 bits per chunk, bit i = byte i kept, exactly two bits set,
  *                       low nibble = lower-K chunk
  *   scale  [E][N][K/32] UE4M3 block-scale codes
- *   gscale [E]          fp32 tensor scale gamma_w,e of Eq. 5
+ *   gscale [E]          fp32 tensor scale gamma_w,e of Eq. 5 (gscale_split = 0), or
+ *          [E][2]       with gscale_split = 1: the scales of rows [0, N/2) and [N/2, N), for a gate_up
+ *                       weight whose gate and up projections are separate linears with their own
+ *                       Eq. 5 scale (the model card's checkpoint); needs N % 128 == 0. Compressing the
+ *                       [2E][N/2][K] view of the same weights produces it: the byte layout of packed,
+ *                       mask and scale is the same.
  *   kl                  the same weights in the kernel layout (moesq_prepack_weights), read by the
  *                       GEMM calls; moesq_kernel_layout_bytes(E, N, K) bytes, 16-byte aligned
  * The GEMM calls read only kl and gscale (packed/mask/scale may then be NULL); the storage calls
@@ -84,6 +89,7 @@ typedef struct {
   const uint8_t *scale;
   const float *gscale;
   const uint8_t *kl;
+  int32_t gscale_split;  /* 0 or 1, see gscale */
 } moesq_weights;
 
 /*

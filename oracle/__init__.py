@@ -186,6 +186,27 @@ def compress(w):
     return dict(packed=packed, mask=mask, scale=scale, gscale=gscale, E=E, N=N, K=K)
 
 
+def compress_split(w):
+    """A gate_up weight w [E, N, K] whose row halves [0, N/2) and [N/2, N) are separate linears, each
+    with its own Eq. 5 tensor scale (the model card's checkpoint keeps gate and up apart): every half
+    is compressed as a tensor of its own. -> dict as compress() with gscale [E, 2] and gsplit."""
+    w = _c(w, np.float32)
+    E, N, K = w.shape
+    W = compress(w.reshape(2 * E, N // 2, K))
+    return dict(packed=W["packed"].reshape(E, N, K // 4), mask=W["mask"].reshape(E, N, K // 16),
+                scale=W["scale"].reshape(E, N, K // 32), gscale=W["gscale"].reshape(E, 2), E=E, N=N, K=K,
+                gsplit=True)
+
+
+def split_halves(W):
+    """The two linears of split weights as weights of their own: [gate rows, up rows]."""
+    n2 = W["N"] // 2
+    return [dict(packed=_c(W["packed"][:, h * n2:(h + 1) * n2], np.uint8),
+                 mask=_c(W["mask"][:, h * n2:(h + 1) * n2], np.uint8),
+                 scale=_c(W["scale"][:, h * n2:(h + 1) * n2], np.uint8),
+                 gscale=_c(W["gscale"][:, h], np.float32), E=W["E"], N=n2, K=W["K"]) for h in (0, 1)]
+
+
 def dequant_weights(W, e):
     """Dequantized weights of expert e without the tensor scale: e2m1 * e4m3, [N, K] double."""
     dense = unpack(W["packed"][e], W["mask"][e])
@@ -220,7 +241,10 @@ def dispatch_quantize(x, sorted_slot, k, offsets, gamma):
 
 
 def grouped_gemm(W, q, s, gamma_a, offsets, row_list=None):
-    """Rows of Y (double) for permuted rows row_list (default: all rows)."""
+    """Rows of Y (double) for permuted rows row_list (default: all rows). Split weights (separate gate
+    and up linears) are two grouped GEMMs whose outputs sit side by side."""
+    if W.get("gsplit"):
+        return np.concatenate([grouped_gemm(Wh, q, s, gamma_a, offsets, row_list) for Wh in split_halves(W)], axis=1)
     offsets = _c(offsets, np.int32)
     E = W["E"]
     rows = int(offsets[-1])

@@ -40,7 +40,7 @@ class MoesqError(RuntimeError):
 class _CWeights(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
+                ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p), ("gscale_split", ctypes.c_int32)]
 
 
 _lib = None
@@ -126,13 +126,16 @@ def _dev(t):
 
 class Weights:
     """Weights of one projection for E experts (device tensors): pair-bitmask v1 storage
-    packed [E,N,K/4] u8, mask [E,N,K/16] u8, scale [E,N,K/32] u8 (UE4M3), gscale [E] f32, and
+    packed [E,N,K/4] u8, mask [E,N,K/16] u8, scale [E,N,K/32] u8 (UE4M3), gscale [E] f32 (or [E, 2]:
+    separate tensor scales of rows [0, N/2) and [N/2, N), a gate_up weight kept as two linears), and
     kl, the same bytes in the GEMM's kernel layout (built by ``prepack``)."""
 
     def __init__(self, packed, mask, scale, gscale, kl=None):
         E, N, K4 = packed.shape
         self.E, self.N, self.K = E, N, K4 * 4
-        assert mask.shape == (E, N, self.K // 16) and scale.shape == (E, N, self.K // 32) and gscale.shape == (E,)
+        assert mask.shape == (E, N, self.K // 16) and scale.shape == (E, N, self.K // 32)
+        assert gscale.shape in ((E,), (E, 2)) and gscale.is_contiguous()
+        self.gsplit = gscale.dim() == 2
         for t in (packed, mask, scale):
             assert t.dtype == torch.uint8 and t.is_contiguous()
         assert gscale.dtype == torch.float32
@@ -158,7 +161,7 @@ class Weights:
     def cstruct(self):
         return _CWeights(self.E, self.N, self.K, self.packed.data_ptr(), self.mask.data_ptr(),
                          self.scale.data_ptr(), self.gscale.data_ptr(),
-                         None if self.kl is None else self.kl.data_ptr())
+                         None if self.kl is None else self.kl.data_ptr(), int(self.gsplit))
 
     def nbytes(self):
         return self.packed.numel() + self.mask.numel() + self.scale.numel()
@@ -307,17 +310,25 @@ def moesq_prepack_weights(W):
     return W.prepack()
 
 
-def moesq_compress_weights(w, out=None, workspace=None, dev_status=None, prepack=True):
+def moesq_compress_weights(w, out=None, workspace=None, dev_status=None, prepack=True, split_halves=False):
     """fp32 weights [E, N, K] -> Weights (paired-4:8 pruning + NVFP4 + pair-bitmask v1), plus the
-    kernel layout when ``prepack`` (and K % 256 == 0, N % 64 == 0)."""
+    kernel layout when ``prepack`` (and K % 256 == 0, N % 64 == 0). ``split_halves``: rows [0, N/2)
+    and [N/2, N) are separate linears (gate and up) with their own tensor scale: the [2E, N/2, K]
+    view is compressed (same byte layout) and gscale comes back as [E, 2]."""
     _dev(w)
     assert w.dtype == torch.float32 and w.is_contiguous()
     E, N, K = w.shape
-    out = Weights.empty(E, N, K, w.device) if out is None else out
-    need = moesq_workspace_bytes(WS_COMPRESS, 0, 0, E)
+    if out is None:
+        out = Weights.empty(E, N, K, w.device)
+        if split_halves:
+            out = Weights(out.packed, out.mask, out.scale, torch.empty((E, 2), dtype=torch.float32, device=w.device))
+    assert out.gsplit == split_halves
+    Ec, Nc = (2 * E, N // 2) if split_halves else (E, N)
+    assert N % 2 == 0 or not split_halves
+    need = moesq_workspace_bytes(WS_COMPRESS, 0, 0, Ec)
     workspace = torch.empty(need, dtype=torch.uint8, device=w.device) if workspace is None else workspace
     _check("moesq_compress_weights",
-           lib().moesq_compress_weights(_stream(), _p(w), E, N, K, _p(out.packed), _p(out.mask), _p(out.scale),
+           lib().moesq_compress_weights(_stream(), _p(w), Ec, Nc, K, _p(out.packed), _p(out.mask), _p(out.scale),
                                         _p(out.gscale), _p(workspace), workspace.numel(), _p(dev_status)))
     if prepack and K % 256 == 0 and N % 64 == 0:
         out.prepack()

@@ -121,6 +121,8 @@ static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* 
   if (rows > 0 && (!q || !s || !y)) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 32 != 0) return MOESQ_ERR_INVALID_ARG;
   if (W->K % 256 != 0 || W->N % 64 != 0 || W->E > kMaxExpertsGemm) return MOESQ_ERR_UNSUPPORTED;
+  if (W->gscale_split != 0 && W->gscale_split != 1) return MOESQ_ERR_INVALID_ARG;
+  if (W->gscale_split && W->N % 128 != 0) return MOESQ_ERR_UNSUPPORTED;
   if (!aligned(W->kl, 16) || !aligned(q, 16) || !aligned(s, 2) || !aligned(y, 16) || !aligned(xk, 16))
     return MOESQ_ERR_UNSUPPORTED;
   if (xk && rows * W->K * 2 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
@@ -140,7 +142,7 @@ int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, c
   GemmArgs a{};
   a.kl = W->kl; a.gscale = W->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
-  a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
+  a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16; a.gsplit = W->gscale_split;
   if (flags & MOESQ_F_FORCE_DECODE) return launch_gemm_variant((hipStream_t)stream, a, rows, 0);
   if (flags & MOESQ_F_FORCE_PREFILL) return launch_gemm_variant((hipStream_t)stream, a, rows, 1);
   return launch_gemm((hipStream_t)stream, a, rows);
@@ -157,6 +159,8 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   int rc = gemm_common(W13, q, s, xk, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   if (I % 256 != 0 || W13->K % 256 != 0 || W2->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
+  if (W2->gscale_split != 0 && W2->gscale_split != 1) return MOESQ_ERR_INVALID_ARG;
+  if (W2->gscale_split && W2->N % 128 != 0) return MOESQ_ERR_UNSUPPORTED;
   if (!aligned(W2->kl, 16)) return MOESQ_ERR_UNSUPPORTED;
   if ((int64_t)W2->N * W2->K / 32 * 11 >= ((int64_t)1 << 31) || rows * (I / 2) >= ((int64_t)1 << 31))
     return MOESQ_ERR_UNSUPPORTED;
@@ -172,7 +176,7 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   GemmArgs a{};
   a.kl = W13->kl; a.gscale = W13->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
-  a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0;
+  a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0; a.gsplit = W13->gscale_split;
   a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk; a.dump = dumpp;
   // few tokens per expert: both GEMMs stream the weights; otherwise both are tiled
   int variant = rows <= (int64_t)16 * W13->E ? 0 : 1;
@@ -183,7 +187,7 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   GemmArgs b{};
   b.kl = W2->kl; b.gscale = W2->gscale;
   b.q = hq; b.s = hs; b.xk = hk; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
-  b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16;
+  b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16; b.gsplit = W2->gscale_split;
   return launch_gemm_variant((hipStream_t)stream, b, rows, variant);
 }
 
@@ -255,6 +259,7 @@ int moesq_dense_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t
   const int rc = gemm_common(W, q, s, xk, gamma_a, offsets, rows, y);
   if (rc != MOESQ_OK) return rc;
   if ((int64_t)W->N * W->K / 16 * 9 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  if (W->gscale_split) return MOESQ_ERR_UNSUPPORTED;  // the dense control has one tensor scale per expert
   GemmArgs a{};
   a.kl = W->kl; a.gscale = W->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;

@@ -251,6 +251,10 @@ struct DStage<true> {
   MOESQ_DEV void load(rsrc_t rq, rsrc_t, uint32_t, uint32_t, uint32_t vox, int ss) { load_xk(x, rq, vox, ss); }
 };
 
+// gamma_w of expert e for rows in half h (0: rows < N/2, 1: rows >= N/2): one scale per expert, or a
+// (gate, up) pair when the weights carry split tensor scales.
+MOESQ_DEV float wscale(const GemmArgs& a, int e, int h) { return a.gsplit ? a.gscale[2 * e + h] : a.gscale[e]; }
+
 MOESQ_DEV uint32_t expert_kl_bytes(int N, int K) { return (uint32_t)(N / 16) * (uint32_t)(K / 256) * kFragBytes; }
 
 // ============================================================== dense NVFP4 control operand =====
@@ -386,10 +390,11 @@ MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<t
 // MLP gate_up epilogue for one token (permuted row p; tv: the row is a real token): g0, g1 are the two
 // gate fragments and u0, u1 the matching up fragments of the 32 intermediate columns [ib, ib + 32);
 // lane (r16, cc) holds columns 16 f + 4 cc .. + 3 of fragment f. h = SiLU(g) * u in fp32 (the optional
-// fp32 dump keeps g and u), then the NVFP4 requantization of the 32-block with the expert's gamma_h
+// fp32 dump keeps g and u; alpha and alpha_u are the gate and up alpha_e, equal unless the weights carry
+// split tensor scales), then the NVFP4 requantization of the 32-block with the expert's gamma_h
 // (amax over the 4 lanes cc = 0..3: xor 16, 32), and the h codes, block scale and optional f16 copy.
-MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float gh, f32x4 g0,
-                                  f32x4 g1, f32x4 u0, f32x4 u1) {
+MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float alpha_u,
+                                  float gh, f32x4 g0, f32x4 g1, f32x4 u0, f32x4 u1) {
   const int N = a.N, I = N / 2;
   const f32x4 gg[2] = {g0, g1}, uu[2] = {u0, u1};
   float h[8];
@@ -398,14 +403,14 @@ MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib,
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const float g = gg[f][r] * alpha;
-      const float u = uu[f][r] * alpha;
+      const float u = uu[f][r] * alpha_u;
       h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
     }
     if (tv && a.dump) {
       const int64_t rowo = p * N;
       float4 gv, uv;
       gv.x = gg[f][0] * alpha; gv.y = gg[f][1] * alpha; gv.z = gg[f][2] * alpha; gv.w = gg[f][3] * alpha;
-      uv.x = uu[f][0] * alpha; uv.y = uu[f][1] * alpha; uv.z = uu[f][2] * alpha; uv.w = uu[f][3] * alpha;
+      uv.x = uu[f][0] * alpha_u; uv.y = uu[f][1] * alpha_u; uv.z = uu[f][2] * alpha_u; uv.w = uu[f][3] * alpha_u;
       *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
       *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
     }
@@ -490,8 +495,11 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
   const rsrc_t rq = XK ? make_rsrc((const uint8_t*)a.xk + (size_t)off * K * 2, (uint32_t)ne * K * 2)
                       : make_rsrc(a.q + (size_t)off * (K / 2), (uint32_t)ne * (K / 2));
   const rsrc_t rs = make_rsrc(a.s + (size_t)off * (K / 32), (uint32_t)ne * (K / 32));
-  const float alpha = 1.0f / (a.gscale[e] * a.gamma_a[e]);
   const int n0 = rb0 * 16;
+  // alpha_e = 1/(gamma_w gamma_a); the MLP's gate rows take the first and its up rows the second
+  // tensor scale, a plain wave the scale of its row half
+  const float alpha = 1.0f / (wscale(a, e, MLP ? 0 : (n0 >= N / 2)) * a.gamma_a[e]);
+  const float alpha_u = MLP ? 1.0f / (wscale(a, e, 1) * a.gamma_a[e]) : alpha;
   for (int tb = 0; tb < ne; tb += 16) {
     f32x4 acc[MF];
 #pragma unroll
@@ -541,7 +549,8 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
 #pragma unroll
             for (int v = 1; v < KS; v++) sum[f] = sum[f] + red[v][f][lane];
           }
-          mlp_epilogue_token(a, off + tok, tv, 32 * blockIdx.x, c, alpha, a.gamma_h[e], sum[0], sum[1], sum[2], sum[3]);
+          mlp_epilogue_token(a, off + tok, tv, 32 * blockIdx.x, c, alpha, alpha_u, a.gamma_h[e], sum[0], sum[1], sum[2],
+                             sum[3]);
         }
       } else {
         for (int f = kw; f < MF; f += KS) {
@@ -745,7 +754,7 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
 template <int MF>
 struct TileCtx {
   int e, off, ne, tb, rb, nv;
-  float alpha, gh;
+  float alpha, alpha_u, gh;
   rsrc_t rw;          // expert's weights (kernel layout)
   WSrc src;           // the wave's m-fragments in the kernel layout
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
@@ -786,7 +795,10 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
     c.src.g1 = 0;
     c.src.j1 = 0;
   }
-  c.alpha = 1.0f / (a.gscale[c.e] * a.gamma_a[c.e]);
+  // alpha_e: the MLP tile's gate and up rows take the two tensor scales, a plain wave its row half's
+  const int half = MLP ? 0 : (min(c.rb * 512 + 64 * w, N - 64) >= N / 2);
+  c.alpha = 1.0f / (wscale(a, c.e, half) * a.gamma_a[c.e]);
+  c.alpha_u = MLP ? 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]) : c.alpha;
   c.gh = MLP ? a.gamma_h[c.e] : 0.0f;
   if (XK) {
     c.rq = make_rsrc((const uint8_t*)a.xk + (size_t)c.off * K * 2, (uint32_t)c.ne * K * 2);
@@ -893,7 +905,8 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   for (int n = 0; n < NF; n++) {
     if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
-    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, c.gh, acc[0][n], acc[1][n], acc[2][n], acc[3][n]);
+    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, c.alpha_u, c.gh, acc[0][n], acc[1][n], acc[2][n],
+                       acc[3][n]);
   }
 }
 

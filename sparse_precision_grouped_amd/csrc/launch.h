@@ -26,6 +26,7 @@ struct GemmArgs {
   void* y;                // [rows][N] (plain epilogue)
   int32_t E, N, K;
   int32_t y_bf16;
+  int32_t gsplit;         // gscale holds (rows < N/2, rows >= N/2) pairs per expert
   // MLP gate_up epilogue (N = 2I): SwiGLU + requant into h_q [rows][I/2], h_s [rows][I/32]
   const float* gamma_h;   // [E] or nullptr for the plain epilogue
   uint8_t* h_q;

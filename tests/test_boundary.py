@@ -128,7 +128,7 @@ def test_gemm_and_mlp_validation(L):
     class CW(ctypes.Structure):
         _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                     ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
+                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p), ("gscale_split", ctypes.c_int32)]
     vp = ctypes.c_void_p
     g = L.moesq_grouped_gemm
     g.argtypes = [vp, ctypes.POINTER(CW), vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int32, ctypes.c_uint32]
@@ -141,6 +141,8 @@ def test_gemm_and_mlp_validation(L):
     assert call(CW(4, 128, 96, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS      # K % 256 != 0
     assert call(CW(4, 100, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS     # N % 64 != 0
     assert call(CW(4, 128, 256, 0, 0, 0, FAKE, 0)) == EARG            # no kernel layout
+    assert call(CW(4, 128, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 2)) == EARG  # gscale_split is 0 or 1
+    assert call(CW(4, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 1)) == EUNS   # split scales need N % 128 == 0
     m = L.moesq_expert_mlp
     m.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                   ctypes.c_int32, vp, ctypes.c_size_t, ctypes.c_uint32]
@@ -160,7 +162,7 @@ def test_prepack_validation_and_size(L):
     class CW(ctypes.Structure):
         _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                     ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p)]
+                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p), ("gscale_split", ctypes.c_int32)]
     vp = ctypes.c_void_p
     L.moesq_kernel_layout_bytes.restype = ctypes.c_size_t
     L.moesq_kernel_layout_bytes.argtypes = [ctypes.c_int32] * 3

@@ -331,6 +331,55 @@ def test_grouped_gemm_one_hot_activation_reads_weight_column(orc):
             assert np.array_equal(y[p], col)
 
 
+# ------------------------------------------- split gate / up tensor scales (model card) ------
+def test_split_scales_power_of_two_halves(orc):
+    """Up half = 8 x gate half: each linear's Eq. 5 scale absorbs the factor exactly, so the codes of
+    the two halves are identical, gamma_up = gamma_gate / 8 and the up outputs are 8 x the gate
+    outputs; each half also equals the matmul definition with its own scale."""
+    rng = np.random.default_rng(31)
+    E, N, K = 3, 64, 256
+    g = (rng.standard_normal((E, N // 2, K)) * 0.02).astype(np.float32)
+    w = np.concatenate([g, g * np.float32(8.0)], axis=1)
+    W = orc.compress_split(w)
+    assert W["gscale"].shape == (E, 2)
+    assert np.array_equal(W["gscale"][:, 1] * np.float32(8.0), W["gscale"][:, 0])
+    for key in ("packed", "mask", "scale"):
+        assert np.array_equal(W[key][:, :N // 2], W[key][:, N // 2:]), key
+    x = rng.standard_normal((24, K)).astype(np.float32)
+    ids = np.stack([rng.choice(E, 2, replace=False) for _ in range(12)]).astype(np.int32)
+    R = orc.route(ids, E)
+    ga = np.full(E, orc.global_scale_of(x[:12]), np.float32)
+    q, s = orc.dispatch_quantize(x[:12], R["sorted_slot"], 2, R["offsets"], ga)
+    y = orc.grouped_gemm(W, q, s, ga, R["offsets"])
+    assert y.shape == (24, N)
+    assert np.array_equal(y[:, N // 2:], 8.0 * y[:, :N // 2])
+    X = orc.dequant(q, s)
+    off = R["offsets"]
+    for h, Wh in enumerate(orc.split_halves(W)):
+        for e in range(E):
+            ref = X[off[e]:off[e + 1]] @ orc.dequant_weights(Wh, e).T / (np.float64(W["gscale"][e, h]) * np.float64(ga[e]))
+            assert np.allclose(y[off[e]:off[e + 1], h * (N // 2):(h + 1) * (N // 2)], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_split_scales_equal_amax_reduce_to_one_scale(orc):
+    """Halves with the same tensor amax: the split compression and GEMM equal the single-scale ones."""
+    rng = np.random.default_rng(32)
+    E, N, K = 2, 64, 256
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    w[:, 3, 5] = 0.5
+    w[:, N // 2 + 7, 9] = -0.5
+    Ws, W1 = orc.compress_split(w), orc.compress(w)
+    for key in ("packed", "mask", "scale"):
+        assert np.array_equal(Ws[key], W1[key]), key
+    assert np.array_equal(Ws["gscale"][:, 0], W1["gscale"]) and np.array_equal(Ws["gscale"][:, 1], W1["gscale"])
+    x = rng.standard_normal((8, K)).astype(np.float32)
+    ids = np.array([[0, 1]] * 8, np.int32)
+    R = orc.route(ids, E)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    q, s = orc.dispatch_quantize(x, R["sorted_slot"], 2, R["offsets"], ga)
+    assert np.array_equal(orc.grouped_gemm(Ws, q, s, ga, R["offsets"]), orc.grouped_gemm(W1, q, s, ga, R["offsets"]))
+
+
 # ----------------------------------------------------------- SwiGLU / combine ---------------
 def test_swiglu_closed_form(orc):
     from scipy.special import expit

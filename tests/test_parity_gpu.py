@@ -471,6 +471,50 @@ def test_mlp_parity_tiny(kernel):
     assert orc.rel_frobenius(host(out), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_split_tensor_scales(kernel):
+    """Gate and up kept as separate linears, each with its own Eq. 5 tensor scale (the model card's
+    checkpoint): device compression of the [2E, N/2, K] view against the oracle's compress_split
+    (bit-exact), the grouped GEMM on the split weights, and the MLP whose gate_up carries them, on
+    both kernel families."""
+    cfg = gen.CONFIGS["t_mlp"]
+    say("split tensor scales", kernel)
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w13[:, I:] *= np.float32(3.0)  # the up projection at another magnitude: its own tensor scale
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13 = mq.moesq_compress_weights(dev(w13), split_halves=True)
+    W13o = orc.compress_split(w13)
+    for key in ("packed", "mask", "scale", "gscale"):
+        assert np.array_equal(host(getattr(W13, key)), W13o[key]), key
+    assert np.all(W13o["gscale"][:, 0] != W13o["gscale"][:, 1])
+    W2 = mq.moesq_compress_weights(dev(w2))
+    W2o = orc.compress(w2)
+    x = gen.activations(cfg, 0, T, H)
+    ids, _ = gen.routing(cfg)
+    R = orc.route(ids, E)
+    off = R["offsets"]
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    gh = np.full(E, cfg.gamma_h / 3.0, np.float32)  # h is about 3x larger than in the single-scale case
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, off, ga)
+    y = host(mq.moesq_grouped_gemm(W13, dev(qo), dev(so), dev(ga), dev(off), y_dtype=torch.float32, flags=kf))
+    ref = orc.grouped_gemm(W13o, qo, so, ga, off)
+    for h in (slice(0, I), slice(I, I2)):
+        assert orc.rel_frobenius(y[:, h], ref[:, h]) <= GEMM_TOL
+    y2, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(off), y_dtype=torch.float32,
+                                 flags=mq.F_DUMP_GATEUP | kf)
+    rows = int(off[-1])
+    hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, off)
+    assert orc.rel_frobenius(host(dump), M["y13"]) <= GEMM_TOL
+    flips = np.mean(orc.dequant(host(hq), host(hs)) != orc.dequant(M["hq"], M["hs"]))
+    assert np.mean(host(hs) != M["hs"]) <= 1e-3 and flips <= 2e-3
+    err = orc.rel_frobenius(host(y2), M["y2"])
+    say("split scales: MLP y2 rel-Frobenius", err, "h flips", flips)
+    assert err <= 1e-2
+
+
 @pytest.mark.parametrize("name", ["c4", "c3_mlp"])
 def test_mlp_parity_full_size(name):
     """The Kimi-shaped routed-expert MLP at full size (E=384, H=7168, I=2048, top-8): c4 (T=8192, Zipf,
