@@ -54,12 +54,20 @@ extern "C" {
 #define MOESQ_F_FORCE_DECODE 2u  /* moesq_grouped_gemm: use the weight-streaming (decode) kernel */
 #define MOESQ_F_FORCE_PREFILL 4u /* moesq_grouped_gemm: use the tiled (prefill) kernel; without either
                                     flag the kernel is chosen from rows / E (<= 16: decode) */
+#define MOESQ_F_CAPACITY 8u      /* moesq_grouped_gemm, moesq_expert_mlp, moesq_dense_grouped_gemm: the
+                                    activations and outputs are in the fixed-capacity layout of paper
+                                    Appendix D.1 (expert e owns rows [e*C, (e+1)*C), C = rows / E, rows
+                                    % E == 0) and `offsets` points to the token counts [E] instead: the
+                                    first min(count, C) rows of each block are used, the others are
+                                    padding, neither read nor written (moesq_route_capacity builds the
+                                    layout's slot positions) */
 
 /* ---- workspace query kinds --------------------------------------------------------------------- */
 #define MOESQ_WS_ROUTE 1
 #define MOESQ_WS_MLP 2
 #define MOESQ_WS_MLP_DUMP 3
 #define MOESQ_WS_COMPRESS 4
+#define MOESQ_WS_ROUTE_CAPACITY 5
 
 /*
  * Compressed weights of one projection for E experts, pair-bitmask v1 layout (model card, "Sparse
@@ -112,6 +120,20 @@ int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_
                         void *workspace, size_t workspace_bytes, int32_t *dev_status);
 
 /*
+ * Routing into the fixed-capacity layout (paper Appendix D.1: activations and outputs batched with a
+ * fixed per-expert capacity C, so expert e's operands sit at a fixed stride and no pointer arrays are
+ * needed): slot f = t*k + j routed to expert e with stable rank r among e's slots (ascending f) gets
+ * slot_pos[f] = e*C + r when r < C, else -1 (over capacity: not placed; combine skips it).
+ *   counts    [E] all slots routed to each expert (may exceed C; the GEMMs use min(count, C))
+ *   slot_pos  [T*k]; -1 also for ids outside [0, E), reported in *dev_status as moesq_route_permute
+ *   workspace moesq_workspace_bytes(MOESQ_WS_ROUTE_CAPACITY, T, k, E, 0, 0, 0) bytes, 256-byte aligned
+ * Limits: E <= 512, T*k < 2^31, E*C < 2^31.
+ */
+int moesq_route_capacity(void *stream, const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t capacity,
+                         int32_t *counts, int32_t *slot_pos, void *workspace, size_t workspace_bytes,
+                         int32_t *dev_status);
+
+/*
  * Dynamic NVFP4 activation quantization (paper Section 3.4 and Appendix D.1: activations are
  * quantized at run time into 32-element blocks; Eq. 3 + Eq. 5 with the given tensor scale), fused
  * with token dispatch (a scatter: every token row of x is read once and its codes are written to each
@@ -122,7 +144,9 @@ int moesq_route_permute(void *stream, const int32_t *topk_ids, int64_t T, int32_
  *               rows no slot points to are not written. NULL: rows must equal T and row p is x row p.
  *   gamma       [G] fp32 tensor scales. With offsets != NULL, row p uses gamma[e] where
  *               offsets[e] <= p < offsets[e+1] (G = E, the per-expert input scale of the model
- *               card); with offsets == NULL every row uses gamma[0].
+ *               card); with offsets == NULL and E > 0 the rows are in the fixed-capacity layout
+ *               (MOESQ_F_CAPACITY; rows % E == 0) and row p uses gamma[p / (rows / E)]; with
+ *               offsets == NULL and E == 0 every row uses gamma[0].
  *   q           [rows][K/2] E2M1 codes, s [rows][K/32] UE4M3 codes.
  *   xk          optional (NULL to skip), 16-byte aligned: [rows][K] f16, the same values dequantized
  *               (e2m1 * e4m3, exact in f16) with every 8-group of K stored in the order

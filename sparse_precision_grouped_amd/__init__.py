@@ -18,8 +18,8 @@ __all__ = [
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
     "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
     "moesq_prepack_weights", "moesq_kernel_layout_bytes",
-    "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL",
-    "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS",
+    "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL", "F_CAPACITY",
+    "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS", "WS_ROUTE_CAPACITY", "moesq_route_capacity",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,8 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libmoesq.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_PATTERN, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL = 1, 2, 4
-WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS = 1, 2, 3, 4
+F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL, F_CAPACITY = 1, 2, 4, 8
+WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS, WS_ROUTE_CAPACITY = 1, 2, 3, 4, 5
 
 
 class MoesqError(RuntimeError):
@@ -57,6 +57,7 @@ def lib():
         W = ctypes.POINTER(_CWeights)
         L.moesq_route_permute.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_quantize_act.argtypes = [vp, vp, i32, i64, i32, i64, vp, i32, i64, vp, vp, i32, vp, vp, vp]
+        L.moesq_route_capacity.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, sz, vp]
         L.moesq_route_quantize.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp,
                                            vp, vp, vp]
         L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, vp, i64, vp, i32, u32]
@@ -77,7 +78,7 @@ def lib():
         L.moesq_status_str.argtypes = [i32]
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
-        for name in ("moesq_route_permute", "moesq_quantize_act", "moesq_route_quantize", "moesq_grouped_gemm", "moesq_expert_mlp",
+        for name in ("moesq_route_permute", "moesq_route_capacity", "moesq_quantize_act", "moesq_route_quantize", "moesq_grouped_gemm", "moesq_expert_mlp",
                      "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale",
                      "moesq_prepack_weights"):
             getattr(L, name).restype = ctypes.c_int
@@ -189,10 +190,29 @@ def moesq_route_permute(topk_ids, E, counts=None, offsets=None, sorted_slot=None
     return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos)
 
 
-def moesq_quantize_act(x, gamma, slot_pos=None, k=1, offsets=None, q=None, s=None, rows=None, xk=None):
+def moesq_route_capacity(topk_ids, E, capacity, counts=None, slot_pos=None, workspace=None, dev_status=None):
+    """Slot positions in the fixed-capacity layout (expert e owns rows [e C, (e + 1) C)): returns
+    dict(counts [E], slot_pos [T*k]; -1 for slots over the capacity)."""
+    _dev(topk_ids)
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    slot_pos = torch.empty(T * k, dtype=torch.int32, device=dev) if slot_pos is None else slot_pos
+    need = moesq_workspace_bytes(WS_ROUTE_CAPACITY, T, k, E)
+    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _check("moesq_route_capacity",
+           lib().moesq_route_capacity(_stream(), _p(topk_ids), T, k, E, capacity, _p(counts), _p(slot_pos),
+                                      _p(workspace), workspace.numel(), _p(dev_status)))
+    return dict(counts=counts, slot_pos=slot_pos)
+
+
+def moesq_quantize_act(x, gamma, slot_pos=None, k=1, offsets=None, q=None, s=None, rows=None, xk=None,
+                       capacity_experts=0):
     """NVFP4-quantize rows of x [T, K] (fp32/bf16). With slot_pos (from moesq_route_permute), token t's
     j-th routed copy goes to permuted row slot_pos[t*k + j] and (with offsets) uses gamma[expert of that
-    row]. Returns (q [rows,K/2], s [rows,K/32]);
+    row]; with ``capacity_experts`` = E (and no offsets) the rows are in the fixed-capacity layout and row
+    p uses gamma[p // (rows // E)]. Returns (q [rows,K/2], s [rows,K/32]);
     with ``xk`` (a [rows, K] float16 tensor, or True to allocate one) also writes the GEMM's f16
     operand copy and returns (q, s, xk)."""
     _dev(x)
@@ -200,7 +220,7 @@ def moesq_quantize_act(x, gamma, slot_pos=None, k=1, offsets=None, q=None, s=Non
     assert x.stride(1) == 1
     if rows is None:
         rows = T if slot_pos is None else slot_pos.numel()
-    E = 0 if offsets is None else offsets.numel() - 1
+    E = capacity_experts if offsets is None else offsets.numel() - 1
     q = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device) if s is None else s
     want_xk = xk is not None

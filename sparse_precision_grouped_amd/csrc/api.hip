@@ -18,6 +18,12 @@ bool weights_ok(const moesq_weights* W) {
 
 constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Capacity routing workspace: the prefix routing's own workspace, then its offsets [E+1], sorted slots
+// [n] and slot positions [n], each region 256-byte aligned.
+static size_t route_capacity_ws(int64_t n, int32_t E) {
+  return align256(route_workspace_bytes(n, E)) + align256((size_t)(E + 1) * 4) + 2 * align256((size_t)n * 4);
+}
+
 // MLP workspace: h_q [rows][I/2], h_s [rows][I/32], h_k [rows][I] f16, then (dump) fp32 [rows][2I],
 // each region starting on a 256-byte boundary.
 size_t mlp_ws(int64_t rows, int32_t I, bool dump) {
@@ -52,6 +58,7 @@ size_t moesq_workspace_bytes(int32_t kind, int64_t T, int32_t k, int32_t E, int3
     case MOESQ_WS_MLP: return T >= 0 && I > 0 ? mlp_ws(T, I, false) : 0;
     case MOESQ_WS_MLP_DUMP: return T >= 0 && I > 0 ? mlp_ws(T, I, true) : 0;
     case MOESQ_WS_COMPRESS: return E > 0 ? (size_t)E * sizeof(uint32_t) : 0;
+    case MOESQ_WS_ROUTE_CAPACITY: return (T >= 0 && k > 0 && E > 0) ? route_capacity_ws(T * k, E) : 0;
     default: return 0;
   }
 }
@@ -70,6 +77,28 @@ int moesq_route_permute(void* stream, const int32_t* topk_ids, int64_t T, int32_
                       dev_status);
 }
 
+int moesq_route_capacity(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t capacity,
+                         int32_t* counts, int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                         int32_t* dev_status) {
+  if (T < 0 || k <= 0 || E <= 0 || k > E || capacity <= 0) return MOESQ_ERR_INVALID_ARG;
+  if (!counts) return MOESQ_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !slot_pos)) return MOESQ_ERR_INVALID_ARG;
+  if (E > kMaxExpertsRoute) return MOESQ_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= ((int64_t)1 << 31) || (int64_t)E * capacity >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
+  const int64_t n = T * k;
+  const size_t need = route_capacity_ws(n, E);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return MOESQ_ERR_WORKSPACE;
+  uint8_t* w = (uint8_t*)workspace;
+  void* rws = w;
+  int32_t* offs = (int32_t*)(w + align256(route_workspace_bytes(n, E)));
+  int32_t* sorted = (int32_t*)((uint8_t*)offs + align256((size_t)(E + 1) * 4));
+  int32_t* pos = (int32_t*)((uint8_t*)sorted + align256((size_t)n * 4));
+  const int rc = launch_route((hipStream_t)stream, topk_ids, n, E, counts, offs, sorted, pos,
+                              route_workspace_bytes(n, E) ? rws : nullptr, dev_status);
+  if (rc != MOESQ_OK) return rc;
+  return launch_capacity_slots((hipStream_t)stream, topk_ids, n, E, capacity, offs, pos, slot_pos);
+}
+
 int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, int32_t K, int64_t ld_x,
                        const int32_t* slot_pos, int32_t k, int64_t rows, const float* gamma, const int32_t* offsets,
                        int32_t E, uint8_t* q, uint8_t* s, void* xk) {
@@ -86,10 +115,11 @@ int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, 
   }
   if (offsets && E <= 0) return MOESQ_ERR_INVALID_ARG;
   if (offsets && E > 4096) return MOESQ_ERR_UNSUPPORTED;
+  if (!offsets && E > 0 && (rows % E != 0 || rows == 0)) return MOESQ_ERR_INVALID_ARG;  // capacity layout
   if (rows >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
   if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4) || !aligned(xk, 16)) return MOESQ_ERR_UNSUPPORTED;
   return launch_quantize((hipStream_t)stream, x, x_dtype == MOESQ_BF16, T, K, ld_x, slot_pos, k, gamma, offsets, E,
-                         q, s, xk);
+                         q, s, xk, (!offsets && E > 0) ? (int32_t)(rows / E) : 0);
 }
 
 int moesq_route_quantize(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
@@ -133,6 +163,15 @@ static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* 
   return MOESQ_OK;
 }
 
+// MOESQ_F_CAPACITY: offsets holds counts[E] and the rows form E blocks of rows / E (the capacity).
+static int capacity_of(uint32_t flags, int32_t E, int64_t rows, int32_t& cap) {
+  cap = 0;
+  if (!(flags & MOESQ_F_CAPACITY)) return MOESQ_OK;
+  if (rows % E != 0) return MOESQ_ERR_INVALID_ARG;
+  cap = (int32_t)(rows / E);
+  return MOESQ_OK;
+}
+
 int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,
                        const float* gamma_a, const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype,
                        uint32_t flags) {
@@ -143,6 +182,7 @@ int moesq_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t* q, c
   a.kl = W->kl; a.gscale = W->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
   a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16; a.gsplit = W->gscale_split;
+  if (capacity_of(flags, W->E, rows, a.cap) != MOESQ_OK) return MOESQ_ERR_INVALID_ARG;
   if (flags & MOESQ_F_FORCE_DECODE) return launch_gemm_variant((hipStream_t)stream, a, rows, 0);
   if (flags & MOESQ_F_FORCE_PREFILL) return launch_gemm_variant((hipStream_t)stream, a, rows, 1);
   return launch_gemm((hipStream_t)stream, a, rows);
@@ -177,6 +217,7 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   a.kl = W13->kl; a.gscale = W13->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
   a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0; a.gsplit = W13->gscale_split;
+  if (capacity_of(flags, W13->E, rows, a.cap) != MOESQ_OK) return MOESQ_ERR_INVALID_ARG;
   a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk; a.dump = dumpp;
   // few tokens per expert: both GEMMs stream the weights; otherwise both are tiled
   int variant = rows <= (int64_t)16 * W13->E ? 0 : 1;
@@ -188,6 +229,7 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   b.kl = W2->kl; b.gscale = W2->gscale;
   b.q = hq; b.s = hs; b.xk = hk; b.gamma_a = gamma_h; b.offsets = offsets; b.y = y;
   b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16; b.gsplit = W2->gscale_split;
+  b.cap = a.cap;
   return launch_gemm_variant((hipStream_t)stream, b, rows, variant);
 }
 
@@ -264,6 +306,7 @@ int moesq_dense_grouped_gemm(void* stream, const moesq_weights* W, const uint8_t
   a.kl = W->kl; a.gscale = W->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
   a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16;
+  if (capacity_of(flags, W->E, rows, a.cap) != MOESQ_OK) return MOESQ_ERR_INVALID_ARG;
   int variant = rows <= (int64_t)16 * W->E ? 0 : 1;
   if (flags & MOESQ_F_FORCE_DECODE) variant = 0;
   if (flags & MOESQ_F_FORCE_PREFILL) variant = 1;

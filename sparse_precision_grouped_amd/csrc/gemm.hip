@@ -251,6 +251,19 @@ struct DStage<true> {
   MOESQ_DEV void load(rsrc_t rq, rsrc_t, uint32_t, uint32_t, uint32_t vox, int ss) { load_xk(x, rq, vox, ss); }
 };
 
+// The rows of expert e: [off, off + ne). Prefix layout: offsets[e] .. offsets[e+1]. Capacity layout
+// (cap > 0, offsets holds the token counts): rows e * cap .. + min(count, cap) of a buffer with a fixed
+// per-expert capacity; the remaining rows of the expert are padding and are neither read nor written.
+MOESQ_DEV void expert_rows(const GemmArgs& a, int e, int& off, int& ne) {
+  if (a.cap > 0) {
+    off = e * a.cap;
+    ne = min(a.offsets[e], a.cap);
+  } else {
+    off = a.offsets[e];
+    ne = a.offsets[e + 1] - off;
+  }
+}
+
 // gamma_w of expert e for rows in half h (0: rows < N/2, 1: rows >= N/2): one scale per expert, or a
 // (gate, up) pair when the weights carry split tensor scales.
 MOESQ_DEV float wscale(const GemmArgs& a, int e, int h) { return a.gsplit ? a.gscale[2 * e + h] : a.gscale[e]; }
@@ -469,8 +482,8 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
   static_assert(!MLP || (MF == 4 && RG == 1 && KS > 1 && !DENSE), "MLP epilogue: 32 gate + 32 up rows per workgroup");
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
-  const int off = a.offsets[e];
-  const int ne = a.offsets[e + 1] - off;
+  int off, ne;
+  expert_rows(a, e, off, ne);
   if (ne <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, c = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -712,18 +725,25 @@ struct TWS<MF, MLP, true> {
 };
 
 // Per-expert tile counts ceil(n_e / kTileTok) -> exclusive prefix tile_pre[0..E] in LDS (E+1
-// entries), and the expert offsets copied to off_l[0..E]. part: LDS scratch of THREADS ints.
+// entries), each expert's first row off_l[e] and row count ne_l[e] (E entries). part: LDS scratch of
+// THREADS ints.
 template <int THREADS>
-MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int32_t* tile_pre, int32_t* off_l,
+MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* off_l, int32_t* ne_l,
                                  int32_t* part) {
   constexpr int PER_LANE = THREADS / 64;
   const int tid = threadIdx.x;
-  for (int i = tid; i <= E; i += THREADS) off_l[i] = offsets[i];
+  const int E = a.E;
+  for (int i = tid; i < E; i += THREADS) {
+    int off, ne;
+    expert_rows(a, i, off, ne);
+    off_l[i] = off;
+    ne_l[i] = max(ne, 0);
+  }
   __syncthreads();
   const int per = (E + THREADS - 1) / THREADS;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; e++) sum += (off_l[e + 1] - off_l[e] + kTileTok - 1) / kTileTok;
+  for (int e = lo; e < hi; e++) sum += (ne_l[e] + kTileTok - 1) / kTileTok;
   part[tid] = sum;
   __syncthreads();
   if (tid < 64) {  // wave 0 scans the partial sums (PER_LANE per lane)
@@ -744,7 +764,7 @@ MOESQ_DEV void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int
   int run = part[tid];
   for (int e = lo; e < hi; e++) {
     tile_pre[e] = run;
-    run += (off_l[e + 1] - off_l[e] + kTileTok - 1) / kTileTok;
+    run += (ne_l[e] + kTileTok - 1) / kTileTok;
   }
   if (hi == E && lo < hi) tile_pre[E] = run;
   __syncthreads();
@@ -763,7 +783,8 @@ struct TileCtx {
 // Tile t of the list ordered expert -> token tile -> row block (row block fastest): workgroups of one
 // XCD that run neighbouring tiles share the activation tile in L2.
 template <int MF, bool MLP, bool XK, bool DENSE>
-MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, int RB, int t,
+MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, const int32_t* ne_l,
+                                int RB, int t,
                                 int w) {
   TileCtx<MF> c;
   int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] * RB <= t
@@ -776,7 +797,7 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kTileTok);
   c.rb = __builtin_amdgcn_readfirstlane(local % RB);
   c.off = __builtin_amdgcn_readfirstlane(off_l[c.e]);
-  c.ne = __builtin_amdgcn_readfirstlane(off_l[c.e + 1]) - c.off;
+  c.ne = __builtin_amdgcn_readfirstlane(ne_l[c.e]);
   c.nv = min(kTileNF, (c.ne - c.tb + 15) / 16);
   const int K = a.K, N = a.N, nss = K / 256;
   const uint32_t ekl = DENSE ? expert_dense_bytes(N, K) : expert_kl_bytes(N, K);
@@ -927,7 +948,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   uint8_t* Bs1 = dyn + BBYTES;
   int32_t* tile_pre = (int32_t*)(dyn + 2 * BBYTES);      // [E+1]
   int32_t* off_l = tile_pre + a.E + 1;                   // [E+1]
-  build_tile_prefix<kTileThreads>(a.offsets, a.E, tile_pre, off_l, part);
+  int32_t* ne_l = off_l + a.E + 1;                       // [E]
+  build_tile_prefix<kTileThreads>(a, tile_pre, off_l, ne_l, part);
   const int K = a.K, nss = K / 256;
   const int RB = MLP ? a.N / 512 : (a.N + 511) / 512;   // MLP: 256 gate + 256 up rows per tile
   const int T = tile_pre[a.E] * RB;
@@ -944,7 +966,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  TileCtx<MF> cur = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, RB, t, w);
+  TileCtx<MF> cur = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t, w);
   TWS<MF, MLP, DENSE> wc, wn;
   PStage p;
   wc.load(cur.rw, cur.src, lane, 0);
@@ -963,7 +985,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     }
     const bool has_n = t_n < tend;
     TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     if (has_n) {
@@ -994,7 +1016,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   }
 }
 
-static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + 2 * (size_t)(E + 1) * 4; }
+static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (2 * (size_t)(E + 1) + (size_t)E) * 4; }
 
 static int device_cu_count() {
   static int cus[64] = {0};

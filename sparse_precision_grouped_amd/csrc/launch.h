@@ -27,6 +27,7 @@ struct GemmArgs {
   int32_t E, N, K;
   int32_t y_bf16;
   int32_t gsplit;         // gscale holds (rows < N/2, rows >= N/2) pairs per expert
+  int32_t cap;            // > 0: capacity layout, offsets holds counts[E] and expert e's rows start at e * cap
   // MLP gate_up epilogue (N = 2I): SwiGLU + requant into h_q [rows][I/2], h_s [rows][I/32]
   const float* gamma_h;   // [E] or nullptr for the plain epilogue
   uint8_t* h_q;
@@ -39,9 +40,13 @@ size_t route_workspace_bytes(int64_t n, int32_t E);
 int launch_route(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t* counts, int32_t* offsets,
                  int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status);
 
+// cap > 0 (with offsets == nullptr): rows are in the capacity layout, row p belongs to expert p / cap.
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
                     const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
-                    uint8_t* q, uint8_t* s, void* xk);
+                    uint8_t* q, uint8_t* s, void* xk, int32_t cap = 0);
+// Capacity-layout slot positions from the prefix routing: e * cap + rank, or -1 past the capacity.
+int launch_capacity_slots(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t cap,
+                          const int32_t* offsets, const int32_t* slot_pos_prefix, int32_t* slot_pos);
 // Routing + scatter quantization: one fused launch when route_quantize_fused(T, k, E), else the
 // routing kernels followed by the quantizer (ws = the routing workspace).
 bool route_quantize_fused(int64_t T, int32_t k, int32_t E);

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                                                        const float* __restrict__ gamma,
                                                        const int32_t* __restrict__ offsets, int32_t E,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                       uint8_t* __restrict__ xk) {
+                                                       uint8_t* __restrict__ xk, int32_t cap) {
   __shared__ int32_t off_l[kQuantMaxE + 1];
   __shared__ int32_t dst[kQuantMaxK];
   __shared__ float gam[kQuantMaxK];
@@ -113,6 +113,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         }
         g = gamma[lo];
       }
+    } else if (p >= 0 && cap > 0) {
+      g = gamma[p / cap];  // capacity layout: expert e owns rows [e cap, (e + 1) cap)
     }
     dst[j] = p;
     gam[j] = g;
@@ -123,10 +125,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 
 int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32_t K, int64_t ld_x,
                     const int32_t* slot_pos, int32_t k, const float* gamma, const int32_t* offsets, int32_t E,
-                    uint8_t* q, uint8_t* s, void* xk) {
+                    uint8_t* q, uint8_t* s, void* xk, int32_t cap) {
   if (T == 0) return MOESQ_OK;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (int)x_bf16, T, K, ld_x, slot_pos, k,
-                     gamma, offsets, E, q, s, (uint8_t*)xk);
+                     gamma, offsets, E, q, s, (uint8_t*)xk, cap);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// Capacity layout ([P] Appendix D.1: activations and outputs batched with a fixed per-expert capacity,
+// so expert e's operands sit at a fixed stride): slot f of expert e with stable rank r among that
+// expert's slots goes to row e * cap + r, or nowhere (-1) when r >= cap; invalid ids stay -1.
+__global__ __launch_bounds__(256) void capacity_slots_kernel(const int32_t* __restrict__ ids, int64_t n, int32_t cap,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ slot_pos_prefix,
+                                                             int32_t* __restrict__ slot_pos) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= n) return;
+  const int32_t p = slot_pos_prefix[f];
+  int32_t out = -1;
+  if (p >= 0) {
+    const int32_t e = ids[f];
+    const int32_t r = p - offsets[e];
+    if (r < cap) out = e * cap + r;
+  }
+  slot_pos[f] = out;
+}
+
+int launch_capacity_slots(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t cap, const int32_t* offsets,
+                          const int32_t* slot_pos_prefix, int32_t* slot_pos) {
+  (void)E;
+  if (n == 0) return MOESQ_OK;
+  hipLaunchKernelGGL(capacity_slots_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, n, cap, offsets,
+                     slot_pos_prefix, slot_pos);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

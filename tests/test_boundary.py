@@ -76,6 +76,21 @@ def test_route_validation(L):
     assert L.moesq_workspace_bytes(1, 16, 8, 128, 0, 0, 0) == 0   # one-workgroup path
 
 
+def test_route_capacity_validation(L):
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    f = L.moesq_route_capacity
+    f.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, sz, vp]
+    call = lambda T=16, k=2, E=8, C=4, ids=FAKE, ws=FAKE, wsb=1 << 20: f(  # noqa: E731
+        None, _p(ids) if ids else None, T, k, E, C, _p(FAKE), _p(FAKE), _p(ws) if ws else None, wsb, None)
+    assert call(C=0) == EARG
+    assert call(k=9) == EARG
+    assert call(ids=0) == EARG
+    assert call(E=600) == EUNS
+    assert call(ws=0) == EWS
+    assert call(wsb=16) == EWS
+    assert L.moesq_workspace_bytes(5, 16, 2, 8, 0, 0, 0) > 0
+
+
 def test_quantize_validation(L):
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     f = L.moesq_quantize_act
@@ -97,6 +112,7 @@ def test_quantize_validation(L):
     assert call(g=FAKE, k=513, rows=8 * 513) == EUNS
     assert call(g=FAKE, k=0) == EARG
     assert call(x=FAKE + 4) == EUNS       # misaligned x
+    assert call(E=3, rows=8) == EARG      # fixed-capacity rows (no offsets, E > 0) must split into E blocks
 
 
 def test_route_quantize_validation(L):

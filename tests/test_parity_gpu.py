@@ -515,6 +515,89 @@ def test_split_tensor_scales(kernel):
     assert err <= 1e-2
 
 
+def _small_weights(E, N, K, seed):
+    """Seeded N(0, 0.02) weights compressed on the device and by the oracle."""
+    w = (np.random.default_rng(seed).standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    return mq.moesq_compress_weights(dev(w)), orc.compress(w)
+
+
+def _capacity_rows(R, ids, C):
+    """The oracle's routing mapped into the fixed-capacity layout: expected slot positions, and for
+    every placed slot its capacity row and its contiguous (prefix-layout) row."""
+    E = R["counts"].size
+    e = ids.ravel().astype(np.int64)
+    r = R["slot_pos"].astype(np.int64) - R["offsets"][e]
+    exp = np.where(r < C, e * C + r, -1).astype(np.int32)
+    keep = exp >= 0
+    return exp, exp[keep].astype(np.int64), R["slot_pos"][keep].astype(np.int64)
+
+
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_capacity_layout_gemm(kernel):
+    """The fixed-capacity layout (expert e owns rows [e C, (e+1) C), counts on the device): routing
+    into it, the scatter quantizer with per-expert scales, and the grouped GEMM, against the oracle's
+    contiguous results mapped row by row; experts below, at zero and over the capacity."""
+    say("capacity layout gemm", kernel)
+    E, N, K, T, k, C = 16, 256, 512, 64, 4, 20
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    Wd, W = _small_weights(E, N, K, 41)
+    ids, _ = gen.route_zipf(41, T, E, k, 1.1, 2)
+    x = gen.student_t(41, gen.act_stream(5), T * K).reshape(T, K)
+    ga = (np.float32(orc.global_scale_of(x)) * np.linspace(0.8, 1.25, E)).astype(np.float32)
+    R = orc.route(ids, E)
+    exp, cap_rows, pre_rows = _capacity_rows(R, ids, C)
+    rc = mq.moesq_route_capacity(dev(ids), E, C)
+    assert np.array_equal(host(rc["counts"]), R["counts"])
+    assert np.array_equal(host(rc["slot_pos"]), exp)
+    q, s = mq.moesq_quantize_act(dev(x), dev(ga), slot_pos=rc["slot_pos"], k=k, rows=E * C, capacity_experts=E)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    assert np.array_equal(host(q)[cap_rows], qo[pre_rows]) and np.array_equal(host(s)[cap_rows], so[pre_rows])
+    y = host(mq.moesq_grouped_gemm(Wd, q, s, dev(ga), rc["counts"], y_dtype=torch.float32, flags=mq.F_CAPACITY | kf))
+    ref = orc.grouped_gemm(W, qo, so, ga, R["offsets"], pre_rows)
+    assert orc.rel_frobenius(y[cap_rows], ref) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_capacity_layout_mlp_and_combine(kernel):
+    """The routed-expert MLP in the fixed-capacity layout and the combine of its outputs (slots over
+    the capacity are dropped and contribute nothing)."""
+    cfg = gen.CONFIGS["t_mlp"]
+    say("capacity layout mlp", kernel)
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    C = 32
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    W13o, W2o = orc.compress(w13), orc.compress(w2)
+    x = gen.activations(cfg, 0, T, H)
+    ids, wts = gen.routing(cfg)
+    R = orc.route(ids, E)
+    exp, cap_rows, pre_rows = _capacity_rows(R, ids, C)
+    assert (R["counts"] > C).any() and (R["counts"] < C).any()
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    gh = np.full(E, cfg.gamma_h, np.float32)
+    rc = mq.moesq_route_capacity(dev(ids), E, C)
+    assert np.array_equal(host(rc["slot_pos"]), exp)
+    q, s = mq.moesq_quantize_act(dev(x), dev(ga), slot_pos=rc["slot_pos"], k=k, rows=E * C, capacity_experts=E)
+    y2, ws = mq.moesq_expert_mlp(W13, W2, q, s, dev(ga), dev(gh), rc["counts"], y_dtype=torch.float32,
+                                 flags=mq.F_DUMP_GATEUP | mq.F_CAPACITY | kf)
+    hq, hs, dump = mq.mlp_workspace_views(ws, E * C, I, dump=True)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"], pre_rows)
+    assert orc.rel_frobenius(host(dump)[cap_rows], M["y13"]) <= GEMM_TOL
+    flips = np.mean(orc.dequant(host(hq)[cap_rows], host(hs)[cap_rows]) != orc.dequant(M["hq"], M["hs"]))
+    assert flips <= 2e-3
+    err = orc.rel_frobenius(host(y2)[cap_rows], M["y2"])
+    say("capacity MLP y2 rel-Frobenius", err, "h flips", flips)
+    assert err <= 1e-2
+    # combine over the capacity layout: the oracle on the same rows, dropped slots pointing at a zero row
+    out = host(mq.moesq_unpermute_combine(y2, rc["slot_pos"], dev(wts), out_dtype=torch.float32))
+    y_ext = np.concatenate([host(y2).astype(np.float64), np.zeros((1, H))])
+    sp = np.where(exp >= 0, exp, E * C).astype(np.int32)
+    assert orc.rel_frobenius(out, orc.combine(y_ext, sp, wts)) <= 1e-6
+
+
 @pytest.mark.parametrize("name", ["c4", "c3_mlp"])
 def test_mlp_parity_full_size(name):
     """The Kimi-shaped routed-expert MLP at full size (E=384, H=7168, I=2048, top-8): c4 (T=8192, Zipf,
