@@ -115,9 +115,11 @@ def summarize_pmc(argv):
     for (k, c), (v, n) in write.items():
         if c == "WRITE_SIZE":
             per_kernel.setdefault(k, {})["write_bytes"] = v * 1024.0 * f_write
-    if wl == "c4":
+    if wl in ("c4", "c3_mlp"):
+        # one moesq_expert_mlp call: its gate_up and down kernels (distinct template instances)
         key = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
-        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if "gemm_tile_kernel" in k)
+        total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items()
+                    if "gemm_tile_kernel" in k or "gemm_decode_kernel" in k)
     else:
         key = "gemm_decode_kernel" if any("gemm_decode_kernel" in k for k in per_kernel) else "gemm_tile_kernel"
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
@@ -540,8 +542,20 @@ def main(argv=None):
     t = (time.perf_counter() - t0) / args.steps
     value = wl.eff_flops_per_step() / t / 1e12
 
-    # dominant kernel: HIP events on the launch stream around each launch
+    # spread of the step time (outside the timed region): HIP events around each replay of the R-step
+    # graph, per step
     st = torch.cuda.current_stream()
+    reps = max(5, min(50, args.steps // wl.R))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(st)
+        wl.chain.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 / wl.R for a, b in evs])
+    pcts = [round(float(np.percentile(per_step, q)), 2) for q in (10, 50, 90)]
+
+    # dominant kernel: HIP events on the launch stream around each launch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.kernel_iters)]
     for i, (a, b) in enumerate(evs):
@@ -580,7 +594,7 @@ def main(argv=None):
             ", then K=%d N=%d" % (cfg.K2, cfg.N2) if cfg.N2 else ""),
             "rows": wl.rows, "weight_copies": wl.R, "graph_replay": "%d steps per graph" % wl.R,
             "activation_operand": "f16 copy" if f16_operand else "nvfp4",
-            "step_gbps_algorithmic": step_gbps},
+            "step_gbps_algorithmic": step_gbps, "step_us_p10_p50_p90": pcts},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line))
