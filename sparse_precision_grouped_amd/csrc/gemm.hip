@@ -493,8 +493,14 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
   const uint32_t ekl = DENSE ? expert_dense_bytes(N, K) : expert_kl_bytes(N, K);
   const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
   WSrc src;
+  // MLP: workgroups 2m and 2m+1 read the two halves of the same 64-row units' mask and scale lines;
+  // when gridDim.x is a multiple of 16 the blocks are renumbered so that such a pair is dispatched 8
+  // apart, i.e. to the same XCD (workgroups go to the XCDs round-robin), and shares its L2 lines.
+  const int bx = (MLP && gridDim.x % 16 == 0)
+                     ? (int)((blockIdx.x & ~15u) + 2 * (blockIdx.x & 7u) + ((blockIdx.x >> 3) & 1u))
+                     : (int)blockIdx.x;
   if (MLP) {
-    const int rgate = 2 * blockIdx.x, rup = N / 32 + 2 * blockIdx.x;  // 16-row blocks of the gate / up rows
+    const int rgate = 2 * bx, rup = N / 32 + 2 * bx;  // 16-row blocks of the gate / up rows
     src.g0 = (uint32_t)(rgate / 4) * (uint32_t)nss * kGroupBytes;
     src.j0 = rgate % 4;
     src.g1 = (uint32_t)(rup / 4) * (uint32_t)nss * kGroupBytes;
@@ -562,7 +568,7 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
 #pragma unroll
             for (int v = 1; v < KS; v++) sum[f] = sum[f] + red[v][f][lane];
           }
-          mlp_epilogue_token(a, off + tok, tv, 32 * blockIdx.x, c, alpha, alpha_u, a.gamma_h[e], sum[0], sum[1], sum[2],
+          mlp_epilogue_token(a, off + tok, tv, 32 * bx, c, alpha, alpha_u, a.gamma_h[e], sum[0], sum[1], sum[2],
                              sum[3]);
         }
       } else {
