@@ -56,6 +56,25 @@ def gemm_bytes(n_active, N, K, rows, E, out_bytes=2):
     return (n_active * weight_bytes(N, K) + rows * (K / 2 + K / 32) + rows * N * out_bytes + (E + 1) * 4 + 2 * E * 4)
 
 
+def fused_step_bytes(n_active, N, K, T, k, E, x_bytes=4):
+    """Algorithmic HBM bytes of the one-launch decode step (route + quantize + GEMM): compressed
+    weights of the experts with tokens, the token rows and ids read once, the routing tables, the
+    activation codes + block scales and the bf16 outputs written once, per-expert scales."""
+    rows = T * k
+    return (n_active * weight_bytes(N, K) + T * K * x_bytes + rows * 4 + rows * 8 + (2 * E + 1) * 4 +
+            rows * (K / 2 + K / 32) + rows * N * 2 + 2 * E * 4)
+
+
+FUSED_KERNEL = "dispatch_gemm_kernel"
+MLP_KEY = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
+
+
+def fused_eligible(cfg):
+    """The library's one-launch condition for moesq_route_quantize_gemm."""
+    rows = cfg.T * cfg.k
+    return not cfg.mlp and not cfg.N2 and rows <= 1024 and 8 * rows <= cfg.E and cfg.K <= 2048
+
+
 def _src_hash():
     h = hashlib.sha256()
     for f in ("gemm.hip", "common.h"):
@@ -117,11 +136,12 @@ def summarize_pmc(argv):
             per_kernel.setdefault(k, {})["write_bytes"] = v * 1024.0 * f_write
     if wl in ("c4", "c3_mlp"):
         # one moesq_expert_mlp call: its gate_up and down kernels (distinct template instances)
-        key = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
+        key = MLP_KEY
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items()
                     if "gemm_tile_kernel" in k or "gemm_decode_kernel" in k)
     else:
-        key = "gemm_decode_kernel" if any("gemm_decode_kernel" in k for k in per_kernel) else "gemm_tile_kernel"
+        key = next((n for n in (FUSED_KERNEL, "gemm_decode_kernel") if any(n in k for k in per_kernel)),
+                   "gemm_tile_kernel")
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     t = json.load(open(path)) if os.path.exists(path) else {}
@@ -150,7 +170,7 @@ def _traffic(kernel_key):
 class Workload:
     """Device buffers, graphs and accounting for one named config."""
 
-    def __init__(self, name, rotate, torch, gen, mq, f16_operand=False):
+    def __init__(self, name, rotate, torch, gen, mq, f16_operand=False, fused=False):
         self.torch, self.gen, self.mq = torch, gen, mq
         self.cfg = cfg = gen.CONFIGS[name]
         self.name = name
@@ -159,6 +179,8 @@ class Workload:
         E, T, k = cfg.E, cfg.T, cfg.k
         self.rows = T * k
         self.tiled = self.kind == "mlp" or self.rows > 16 * E
+        # routing, quantization and the GEMM in one launch (moesq_route_quantize_gemm)
+        self.fused = fused and fused_eligible(cfg)
         # weights: compressed once on the device, then copied for rotation
         self.W = self._weights(0, cfg.N, cfg.K)
         self.W2 = self._weights(1, cfg.N2, cfg.K2) if self.kind != "single" else None
@@ -233,6 +255,10 @@ class Workload:
     def step(self, r):
         mq, cfg, sl = self.mq, self.cfg, self.slots[r]
         rt = sl["rt"]
+        if self.fused:
+            mq.moesq_route_quantize_gemm(sl["ids"], sl["x"], sl["ga"], self.Wc[r], rt=rt, q=sl["q"], s=sl["s"],
+                                         y=sl["y"], workspace=sl["ws_route"])
+            return
         # routing + dispatch quantization (one launch for decode-sized batches)
         mq.moesq_route_quantize(sl["ids"], cfg.E, sl["x"], sl["ga"], rt=rt, q=sl["q"], s=sl["s"], xk=sl["xk"],
                                 workspace=sl["ws_route"])
@@ -252,7 +278,9 @@ class Workload:
         """The dominant kernel launch of a step (enqueued on the current stream)."""
         mq, sl = self.mq, self.slots[r]
         rt = sl["rt"]
-        if self.kind == "mlp":
+        if self.fused:
+            self.step(r)
+        elif self.kind == "mlp":
             mq.moesq_expert_mlp(self.Wc[r], self.W2c[r], sl["q"], sl["s"], sl["ga"], sl["gh"], rt["offsets"],
                                 y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
         else:
@@ -306,13 +334,17 @@ class Workload:
                                     out_bytes=(I / 2 + I / 32) / cfg.N) +
                          gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N2, cfg.K2, self.rows, cfg.E)
                          for sl in self.slots])
-            return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
+            return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, MLP_KEY
+        if self.fused:
+            b = np.mean([fused_step_bytes(int((sl["counts_host"] > 0).sum()), cfg.N, cfg.K, cfg.T, cfg.k, cfg.E,
+                                          x_bytes=2 if cfg.x_bf16 else 4) for sl in self.slots])
+            return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, FUSED_KERNEL
         if decode:
             b = np.mean([gemm_bytes(int((sl["counts_host"] > 0).sum()), cfg.N, cfg.K, self.rows, cfg.E)
                          for sl in self.slots])
             return "hbm", b / 1e9, "GB/s", HBM_PEAK_GBS, "gemm_decode_kernel"
         kept = 0.5 * self.eff_flops_per_step() if self.kind == "mlp" else cfg.N * cfg.K * self.rows
-        kern = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)" if self.kind == "mlp" else "gemm_tile_kernel"
+        kern = MLP_KEY if self.kind == "mlp" else "gemm_tile_kernel"
         return "mfma", kept / 1e12, "TFLOP/s", F16_PEAK_TFLOPS, kern
 
 
@@ -491,6 +523,9 @@ def main(argv=None):
                     help="activation operand of the GEMMs: NVFP4 codes decoded in the kernel, or the quantizer's "
                          "f16 copy; auto = f16 for single-projection weight-streaming (decode) workloads, NVFP4 "
                          "otherwise")
+    ap.add_argument("--dispatch", choices=["fused", "separate"], default="fused",
+                    help="decode step of a single projection: routing, quantization and the GEMM in one launch "
+                         "(moesq_route_quantize_gemm, where it applies) or as two calls")
     ap.add_argument("--sweep", choices=sorted(SWEEP_LAYERS) + ["all"],
                     help="the pages' G x N kernel sweep on one layer shape (one JSON line per point)")
     ap.add_argument("--sweep-kernel", choices=["auto", "decode", "tiled"], default="auto")
@@ -531,8 +566,10 @@ def main(argv=None):
     # the f16 copy pays off in the single-projection weight-streaming kernel; the MLP kernels keep the
     # NVFP4 codes (the MLP epilogue's registers leave the f16-operand form at 2 waves per SIMD)
     decode_shaped = not cfgw.mlp and cfgw.T * cfgw.k <= 16 * cfgw.E
-    f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped)
-    wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand)
+    fused = args.dispatch == "fused" and fused_eligible(cfgw)
+    # the one-launch step builds its f16 operand in LDS and writes no copy
+    f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped and not fused)
+    wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand, fused)
     wl.capture()
     wl.run(args.warmup)
     torch.cuda.synchronize()
@@ -580,7 +617,10 @@ def main(argv=None):
     # whole-step algorithmic GEMM bytes per second (weight-streaming workloads only)
     n_act = np.mean([(sl["counts_host"] > 0).sum() for sl in wl.slots])
     step_gbps = None
-    if wl.kind == "single":
+    if wl.fused:
+        step_gbps = round(fused_step_bytes(n_act, cfg.N, cfg.K, cfg.T, cfg.k, cfg.E,
+                                           x_bytes=2 if cfg.x_bf16 else 4) / t / 1e9, 1)
+    elif wl.kind == "single":
         step_gbps = round(gemm_bytes(n_act, cfg.N, cfg.K, wl.rows, cfg.E) / t / 1e9, 1)
     elif wl.kind == "pair":
         step_gbps = round((gemm_bytes(n_act, cfg.N, cfg.K, wl.rows, cfg.E) +
@@ -593,7 +633,9 @@ def main(argv=None):
             args.workload, cfg.desc, cfg.E, cfg.K, cfg.N, cfg.T, cfg.k, cfg.routing,
             ", then K=%d N=%d" % (cfg.K2, cfg.N2) if cfg.N2 else ""),
             "rows": wl.rows, "weight_copies": wl.R, "graph_replay": "%d steps per graph" % wl.R,
-            "activation_operand": "f16 copy" if f16_operand else "nvfp4",
+            "activation_operand": ("f16, quantized into LDS by the GEMM's workgroups" if wl.fused else
+                                   "f16 copy" if f16_operand else "nvfp4"),
+            "dispatch": "one launch (route+quantize+GEMM)" if wl.fused else "separate launches",
             "step_gbps_algorithmic": step_gbps, "step_us_p10_p50_p90": pcts},
         "roofline": roofline, "cpu_baseline": cpu,
     }

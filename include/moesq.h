@@ -181,6 +181,25 @@ int moesq_route_quantize(void *stream, const int32_t *topk_ids, int64_t T, int32
                          int32_t *dev_status);
 
 /*
+ * Dispatch and grouped GEMM in one call (paper Appendix D.1: routing metadata and the quantized
+ * activations are produced on the device and consumed by the grouped GEMM of Section 2 / 3.4):
+ * moesq_route_quantize(topk_ids, T, k, E, x, ..., gamma = gamma_a, ...) followed by
+ * moesq_grouped_gemm(W, q, s, xk, gamma_a, offsets, rows = T*k, y, y_dtype, flags = 0). Every output
+ * (counts, offsets, sorted_slot, slot_pos, q, s, xk, y, *dev_status) is byte-identical to that pair of
+ * calls. For the smallest decode batches (8 T*k <= E, K <= 2048) it is one kernel launch: each
+ * weight-streaming workgroup ranks the ids of its expert and quantizes that expert's tokens itself, so
+ * no dispatch kernel runs before the GEMM; otherwise it enqueues the two calls (pass xk for the faster
+ * weight-streaming GEMM there).
+ *   W->E == E, W->K == K; other arguments as in the two calls (workspace: as moesq_route_quantize).
+ * Errors: the union of the two calls' argument checks, returned before anything is enqueued.
+ */
+int moesq_route_quantize_gemm(void *stream, const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                              const void *x, int32_t x_dtype, int32_t K, int64_t ld_x, const float *gamma_a,
+                              const moesq_weights *W, int32_t *counts, int32_t *offsets, int32_t *sorted_slot,
+                              int32_t *slot_pos, void *workspace, size_t workspace_bytes, uint8_t *q, uint8_t *s,
+                              void *xk, void *y, int32_t y_dtype, int32_t *dev_status);
+
+/*
  * Grouped sparse GEMM (paper Section 2: Y_e = X_e W_e^T in one launch for variable per-expert token
  * counts; Section 3.4: sparse operand W on the left, Y_e^T = W_e X_e^T; block scales applied in the
  * product, alpha_e = 1/(gamma_w,e * gamma_a,e) applied to the fp32 accumulator).

@@ -164,6 +164,45 @@ static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* 
 }
 
 // MOESQ_F_CAPACITY: offsets holds counts[E] and the rows form E blocks of rows / E (the capacity).
+int moesq_route_quantize_gemm(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                              const void* x, int32_t x_dtype, int32_t K, int64_t ld_x, const float* gamma_a,
+                              const moesq_weights* W, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                              int32_t* slot_pos, void* workspace, size_t workspace_bytes, uint8_t* q, uint8_t* s,
+                              void* xk, void* y, int32_t y_dtype, int32_t* dev_status) {
+  if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  if (!W || W->E != E || W->K != K) return MOESQ_ERR_INVALID_ARG;
+  const int64_t rows = T * (int64_t)k;
+  // the two calls' argument checks, all before anything is enqueued
+  if (T < 0 || k <= 0 || E <= 0 || k > E) return MOESQ_ERR_INVALID_ARG;
+  int rc = gemm_common(W, q, s, xk, gamma_a, offsets, rows, y);
+  if (rc != MOESQ_OK) return rc;
+  if (!counts) return MOESQ_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !sorted_slot || !slot_pos || !x)) return MOESQ_ERR_INVALID_ARG;
+  if (E > kMaxExpertsRoute) return MOESQ_ERR_UNSUPPORTED;
+  if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
+  if (ld_x < K) return MOESQ_ERR_INVALID_ARG;
+  if (k > 512) return MOESQ_ERR_UNSUPPORTED;
+  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4)) return MOESQ_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  if (!dispatch_gemm_fused(T, k, E, K)) {
+    if (!route_quantize_fused(T, k, E)) {
+      const size_t need = route_workspace_bytes(rows, E);
+      if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return MOESQ_ERR_WORKSPACE;
+    }
+    rc = launch_route_quantize(st, topk_ids, T, k, E, x, x_dtype == MOESQ_BF16, K, ld_x, gamma_a, counts, offsets,
+                               sorted_slot, slot_pos, workspace, dev_status, q, s, xk);
+    if (rc != MOESQ_OK) return rc;
+  }
+  GemmArgs a{};
+  a.kl = W->kl; a.gscale = W->gscale;
+  a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = y;
+  a.E = W->E; a.N = W->N; a.K = W->K; a.y_bf16 = y_dtype == MOESQ_BF16; a.gsplit = W->gscale_split;
+  if (dispatch_gemm_fused(T, k, E, K))
+    return launch_dispatch_gemm(st, a, topk_ids, T, k, x, x_dtype == MOESQ_BF16, ld_x, counts, offsets, sorted_slot,
+                                slot_pos, dev_status, q, s, xk);
+  return launch_gemm(st, a, rows);
+}
+
 static int capacity_of(uint32_t flags, int32_t E, int64_t rows, int32_t& cap) {
   cap = 0;
   if (!(flags & MOESQ_F_CAPACITY)) return MOESQ_OK;

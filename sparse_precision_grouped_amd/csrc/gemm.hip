@@ -584,6 +584,244 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
   }
 }
 
+// ==================================================== dispatch + GEMM in one launch (decode) =====
+// Small decode batches: the routing, the activation quantization and the weight-streaming GEMM of one
+// layer in a single launch (the work of route_quantize_kernel followed by gemm_decode_kernel<4, 4, 1,
+// true>, with the same results). Workgroup (x, e) ranks all T*k ids itself to find expert e's count,
+// offset and slots in slot order, issues its first weight loads, then quantizes the expert's tokens
+// (up to kDispTok per pass) into LDS as the f16 operand while those loads are in flight, and runs the
+// decode kernel's K-split MMA loop and fixed-order reduction with B read from LDS. The workgroups of
+// row block 0 also write the routing tables and the q / s (/ xk) rows of their expert, so every output
+// of the two-call path is produced.
+constexpr int kDispTok = 8;          // tokens per pass (LDS rows)
+constexpr int kDispMaxSlots = 1024;  // T*k
+constexpr int kDispMaxK = 2048;
+
+struct DispArgs {
+  const int32_t* ids;
+  int32_t n, k;  // slots T*k, top-k
+  const void* x;
+  int32_t x_bf16;
+  int64_t ld_x;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slot;
+  int32_t* slot_pos;
+  int32_t* dev_status;
+  uint8_t* q;
+  uint8_t* s;
+  uint8_t* xk;  // optional f16 copy of the quantized rows
+};
+
+MOESQ_DEV void lds_xk(XKStage& st, const uint8_t* brow, bool tv, int ss) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st.lo[s] = tv ? *(const u32x4*)(brow + 512 * ss + 32 * s) : z;
+    st.hi[s] = tv ? *(const u32x4*)(brow + 512 * ss + 32 * s + 256) : z;
+  }
+}
+
+// The 8 token values of quantization item gi (row i = gi / gpr of the pass, 8-group gi % gpr), or zeros.
+MOESQ_DEV void load_token8(const DispArgs& d, const int32_t* list, int tb, int gpr, int gi, int nq, float v[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) v[j] = 0.0f;
+  if (gi >= nq) return;
+  const int i = gi / gpr, ch = gi - i * gpr;
+  const int64_t t = list[tb + i] / d.k;
+  if (d.x_bf16) {
+    const uint4 raw = *(const uint4*)((const uint16_t*)d.x + t * d.ld_x + 8 * ch);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      v[2 * j] = bf16_bits_to_f32(wd[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(wd[j] >> 16);
+    }
+  } else {
+    const float4 x0 = *(const float4*)((const float*)d.x + t * d.ld_x + 8 * ch);
+    const float4 x1 = *(const float4*)((const float*)d.x + t * d.ld_x + 8 * ch + 4);
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void dispatch_gemm_kernel(GemmArgs a,
+                                                                                                     DispArgs d) {
+  constexpr int MF = 4, KS = 4, R = kDispMaxSlots / 256;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_act[];  // kDispTok rows of 2K + 16 bytes; then the reduction
+  __shared__ int32_t list[kDispMaxSlots];                            // expert e's slots in slot order
+  __shared__ int32_t ceq[R][4], clt[R][4];
+  const int e = blockIdx.y, bx = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = a.E, K = a.K, N = a.N, nss = K / 256;
+  // ---- routing of expert e
+  int idv[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int f = tid + 256 * r;
+    idv[r] = f < d.n ? d.ids[f] : -1;
+  }
+  uint64_t meq[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const bool valid = idv[r] >= 0 && idv[r] < E;
+    meq[r] = __ballot(idv[r] == e);
+    const uint64_t mlt = __ballot(valid && idv[r] < e);
+    if (lane == 0) {
+      ceq[r][w] = __builtin_popcountll(meq[r]);
+      clt[r][w] = __builtin_popcountll(mlt);
+    }
+  }
+  __syncthreads();
+  int ne = 0, off = 0;
+  int base[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      if (v == w) base[r] = ne;
+      ne += ceq[r][v];
+      off += clt[r][v];
+    }
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    if (idv[r] == e) {
+      const int f = tid + 256 * r;
+      const int rank = base[r] + __builtin_popcountll(meq[r] & below);
+      list[rank] = f;
+      if (bx == 0) {
+        d.sorted_slot[off + rank] = f;
+        d.slot_pos[f] = off + rank;
+      }
+    }
+  }
+  if (bx == 0) {
+    if (tid == 0) {
+      d.counts[e] = ne;
+      d.offsets[e] = off;
+      if (e == E - 1) d.offsets[E] = off + ne;  // all valid slots
+    }
+    if (e == 0) {
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        const int f = tid + 256 * r;
+        if (f < d.n && !(idv[r] >= 0 && idv[r] < E)) {
+          d.slot_pos[f] = -1;
+          if (d.dev_status) *d.dev_status = MOESQ_ERR_INVALID_ARG;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (ne == 0) return;
+  // ---- weights and the K-split MMA, as gemm_decode_kernel<4, 4, 1>
+  const int kw = w, rb0 = bx * MF, n0 = rb0 * 16;
+  const int r16 = lane & 15, c = lane >> 4;
+  const uint32_t ekl = expert_kl_bytes(N, K);
+  const rsrc_t rw = make_rsrc(a.kl + (size_t)e * ekl, ekl);
+  WSrc src;
+  src.g0 = (uint32_t)(rb0 / 4) * (uint32_t)nss * kGroupBytes;
+  src.j0 = 0;
+  src.g1 = 0;
+  src.j1 = 0;
+  const float ga = a.gamma_a[e];
+  const float alpha = 1.0f / (wscale(a, e, n0 >= N / 2) * ga);
+  const int rowb = 2 * K + 16;  // LDS row stride of the f16 activations
+  const int gpr = K / 8;        // 8-groups per row
+  const uint8_t* brow = lds_act + r16 * rowb + 16 * (8 * (c >> 1) + (c & 1));
+  for (int tb = 0; tb < ne; tb += kDispTok) {
+    const int nb = min(kDispTok, ne - tb);
+    const int nq = nb * gpr;
+    // this thread's first 8 token values, loaded before the weights: waiting for them then does not
+    // wait for the weight loads (vector-memory counters complete in issue order)
+    float v[8];
+    load_token8(d, list, tb, gpr, tid, nq, v);
+    WS<MF, false> w0, w1;
+    int ss = kw;
+    if (ss < nss) w0.load(rw, src, lane, ss);
+    if (ss + KS < nss) w1.load(rw, src, lane, ss + KS);
+    // quantize the pass's tokens (as quantize_token_copies: 4 lanes per 32-block) into LDS
+    for (int gi0 = 0; gi0 < nq; gi0 += 256) {
+      const int gi = gi0 + tid;
+      const bool gv = gi < nq;
+      const int i = gv ? gi / gpr : 0, ch = gi - i * gpr;
+      if (gi0 > 0) load_token8(d, list, tb, gpr, gi, nq, v);
+      uint32_t codes, sc;
+      quant8_block4(v, ga, codes, sc);
+      f16x2 sv, unused;
+      e4m3_pair_f16x2(sc, sv, unused);
+      const u32x4 xv = decode_x_group(codes, sv);
+      if (gv) {
+        *(u32x4*)(lds_act + i * rowb + 16 * ch) = xv;
+        if (bx == 0) {
+          const int64_t p = off + tb + i;
+          *(uint32_t*)(d.q + p * (K / 2) + 4 * ch) = codes;
+          if ((lane & 3) == 0) d.s[p * (K / 32) + ch / 4] = (uint8_t)sc;
+          if (d.xk) *(u32x4*)(d.xk + (p * K + 8 * ch) * 2) = xv;
+        }
+      }
+    }
+    __syncthreads();
+    f32x4 acc[MF];
+#pragma unroll
+    for (int f = 0; f < MF; f++) acc[f] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const bool tv = r16 < nb;
+    while (ss < nss) {
+      const int s1 = ss + KS, s2 = ss + 2 * KS, s3 = ss + 3 * KS;
+      {
+        XKStage xs;
+        lds_xk(xs, brow, tv, ss);
+        mma_superstep_xk(acc, w0.w, xs);
+      }
+      if (s2 < nss) w0.load(rw, src, lane, s2);
+      if (s1 < nss) {
+        XKStage xs;
+        lds_xk(xs, brow, tv, s1);
+        mma_superstep_xk(acc, w1.w, xs);
+        if (s3 < nss) w1.load(rw, src, lane, s3);
+      }
+      ss = s2;
+    }
+    // fixed-order K reduction through LDS (reusing the activation rows)
+    __syncthreads();
+    f32x4* red = (f32x4*)lds_act;  // [KS][MF][64]
+#pragma unroll
+    for (int f = 0; f < MF; f++) red[(kw * MF + f) * 64 + lane] = acc[f];
+    __syncthreads();
+    for (int f = kw; f < MF; f += KS) {
+      f32x4 sum = red[f * 64 + lane];
+#pragma unroll
+      for (int v = 1; v < KS; v++) sum = sum + red[(v * MF + f) * 64 + lane];
+      if (tv) store4(a.y, (int64_t)(off + tb + r16) * N + n0 + 16 * f + 4 * c, sum, alpha, a.y_bf16);
+    }
+    __syncthreads();
+  }
+}
+
+// One launch only where it is faster than the two: every workgroup of an expert repeats the
+// quantization of that expert's tokens, which outweighs the saved launch once the batch has more
+// than about one token per eight experts (measured at E = 128, K = 2048, N = 1536: 11.9 vs 14.3 us at
+// T*k = 8, equal at T*k = 32, 34.8 vs 29.2 us at T*k = 128).
+bool dispatch_gemm_fused(int64_t T, int32_t k, int32_t E, int32_t K) {
+  const int64_t n = T * k;
+  return T > 0 && n <= kDispMaxSlots && 8 * n <= (int64_t)E && K <= kDispMaxK && E <= kMaxExpertsRoute;
+}
+
+int launch_dispatch_gemm(hipStream_t st, const GemmArgs& a, const int32_t* ids, int64_t T, int32_t k, const void* x,
+                         bool x_bf16, int64_t ld_x, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                         int32_t* slot_pos, int32_t* dev_status, uint8_t* q, uint8_t* s, void* xk) {
+  DispArgs d{};
+  d.ids = ids; d.n = (int32_t)(T * k); d.k = k;
+  d.x = x; d.x_bf16 = x_bf16; d.ld_x = ld_x;
+  d.counts = counts; d.offsets = offsets; d.sorted_slot = sorted_slot; d.slot_pos = slot_pos;
+  d.dev_status = dev_status; d.q = q; d.s = s; d.xk = (uint8_t*)xk;
+  const size_t lds = (size_t)max(kDispTok * (2 * a.K + 16), 4 * 4 * 64 * 16);
+  hipLaunchKernelGGL(dispatch_gemm_kernel, dim3(a.N / 64, a.E), dim3(256), lds, st, a, d);
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
 // ============================================================================= tiled kernel =====
 // Prefill-sized problems. A workgroup of 8 waves computes 512 weight rows x 128 tokens of one expert
 // (MLP gate_up: 256 gate rows and the matching 256 up rows); a wave owns 64 rows (4 m-fragments)

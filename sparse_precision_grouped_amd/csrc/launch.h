@@ -74,6 +74,13 @@ int launch_gemm(hipStream_t st, const GemmArgs& a, int64_t rows);
 // variant 0 = decode (weight streaming; with gamma_h the MLP gate_up epilogue), 1 = prefill (tiled).
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
 
+// Route + quantize + decode GEMM in one launch for small decode batches (dispatch_gemm_fused): the
+// same outputs as launch_route_quantize followed by the default weight-streaming GEMM with xk.
+bool dispatch_gemm_fused(int64_t T, int32_t k, int32_t E, int32_t K);
+int launch_dispatch_gemm(hipStream_t st, const GemmArgs& a, const int32_t* ids, int64_t T, int32_t k, const void* x,
+                         bool x_bf16, int64_t ld_x, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                         int32_t* slot_pos, int32_t* dev_status, uint8_t* q, uint8_t* s, void* xk);
+
 int launch_combine(hipStream_t st, const void* y, bool y_bf16, const int32_t* slot_pos, const float* w, int64_t T,
                    int32_t k, int32_t H, void* out, bool out_bf16);
 

@@ -34,3 +34,27 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_fused_step_accounting():
+    """The one-launch decode step's algorithmic bytes: every term once, by hand for the benchmark's
+    decode configuration (E=128, K=2048, N=1536, T=16, top-8, fp32 tokens) with 81 active experts."""
+    rows = 16 * 8
+    by_hand = (81 * 1536 * 2048 * 11 / 32      # compressed weights of the experts with tokens
+               + 16 * 2048 * 4                 # token rows, read once
+               + rows * 4                      # ids
+               + rows * 8 + (2 * 128 + 1) * 4  # sorted_slot + slot_pos, counts + offsets
+               + rows * (1024 + 64)            # codes + block scales written
+               + rows * 1536 * 2               # bf16 outputs
+               + 2 * 128 * 4)                  # gamma_w, gamma_a
+    assert bench.fused_step_bytes(81, 1536, 2048, 16, 8, 128) == by_hand
+
+
+def test_fused_eligibility_matches_the_library_limits():
+    import gen
+    import dataclasses
+    assert bench.fused_eligible(dataclasses.replace(gen.CONFIGS["c1"], T=2))   # 16 rows, E = 128
+    assert not bench.fused_eligible(gen.CONFIGS["c1"])       # 128 rows: two launches are faster
+    assert not bench.fused_eligible(gen.CONFIGS["c2"])       # prefill
+    assert not bench.fused_eligible(gen.CONFIGS["c3"])       # two projections, K = 7168
+    assert not bench.fused_eligible(gen.CONFIGS["c3_mlp"])   # the MLP

@@ -140,6 +140,43 @@ def test_route_quantize_validation(L):
     assert call(T=256, k=9, E=16) == EWS   # T*k > 2048
 
 
+def test_route_quantize_gemm_validation(L):
+    class CW(ctypes.Structure):
+        _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                    ("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                    ("gscale", ctypes.c_void_p), ("kl", ctypes.c_void_p), ("gscale_split", ctypes.c_int32)]
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    f = L.moesq_route_quantize_gemm
+    f.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, ctypes.POINTER(CW), vp, vp, vp, vp, vp, sz, vp, vp,
+                  vp, vp, i32, vp]
+    base = dict(ids=FAKE, T=16, k=8, E=128, x=FAKE, dt=1, K=2048, ld=2048, gamma=FAKE, cnt=FAKE, ws=None, q=FAKE,
+                y=FAKE, ydt=1, W=(128, 1536, 2048))
+
+    def call(**kw):
+        a = dict(base, **kw)
+        p = lambda v: _p(v) if v else None  # noqa: E731
+        W = CW(*a["W"], FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+        return f(None, p(a["ids"]), a["T"], a["k"], a["E"], p(a["x"]), a["dt"], a["K"], a["ld"], p(a["gamma"]),
+                 ctypes.byref(W), p(a["cnt"]), _p(FAKE), _p(FAKE), _p(FAKE), p(a["ws"]), 0, p(a["q"]), _p(FAKE), None,
+                 p(a["y"]), a["ydt"], None)
+    assert call(ydt=5) == EARG
+    assert call(W=(64, 1536, 2048)) == EARG   # W->E != E
+    assert call(W=(128, 1536, 1024)) == EARG  # W->K != K
+    assert call(k=129) == EARG
+    assert call(ids=0) == EARG
+    assert call(gamma=0) == EARG
+    assert call(q=0) == EARG
+    assert call(y=0) == EARG
+    assert call(cnt=0) == EARG
+    assert call(dt=7) == EARG
+    assert call(ld=1024) == EARG
+    assert call(E=513, W=(513, 1536, 2048)) == EUNS
+    assert call(x=FAKE + 4) == EUNS
+    assert call(W=(128, 1500, 2048)) == EUNS  # N % 64 != 0
+    # beyond the one-launch paths the routing workspace is required
+    assert call(T=65536) == EWS
+
+
 def test_gemm_and_mlp_validation(L):
     class CW(ctypes.Structure):
         _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),

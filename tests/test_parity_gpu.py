@@ -405,6 +405,135 @@ def test_grouped_gemm_edge_cases():
     assert np.all(host(y) == 0)
 
 
+# ------------------------------------------------- dispatch + GEMM in one call --------------
+def _rqg_check(ids, x, E, ga, Wd, Wo=None, bf16=False, y_dtype=torch.float32, oracle_rows=None):
+    """moesq_route_quantize_gemm byte for byte against moesq_route_quantize + moesq_grouped_gemm (the
+    two calls it replaces, with the f16 operand copy), and its y against the oracle's GEMM on the
+    oracle's routing and quantization."""
+    ids = ids.astype(np.int32)
+    T, k = ids.shape
+    xd = dev(x)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        x = xd.float().cpu().numpy()
+    gad = dev(ga)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rt, q, s, xk, y = mq.moesq_route_quantize_gemm(dev(ids), xd, gad, Wd, xk=True, y_dtype=y_dtype, dev_status=st)
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rt2, q2, s2, xk2 = mq.moesq_route_quantize(dev(ids), E, xd, gad, xk=True, dev_status=st2)
+    y2 = mq.moesq_grouped_gemm(Wd, q2, s2, gad, rt2["offsets"], y_dtype=y_dtype, xk=xk2)
+    assert int(host(st)[0]) == int(host(st2)[0])
+    n_ok = int(host(rt2["offsets"])[-1])
+    for key in ("counts", "offsets", "slot_pos"):
+        assert np.array_equal(host(rt[key]), host(rt2[key])), key
+    assert np.array_equal(host(rt["sorted_slot"])[:n_ok], host(rt2["sorted_slot"])[:n_ok])
+    assert np.array_equal(host(q)[:n_ok], host(q2)[:n_ok]) and np.array_equal(host(s)[:n_ok], host(s2)[:n_ok])
+    assert np.array_equal(host(xk.view(torch.int16))[:n_ok], host(xk2.view(torch.int16))[:n_ok])
+    bits = torch.int32 if y_dtype == torch.float32 else torch.int16
+    assert np.array_equal(host(y.view(bits))[:n_ok], host(y2.view(bits))[:n_ok])
+    if Wo is None:
+        return y
+    R = orc.route(ids, E)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    assert np.array_equal(host(q)[:n_ok], qo) and np.array_equal(host(s)[:n_ok], so)
+    rows = np.arange(n_ok) if oracle_rows is None else oracle_rows
+    ref = orc.grouped_gemm(Wo, qo, so, ga, R["offsets"], rows)
+    got = host(y.to(torch.float32))[rows]
+    err = orc.rel_frobenius(got, ref if y_dtype == torch.float32 else bf16_round(ref))
+    say("route_quantize_gemm rel-Frobenius", err)
+    assert err <= GEMM_TOL
+    return y
+
+
+@pytest.mark.parametrize("name,T", [("c0", None), ("c1", None), ("c1", 2), ("c1", 1)])
+def test_route_quantize_gemm_parity(name, T):
+    """The one-call decode step on the benchmark's decode configuration (E=128, K=2048, N=1536, top-8)
+    at its 16 tokens (two launches) and at 2 and 1 tokens (one launch), and the small case, with
+    distinct per-expert activation scales."""
+    c = single_case(name)
+    ids, x = c["ids"][:T], c["x"][:T]
+    say("route_quantize_gemm", name, "T", ids.shape[0])
+    ga = (c["ga"] * np.linspace(0.5, 2.0, c["E"])).astype(np.float32)
+    off = orc.route(ids, c["E"])["offsets"]
+    Wo = c["Wo"].ensure(np.flatnonzero(np.diff(off) > 0)).as_dict()
+    for ydt in (torch.float32, torch.bfloat16):
+        _rqg_check(ids, x, c["E"], ga, c["Wd"], Wo, y_dtype=ydt)
+
+
+def test_route_quantize_gemm_edges():
+    """Multi-pass experts (more tokens than one LDS pass holds), bf16 input, split tensor scales,
+    invalid ids, the one-launch limits (8 T*k = E, K = 2048) and one past each (two calls), and the
+    smallest K."""
+    rng = np.random.default_rng(23)
+
+    def case(T, k, E, N, K, zipf=False, bf16=False, split=False, bad=False, oracle=True):
+        say("route_quantize_gemm edge T", T, "k", k, "E", E, "N", N, "K", K, "zipf", zipf, "split", split, "bad", bad)
+        if zipf:
+            ids, _ = gen.route_zipf(9, T, E, k, 1.3, 0)
+        else:
+            ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        if bad:
+            ids[1, 0] = E
+            ids[T - 1, k - 1] = -3
+        x = gen.student_t(13, gen.act_stream(T + K + N), T * K).reshape(T, K)
+        ga = (np.float32(orc.global_scale_of(x)) * np.linspace(0.8, 1.25, E)).astype(np.float32)
+        w = (np.random.default_rng(T + N).standard_normal((E, N, K)) * 0.02).astype(np.float32)
+        if split:
+            w[:, N // 2:] *= np.float32(3.0)
+            Wd, Wo = mq.moesq_compress_weights(dev(w), split_halves=True), orc.compress_split(w)
+        else:
+            Wd, Wo = mq.moesq_compress_weights(dev(w)), orc.compress(w)
+        _rqg_check(ids, x, E, ga, Wd, Wo if (oracle and not bad) else None, bf16=bf16)
+
+    case(40, 1, 320, 128, 512, zipf=True)         # hot experts: many tokens, several LDS passes
+    case(2, 4, 64, 256, 2048, bf16=True)
+    case(2, 8, 128, 256, 256, split=True)
+    case(3, 3, 80, 64, 256, bad=True)             # ids outside [0, E)
+    case(12, 1, 96, 64, 2048)                     # 8 T*k = E: one launch
+    case(13, 1, 96, 64, 2048)                     # one token more: two calls
+    case(16, 8, 128, 64, 2048)                    # the decode benchmark's batch shape: two calls
+    case(17, 4, 4, 64, 256)                       # T*k > 16 E: two calls, tiled GEMM
+    case(8, 2, 16, 64, 2304)                     # K > 2048: two calls
+
+
+@pytest.mark.parametrize("T", [2, 16])
+def test_route_quantize_gemm_graph_replays(T):
+    """The one-call step (one launch at 2 tokens, two at 16) captured in a HIP graph and replayed with
+    eager work in between: every replay reproduces the eager outputs bit for bit."""
+    c = single_case("c1")
+    say("route_quantize_gemm graph replays c1 T", T)
+    ids_d, x_d, ga_d = dev(c["ids"][:T]), dev(c["x"][:T]), dev(c["ga"])
+    xk = True if T > 2 else None
+    out = mq.moesq_route_quantize_gemm(ids_d, x_d, ga_d, c["Wd"], xk=xk)
+    rt, q, s, y = out[0], out[1], out[2], out[-1]
+    xk = out[3] if T > 2 else None
+    ref = [host(t.view(torch.int16) if t.dtype == torch.bfloat16 else t).copy() for t in (y, q, rt["slot_pos"])]
+
+    def step():
+        mq.moesq_route_quantize_gemm(ids_d, x_d, ga_d, c["Wd"], rt=rt, q=q, s=s, xk=xk, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        y.zero_()
+        q.zero_()
+        rt["slot_pos"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t.view(torch.int16) if t.dtype == torch.bfloat16 else t) for t in (y, q, rt["slot_pos"])]
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), i
+        _ = torch.ones(1024, device=DEV).sum()
+
+
 # ---------------------------------------------------------------- combine --------------------
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
 def test_combine_parity(ydt):
