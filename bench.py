@@ -170,7 +170,7 @@ def _traffic(kernel_key):
 class Workload:
     """Device buffers, graphs and accounting for one named config."""
 
-    def __init__(self, name, rotate, torch, gen, mq, f16_operand=False, fused=False):
+    def __init__(self, name, rotate, torch, gen, mq, f16_operand=False, fused=False, dyn_scale=False):
         self.torch, self.gen, self.mq = torch, gen, mq
         self.cfg = cfg = gen.CONFIGS[name]
         self.name = name
@@ -180,7 +180,9 @@ class Workload:
         self.rows = T * k
         self.tiled = self.kind == "mlp" or self.rows > 16 * E
         # routing, quantization and the GEMM in one launch (moesq_route_quantize_gemm)
-        self.fused = fused and fused_eligible(cfg)
+        self.fused = fused and fused_eligible(cfg) and not dyn_scale
+        # the activation tensor scale computed on the device inside each step (moesq_route_quantize_dyn)
+        self.dyn_scale = dyn_scale
         # weights: compressed once on the device, then copied for rotation
         self.W = self._weights(0, cfg.N, cfg.K)
         self.W2 = self._weights(1, cfg.N2, cfg.K2) if self.kind != "single" else None
@@ -260,8 +262,12 @@ class Workload:
                                          y=sl["y"], workspace=sl["ws_route"])
             return
         # routing + dispatch quantization (one launch for decode-sized batches)
-        mq.moesq_route_quantize(sl["ids"], cfg.E, sl["x"], sl["ga"], rt=rt, q=sl["q"], s=sl["s"], xk=sl["xk"],
-                                workspace=sl["ws_route"])
+        if self.dyn_scale:
+            mq.moesq_route_quantize_dyn(sl["ids"], cfg.E, sl["x"], gamma_out=sl["ga"], rt=rt, q=sl["q"], s=sl["s"],
+                                        xk=sl["xk"], workspace=sl["ws_route"])
+        else:
+            mq.moesq_route_quantize(sl["ids"], cfg.E, sl["x"], sl["ga"], rt=rt, q=sl["q"], s=sl["s"], xk=sl["xk"],
+                                    workspace=sl["ws_route"])
         if self.kind != "mlp":
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
         if self.kind == "pair":
@@ -526,6 +532,9 @@ def main(argv=None):
     ap.add_argument("--dispatch", choices=["fused", "separate"], default="fused",
                     help="decode step of a single projection: routing, quantization and the GEMM in one launch "
                          "(moesq_route_quantize_gemm, where it applies) or as two calls")
+    ap.add_argument("--act-scale", choices=["static", "dynamic"], default="static",
+                    help="activation tensor scale: a per-expert constant computed once (the model card's stored "
+                         "scale), or Eq. 5 over each step's tokens on the device inside the step")
     ap.add_argument("--sweep", choices=sorted(SWEEP_LAYERS) + ["all"],
                     help="the pages' G x N kernel sweep on one layer shape (one JSON line per point)")
     ap.add_argument("--sweep-kernel", choices=["auto", "decode", "tiled"], default="auto")
@@ -566,10 +575,10 @@ def main(argv=None):
     # the f16 copy pays off in the single-projection weight-streaming kernel; the MLP kernels keep the
     # NVFP4 codes (the MLP epilogue's registers leave the f16-operand form at 2 waves per SIMD)
     decode_shaped = not cfgw.mlp and cfgw.T * cfgw.k <= 16 * cfgw.E
-    fused = args.dispatch == "fused" and fused_eligible(cfgw)
+    fused = args.dispatch == "fused" and fused_eligible(cfgw) and args.act_scale == "static"
     # the one-launch step builds its f16 operand in LDS and writes no copy
     f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped and not fused)
-    wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand, fused)
+    wl = Workload(args.workload, args.rotate, torch, gen, mq, f16_operand, fused, args.act_scale == "dynamic")
     wl.capture()
     wl.run(args.warmup)
     torch.cuda.synchronize()
@@ -636,6 +645,8 @@ def main(argv=None):
             "activation_operand": ("f16, quantized into LDS by the GEMM's workgroups" if wl.fused else
                                    "f16 copy" if f16_operand else "nvfp4"),
             "dispatch": "one launch (route+quantize+GEMM)" if wl.fused else "separate launches",
+            "activation_scale": ("dynamic: Eq. 5 over the step's tokens, on the device" if wl.dyn_scale else
+                                 "static per-expert constant"),
             "step_gbps_algorithmic": step_gbps, "step_us_p10_p50_p90": pcts},
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -181,6 +181,25 @@ int moesq_route_quantize(void *stream, const int32_t *topk_ids, int64_t T, int32
                          int32_t *dev_status);
 
 /*
+ * Dispatch with a dynamic activation tensor scale (paper Section 3.4 / Eq. 5 applied to the step's own
+ * tokens, the on-device counterpart of a calibrated per-expert constant): gamma = Eq. 5 over the
+ * amax of all T x K values of x, computed on the device and written to gamma_out[0 .. E) (every
+ * expert gets the same value; pass gamma_out as gamma_a to the grouped GEMM), then exactly
+ * moesq_route_quantize(..., gamma = gamma_out, ...). Outputs are byte-identical to
+ * moesq_global_scale(x) copied to E entries followed by moesq_route_quantize. On the single-launch
+ * path of moesq_route_quantize, when the tokens take at most 256 KiB (T*K*sizeof(x)), each
+ * workgroup also computes the amax itself, so the call stays one launch; otherwise an amax pre-pass
+ * (three small launches) runs first.
+ *   gamma_out [E] fp32 (device, 4-byte aligned); other arguments as moesq_route_quantize.
+ * Errors: as moesq_route_quantize (gamma_out NULL: MOESQ_ERR_INVALID_ARG).
+ */
+int moesq_route_quantize_dyn(void *stream, const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                             const void *x, int32_t x_dtype, int32_t K, int64_t ld_x, float *gamma_out,
+                             int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
+                             void *workspace, size_t workspace_bytes, uint8_t *q, uint8_t *s, void *xk,
+                             int32_t *dev_status);
+
+/*
  * Dispatch and grouped GEMM in one call (paper Appendix D.1: routing metadata and the quantized
  * activations are produced on the device and consumed by the grouped GEMM of Section 2 / 3.4):
  * moesq_route_quantize(topk_ids, T, k, E, x, ..., gamma = gamma_a, ...) followed by
@@ -266,8 +285,9 @@ int moesq_compress_weights(void *stream, const float *w, int32_t E, int32_t N, i
 /*
  * Tensor scale of Eq. 5 for a device tensor x [rows][ld_x] (fp32 or bf16, first K columns):
  * gamma_out[0] = 448 / (amax / 6) in fp32 (1 for an all-zero tensor). Calibration of the static
- * per-expert activation scale (model card: stored per expert linear); not on the timed path.
- * gamma_out is used as scratch while the call runs.
+ * per-expert activation scale (model card: stored per expert linear), and the pre-pass of
+ * moesq_route_quantize_dyn for batches past its single launch. gamma_out is used as scratch while the
+ * call runs.
  */
 int moesq_global_scale(void *stream, const void *x, int32_t x_dtype, int64_t rows, int32_t K, int64_t ld_x,
                        float *gamma_out);

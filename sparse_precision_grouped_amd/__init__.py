@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "MoesqError", "Weights", "lib", "moesq_route_permute", "moesq_quantize_act", "moesq_route_quantize",
-    "moesq_route_quantize_gemm", "moesq_grouped_gemm",
+    "moesq_route_quantize_dyn", "moesq_route_quantize_gemm", "moesq_grouped_gemm",
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
     "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
     "moesq_prepack_weights", "moesq_kernel_layout_bytes",
@@ -61,6 +61,8 @@ def lib():
         L.moesq_route_quantize.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp,
                                            vp, vp, vp]
         L.moesq_grouped_gemm.argtypes = [vp, W, vp, vp, vp, vp, vp, i64, vp, i32, u32]
+        L.moesq_route_quantize_dyn.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz,
+                                               vp, vp, vp, vp]
         L.moesq_route_quantize_gemm.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, W, vp, vp, vp,
                                                 vp, vp, sz, vp, vp, vp, vp, i32, vp]
         L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
@@ -80,7 +82,8 @@ def lib():
         L.moesq_status_str.argtypes = [i32]
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
-        for name in ("moesq_route_permute", "moesq_route_capacity", "moesq_quantize_act", "moesq_route_quantize", "moesq_route_quantize_gemm", "moesq_grouped_gemm", "moesq_expert_mlp",
+        for name in ("moesq_route_permute", "moesq_route_capacity", "moesq_quantize_act", "moesq_route_quantize", "moesq_route_quantize_dyn", "moesq_route_quantize_gemm", "moesq_grouped_gemm",
+                     "moesq_expert_mlp",
                      "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale",
                      "moesq_prepack_weights"):
             getattr(L, name).restype = ctypes.c_int
@@ -266,6 +269,40 @@ def moesq_route_quantize(topk_ids, E, x, gamma, rt=None, q=None, s=None, xk=None
                                       _p(rt["slot_pos"]), _p(workspace), wsb, _p(q), _p(s),
                                       _p(xk if want_xk else None), _p(dev_status)))
     return (rt, q, s, xk) if want_xk else (rt, q, s)
+
+
+def moesq_route_quantize_dyn(topk_ids, E, x, gamma_out=None, rt=None, q=None, s=None, xk=None, workspace=None,
+                             dev_status=None):
+    """moesq_route_quantize with the activation tensor scale computed on the device from x (Eq. 5 over
+    all of x), written to ``gamma_out`` [E] fp32 (allocated when None). Returns (rt, q, s, gamma_out)
+    or (rt, q, s, xk, gamma_out)."""
+    _dev(topk_ids)
+    _dev(x)
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and x.stride(1) == 1
+    T, k = topk_ids.shape
+    K = x.shape[1]
+    dev = x.device
+    i32 = torch.int32
+    if rt is None:
+        rt = dict(counts=torch.empty(E, dtype=i32, device=dev), offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                  sorted_slot=torch.empty(T * k, dtype=i32, device=dev),
+                  slot_pos=torch.empty(T * k, dtype=i32, device=dev))
+    q = torch.empty((T * k, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((T * k, K // 32), dtype=torch.uint8, device=dev) if s is None else s
+    gamma_out = torch.empty(E, dtype=torch.float32, device=dev) if gamma_out is None else gamma_out
+    want_xk = xk is not None
+    if xk is True:
+        xk = torch.empty((T * k, K), dtype=torch.float16, device=dev)
+    need = moesq_workspace_bytes(WS_ROUTE, T, k, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("moesq_route_quantize_dyn",
+           lib().moesq_route_quantize_dyn(_stream(), _p(topk_ids), T, k, E, _p(x), _dtype_code(x.dtype), K,
+                                          x.stride(0), _p(gamma_out), _p(rt["counts"]), _p(rt["offsets"]),
+                                          _p(rt["sorted_slot"]), _p(rt["slot_pos"]), _p(workspace), wsb, _p(q),
+                                          _p(s), _p(xk if want_xk else None), _p(dev_status)))
+    return (rt, q, s, xk, gamma_out) if want_xk else (rt, q, s, gamma_out)
 
 
 def moesq_route_quantize_gemm(topk_ids, x, gamma_a, W, rt=None, q=None, s=None, xk=None, y=None,

@@ -122,13 +122,14 @@ int moesq_quantize_act(void* stream, const void* x, int32_t x_dtype, int64_t T, 
                          q, s, xk, (!offsets && E > 0) ? (int32_t)(rows / E) : 0);
 }
 
-int moesq_route_quantize(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
-                         int32_t x_dtype, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
-                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* workspace,
-                         size_t workspace_bytes, uint8_t* q, uint8_t* s, void* xk, int32_t* dev_status) {
+static int route_quantize_checked(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                                  const void* x, int32_t x_dtype, int32_t K, int64_t ld_x, const float* gamma,
+                                  float* gamma_out, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                  int32_t* slot_pos, void* workspace, size_t workspace_bytes, uint8_t* q, uint8_t* s,
+                                  void* xk, int32_t* dev_status) {
   // routing arguments, as moesq_route_permute
   if (T < 0 || k <= 0 || E <= 0 || k > E) return MOESQ_ERR_INVALID_ARG;
-  if (!counts || !offsets || !gamma) return MOESQ_ERR_INVALID_ARG;
+  if (!counts || !offsets || !(gamma || gamma_out)) return MOESQ_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !sorted_slot || !slot_pos || !x || !q || !s)) return MOESQ_ERR_INVALID_ARG;
   if (E > kMaxExpertsRoute) return MOESQ_ERR_UNSUPPORTED;
   if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
@@ -136,13 +137,32 @@ int moesq_route_quantize(void* stream, const int32_t* topk_ids, int64_t T, int32
   if (x_dtype != MOESQ_F32 && x_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
   if (K <= 0 || K % 32 != 0 || ld_x < K) return MOESQ_ERR_INVALID_ARG;
   if (k > 512) return MOESQ_ERR_UNSUPPORTED;
-  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4) || !aligned(xk, 16)) return MOESQ_ERR_UNSUPPORTED;
+  if (ld_x % 8 != 0 || !aligned(x, 16) || !aligned(q, 4) || !aligned(xk, 16) || !aligned(gamma_out, 4))
+    return MOESQ_ERR_UNSUPPORTED;
   if (!route_quantize_fused(T, k, E)) {
     const size_t need = route_workspace_bytes(T * k, E);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return MOESQ_ERR_WORKSPACE;
   }
   return launch_route_quantize((hipStream_t)stream, topk_ids, T, k, E, x, x_dtype == MOESQ_BF16, K, ld_x, gamma,
-                               counts, offsets, sorted_slot, slot_pos, workspace, dev_status, q, s, xk);
+                               counts, offsets, sorted_slot, slot_pos, workspace, dev_status, q, s, xk, gamma_out);
+}
+
+int moesq_route_quantize(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
+                         int32_t x_dtype, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* workspace,
+                         size_t workspace_bytes, uint8_t* q, uint8_t* s, void* xk, int32_t* dev_status) {
+  if (!gamma) return MOESQ_ERR_INVALID_ARG;
+  return route_quantize_checked(stream, topk_ids, T, k, E, x, x_dtype, K, ld_x, gamma, nullptr, counts, offsets,
+                                sorted_slot, slot_pos, workspace, workspace_bytes, q, s, xk, dev_status);
+}
+
+int moesq_route_quantize_dyn(void* stream, const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, const void* x,
+                             int32_t x_dtype, int32_t K, int64_t ld_x, float* gamma_out, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* workspace,
+                             size_t workspace_bytes, uint8_t* q, uint8_t* s, void* xk, int32_t* dev_status) {
+  if (!gamma_out) return MOESQ_ERR_INVALID_ARG;
+  return route_quantize_checked(stream, topk_ids, T, k, E, x, x_dtype, K, ld_x, nullptr, gamma_out, counts, offsets,
+                                sorted_slot, slot_pos, workspace, workspace_bytes, q, s, xk, dev_status);
 }
 
 static int gemm_common(const moesq_weights* W, const uint8_t* q, const uint8_t* s, const void* xk,

@@ -10,6 +10,7 @@ namespace moesq {
 constexpr int64_t kRouteSingleMax = 2048;  // slots handled by the one-workgroup routing path
 constexpr int32_t kMaxExpertsRoute = 512;
 constexpr int32_t kFusedRouteMaxK = 32;    // top-k handled by the fused route + quantize kernel
+constexpr int64_t kDynScaleMaxBytes = 256 * 1024;  // token bytes each fused workgroup scans for the dynamic scale
 constexpr int32_t kMaxExpertsGemm = 1024;
 
 constexpr int kFragBytes = 1408;  // 16 rows x 256 K of the kernel weight layout
@@ -48,19 +49,24 @@ int launch_quantize(hipStream_t st, const void* x, bool x_bf16, int64_t T, int32
 int launch_capacity_slots(hipStream_t st, const int32_t* ids, int64_t n, int32_t E, int32_t cap,
                           const int32_t* offsets, const int32_t* slot_pos_prefix, int32_t* slot_pos);
 // Routing + scatter quantization: one fused launch when route_quantize_fused(T, k, E), else the
-// routing kernels followed by the quantizer (ws = the routing workspace).
+// routing kernels followed by the quantizer (ws = the routing workspace). With gamma_out the
+// activation tensor scale is computed on the device (Eq. 5 over all of x) and written to gamma_out[E]
+// (gamma is then not read): inside the fused launch when route_quantize_dyn_fused, else by the amax
+// pre-pass first.
 bool route_quantize_fused(int64_t T, int32_t k, int32_t E);
+bool route_quantize_dyn_fused(int64_t T, int32_t k, int32_t E, int32_t K, bool x_bf16);
 int launch_route_quantize(hipStream_t st, const int32_t* ids, int64_t T, int32_t k, int32_t E, const void* x,
                           bool x_bf16, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status,
-                          uint8_t* q, uint8_t* s, void* xk);
+                          uint8_t* q, uint8_t* s, void* xk, float* gamma_out = nullptr);
 
 int launch_prepack_dense(hipStream_t st, const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
                          uint8_t* kl);
 int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
 
+// Eq. 5 scale of a whole tensor, written to gamma_out[0 .. n_out).
 int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
-                        float* gamma_out);
+                        float* gamma_out, int32_t n_out = 1);
 
 int launch_compress(hipStream_t st, const float* w, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
                     uint8_t* scale, float* gscale, void* ws, int32_t* dev_status);

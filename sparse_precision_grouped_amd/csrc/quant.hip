@@ -9,6 +9,77 @@
 
 namespace moesq {
 
+// max |x| over the 8-groups g = first, first + stride, ... < n of a [rows][ld] tensor with gpr 8-groups
+// per row (K % 8 == 0, ld % 8 == 0, 16-byte aligned): U independent loads in flight per round (an index
+// past the end re-reads the last group, which leaves the max unchanged).
+template <int U, bool BF16>
+MOESQ_DEV float amax_groups_t(const void* __restrict__ x, int32_t n, int32_t gpr, int64_t ld, int32_t first,
+                              int32_t stride) {
+  float m = 0.0f;
+  for (int32_t g0 = first; g0 < n; g0 += U * stride) {
+    // addresses first, then every load, then the reductions, so the U loads are in flight together
+    int64_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int32_t g = min(g0 + u * stride, n - 1);
+      const int32_t r = g / gpr;
+      off[u] = (int64_t)r * ld + 8 * (int64_t)(g - r * gpr);
+    }
+    if (BF16) {
+      uint4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) raw[u] = *(const uint4*)((const uint16_t*)x + off[u]);
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(wd[j] & 0xFFFFu)));
+          m = __builtin_fmaxf(m, __builtin_fabsf(bf16_bits_to_f32(wd[j] >> 16)));
+        }
+      }
+    } else {
+      float4 a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        a[u] = *(const float4*)((const float*)x + off[u]);
+        b[u] = *(const float4*)((const float*)x + off[u] + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a[u].x), __builtin_fabsf(a[u].y)),
+                                               __builtin_fmaxf(__builtin_fabsf(a[u].z), __builtin_fabsf(a[u].w))));
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(b[u].x), __builtin_fabsf(b[u].y)),
+                                               __builtin_fmaxf(__builtin_fabsf(b[u].z), __builtin_fabsf(b[u].w))));
+      }
+    }
+  }
+  return m;
+}
+
+template <int U>
+MOESQ_DEV float amax_groups(const void* __restrict__ x, int x_bf16, int32_t n, int32_t gpr, int64_t ld, int32_t first,
+                            int32_t stride) {
+  return x_bf16 ? amax_groups_t<U, true>(x, n, gpr, ld, first, stride)
+                : amax_groups_t<U, false>(x, n, gpr, ld, first, stride);
+}
+
+// Workgroup-wide max of m (256 threads; wmax: 4 floats of LDS).
+MOESQ_DEV float block_max256(float m, float* wmax) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+  if (lane == 0) wmax[w] = m;
+  __syncthreads();
+  return __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+}
+
+// This thread's share of the amax of |x| over rows [0, T) x [0, K) scanned by one workgroup of 256
+// threads (16 loads in flight); block_max256 of it gives the tensor's amax.
+MOESQ_DEV float thread_amax(const void* __restrict__ x, int x_bf16, int64_t T, int32_t K, int64_t ld_x) {
+  return amax_groups<16>(x, x_bf16, (int32_t)(T * (K / 8)), K / 8, ld_x, threadIdx.x, 256);
+}
+
 // Fused dispatch + quantization: one workgroup per token. Its waves take the token's 512-element
 // chunks (wave w: chunks w, w+4, ...), read them once, quantize them (a lane holds 8 consecutive
 // values, four lanes per 32-block, block amax by a 4-lane max reduction) and write the codes to every
@@ -170,8 +241,9 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
     const int32_t* __restrict__ ids, int32_t k, int32_t E, const void* __restrict__ x, int x_bf16, int32_t K,
     int64_t ld_x, const float* __restrict__ gamma, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos, int32_t* dev_status, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ s, uint8_t* __restrict__ xk) {
+    uint8_t* __restrict__ s, uint8_t* __restrict__ xk, float* __restrict__ gamma_out) {
   __shared__ int32_t hist[kMaxExpertsRoute];
+  __shared__ float wmax[4];
   __shared__ int32_t pos[kMaxExpertsRoute + 1];
   __shared__ float gam_all[kMaxExpertsRoute];  // all tensor scales: no load that waits on an id
   __shared__ int32_t wsum[4];
@@ -193,6 +265,9 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
     const int64_t f = tid + (int64_t)r * 256;
     ev[r] = f < n ? ids[f] : -1;
   }
+  // dynamic tensor scale: this thread's part of the amax over all T x K values, loaded together with
+  // the ids (every workgroup scans the whole tensor itself; max is order-free, so all agree)
+  const float am_part = gamma_out ? thread_amax(x, x_bf16, gridDim.x, K, ld_x) : 0.0f;
   int e_my = -1;
   if (tid < k) {
     e_my = ids[f0 + tid];
@@ -200,7 +275,15 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
   }
   for (int i = tid; i < E; i += 256) {
     hist[i] = 0;
-    gam_all[i] = gamma[i];
+    if (!gamma_out) gam_all[i] = gamma[i];
+  }
+  if (gamma_out) {
+    // Eq. 5 from the tensor amax; workgroup 0 publishes it as the per-expert scales the GEMM reads
+    const float g = global_scale_from_amax(block_max256(am_part, wmax));
+    for (int i = tid; i < E; i += 256) {
+      gam_all[i] = g;
+      if (blockIdx.x == 0) gamma_out[i] = g;
+    }
   }
   if (tid < k) {
     mine[tid] = e_my;
@@ -251,17 +334,34 @@ bool route_quantize_fused(int64_t T, int32_t k, int32_t E) {
   return T > 0 && T * k <= kRouteSingleMax && k <= kFusedRouteMaxK && E <= kMaxExpertsRoute;
 }
 
+bool route_quantize_dyn_fused(int64_t T, int32_t k, int32_t E, int32_t K, bool x_bf16) {
+  return route_quantize_fused(T, k, E) && T * K * (x_bf16 ? 2 : 4) <= kDynScaleMaxBytes;
+}
+
 int launch_route_quantize(hipStream_t st, const int32_t* ids, int64_t T, int32_t k, int32_t E, const void* x,
                           bool x_bf16, int32_t K, int64_t ld_x, const float* gamma, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws, int32_t* dev_status,
-                          uint8_t* q, uint8_t* s, void* xk) {
-  if (!route_quantize_fused(T, k, E)) {
+                          uint8_t* q, uint8_t* s, void* xk, float* gamma_out) {
+  const bool one = gamma_out ? route_quantize_dyn_fused(T, k, E, K, x_bf16) : route_quantize_fused(T, k, E);
+  if (!one) {
+    if (gamma_out) {
+      // amax pre-pass: Eq. 5 over the whole tensor, broadcast to the E per-expert scales
+      const int rc = launch_global_scale(st, x, x_bf16, T, K, ld_x, gamma_out, E);
+      if (rc != MOESQ_OK) return rc;
+      gamma = gamma_out;
+    }
+    if (route_quantize_fused(T, k, E)) {
+      hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, ids, k, E, x, (int)x_bf16, K,
+                         ld_x, gamma, counts, offsets, sorted_slot, slot_pos, dev_status, q, s, (uint8_t*)xk,
+                         (float*)nullptr);
+      return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+    }
     const int rc = launch_route(st, ids, T * k, E, counts, offsets, sorted_slot, slot_pos, ws, dev_status);
     if (rc != MOESQ_OK) return rc;
     return launch_quantize(st, x, x_bf16, T, K, ld_x, slot_pos, k, gamma, offsets, E, q, s, xk);
   }
   hipLaunchKernelGGL(route_quantize_kernel, dim3((unsigned)T), dim3(256), 0, st, ids, k, E, x, (int)x_bf16, K, ld_x,
-                     gamma, counts, offsets, sorted_slot, slot_pos, dev_status, q, s, (uint8_t*)xk);
+                     gamma, counts, offsets, sorted_slot, slot_pos, dev_status, q, s, (uint8_t*)xk, gamma_out);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 
@@ -554,37 +654,49 @@ int launch_prepack_dense(hipStream_t st, const uint8_t* codes, const uint8_t* sc
 // amax of a [rows][K] tensor (leading dimension ld) accumulated as float bits in out[0], then
 // replaced in place by gamma = 448 / (amax / 6).
 __global__ __launch_bounds__(256) void amax_rows_kernel(const void* __restrict__ x, int x_bf16, int64_t rows,
-                                                        int32_t K, int64_t ld, uint32_t* __restrict__ out) {
-  const int64_t n = rows * (int64_t)K;
+                                                        int32_t K, int64_t ld, int vec, uint32_t* __restrict__ out) {
+  __shared__ float wmax[4];
   float m = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / K, c = i % K;
-    const float v = x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[r * ld + c]) : ((const float*)x)[r * ld + c];
-    m = __builtin_fmaxf(m, __builtin_fabsf(v));
+  if (vec) {
+    m = amax_groups<4>(x, x_bf16, (int32_t)(rows * (K / 8)), K / 8, ld, blockIdx.x * 256 + threadIdx.x,
+                       gridDim.x * 256);
+  } else {
+    const int64_t n = rows * (int64_t)K;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+      const int64_t r = i / K, c = i % K;
+      const float v = x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[r * ld + c]) : ((const float*)x)[r * ld + c];
+      m = __builtin_fmaxf(m, __builtin_fabsf(v));
+    }
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
-  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(out, __float_as_uint(m));
+  m = block_max256(m, wmax);
+  if (threadIdx.x == 0 && m > 0.0f) atomicMax(out, __float_as_uint(m));  // one device atomic per block
 }
 
-__global__ void finalize_scale_kernel(uint32_t* out) {
-  if (threadIdx.x == 0) {
-    const float g = global_scale_from_amax(__uint_as_float(out[0]));
-    out[0] = __float_as_uint(g);
-  }
+// Eq. 5 from the amax bits in out[0], written to out[0 .. n) (one block; the copies are written before
+// out[0] is replaced, after a barrier).
+__global__ void finalize_scale_kernel(uint32_t* out, int32_t n) {
+  const float g = global_scale_from_amax(__uint_as_float(out[0]));
+  __syncthreads();
+  for (int i = threadIdx.x + 1; i < n; i += blockDim.x) out[i] = __float_as_uint(g);
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = __float_as_uint(g);
 }
 
 int launch_global_scale(hipStream_t st, const void* x, bool x_bf16, int64_t rows, int32_t K, int64_t ld,
-                        float* gamma_out) {
+                        float* gamma_out, int32_t n_out) {
   uint32_t* o = (uint32_t*)gamma_out;
   hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, o, 1);
   const int64_t n = rows * (int64_t)K;
   if (n > 0) {
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(amax_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, rows, K, ld, o);
+    // 8-value vector loads when the rows allow them (and the 8-group count fits 32 bits)
+    const bool vec = K % 8 == 0 && ld % 8 == 0 && ((uintptr_t)x % 16) == 0 && n / 8 < ((int64_t)1 << 31);
+    const int64_t per = vec ? n / 8 : n;
+    int64_t blocks = (per + 1023) / 1024;  // about 4 items per thread
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(amax_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, (int)x_bf16, rows, K, ld,
+                       (int)vec, o);
   }
-  hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(64), 0, st, o);
+  hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(256), 0, st, o, n_out);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

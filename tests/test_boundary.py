@@ -140,6 +140,28 @@ def test_route_quantize_validation(L):
     assert call(T=256, k=9, E=16) == EWS   # T*k > 2048
 
 
+def test_route_quantize_dyn_validation(L):
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    f = L.moesq_route_quantize_dyn
+    f.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
+    base = dict(ids=FAKE, T=16, k=8, E=128, x=FAKE, dt=1, K=2048, ld=2048, g=FAKE, cnt=FAKE, ws=None, q=FAKE)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        p = lambda v: _p(v) if v else None  # noqa: E731
+        return f(None, p(a["ids"]), a["T"], a["k"], a["E"], p(a["x"]), a["dt"], a["K"], a["ld"], p(a["g"]),
+                 p(a["cnt"]), _p(FAKE), _p(FAKE), _p(FAKE), p(a["ws"]), 0, p(a["q"]), _p(FAKE), None, None)
+    assert call(g=0) == EARG              # gamma_out is required
+    assert call(g=FAKE + 2) == EUNS       # misaligned gamma_out
+    assert call(k=129) == EARG
+    assert call(ids=0) == EARG
+    assert call(q=0) == EARG
+    assert call(dt=7) == EARG
+    assert call(K=48, ld=48) == EARG
+    assert call(E=513) == EUNS
+    assert call(T=65536) == EWS
+
+
 def test_route_quantize_gemm_validation(L):
     class CW(ctypes.Structure):
         _fields_ = [("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),

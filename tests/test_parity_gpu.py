@@ -308,10 +308,60 @@ def test_route_quantize_invalid_ids():
     assert np.array_equal(host(q), host(q2)) and np.array_equal(host(s), host(s2))
 
 
+def _route_quantize_dyn_check(ids, x, E, bf16=False):
+    """moesq_route_quantize_dyn: the tensor scale against the oracle's Eq. 5 over all of x, the codes
+    against the oracle's dispatch quantizer with that scale, and every output byte for byte against
+    moesq_global_scale + moesq_route_quantize."""
+    ids = ids.astype(np.int32)
+    T, k = ids.shape
+    xd = dev(x)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        x = xd.float().cpu().numpy()
+    rt, q, s, xk, g = mq.moesq_route_quantize_dyn(dev(ids), E, xd, xk=True)
+    gam = np.float32(orc.global_scale_of(x))
+    assert np.all(host(g) == gam)
+    R = orc.route(ids, E)
+    for key in ("counts", "offsets", "sorted_slot", "slot_pos"):
+        assert np.array_equal(host(rt[key]), R[key]), key
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], np.full(E, gam, np.float32))
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    ga2 = mq.moesq_global_scale(xd).expand(E).contiguous()
+    rt2, q2, s2, xk2 = mq.moesq_route_quantize(dev(ids), E, xd, ga2, xk=True)
+    assert np.array_equal(host(q), host(q2)) and np.array_equal(host(s), host(s2))
+    assert np.array_equal(host(xk.view(torch.int16)), host(xk2.view(torch.int16)))
+
+
+def test_route_quantize_dynamic_scale():
+    """The dynamic activation tensor scale: in the single launch (c1's 16 fp32 tokens of 2048, 128 KiB),
+    past the token-byte budget (amax pre-pass, then the single-launch routing), past the routing's
+    single launch (pre-pass, routing kernels, quantizer), bf16 tokens, one token, all-zero tokens."""
+    c = single_case("c1")
+    say("route+quantize dynamic scale c1")
+    _route_quantize_dyn_check(c["ids"], c["x"], c["E"])
+    rng = np.random.default_rng(29)
+
+    def case(T, k, E, K, bf16=False, zero=False):
+        say("route+quantize dynamic scale T", T, "k", k, "E", E, "K", K, "bf16", bf16, "zero", zero)
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        x = gen.student_t(31, gen.act_stream(T + K), T * K).reshape(T, K)
+        if zero:
+            x[:] = 0.0
+        _route_quantize_dyn_check(ids, x, E, bf16=bf16)
+
+    case(64, 8, 128, 2048)              # 512 KiB of tokens: pre-pass + single-launch routing
+    case(64, 8, 384, 7168, bf16=True)   # the decode MLP's tokens
+    case(300, 8, 64, 256)               # T*k > 2048: pre-pass + routing kernels + quantizer
+    case(1, 4, 16, 512)
+    case(8, 2, 8, 256, zero=True)       # amax 0: gamma = 1, every code 0
+
+
 def test_global_scale_bitexact():
     say("global scale")
     for x in (gen.student_t(4, gen.act_stream(2), 300 * 256).reshape(300, 256),
-              gen.normal(4, gen.act_stream(3), 5 * 4096).reshape(5, 4096), np.zeros((2, 64), np.float32)):
+              gen.normal(4, gen.act_stream(3), 5 * 4096).reshape(5, 4096), np.zeros((2, 64), np.float32),
+              gen.normal(5, gen.act_stream(4), 7 * 37).reshape(7, 37),          # K % 8 != 0: element path
+              gen.student_t(6, gen.act_stream(5), 64 * 7168).reshape(64, 7168)):
         g = mq.moesq_global_scale(dev(x))
         assert host(g)[0] == np.float32(orc.global_scale_of(x))
         gb = mq.moesq_global_scale(torch.from_numpy(x).to(torch.bfloat16).to(DEV))
