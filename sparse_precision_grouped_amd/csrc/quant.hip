@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
   __shared__ float gam_all[kMaxExpertsRoute];  // all tensor scales: no load that waits on an id
   __shared__ int32_t wsum[4];
   __shared__ int32_t mine[kFusedRouteMaxK];
-  __shared__ int32_t rank[kFusedRouteMaxK];
+  __shared__ int32_t wcnt[4][kFusedRouteMaxK];  // per wave: earlier slots with copy j's expert
   __shared__ int32_t dst[kFusedRouteMaxK];
   __shared__ float gam[kFusedRouteMaxK];
   constexpr int R = kRouteSingleMax / 256;
@@ -285,10 +285,7 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
       if (blockIdx.x == 0) gamma_out[i] = g;
     }
   }
-  if (tid < k) {
-    mine[tid] = e_my;
-    rank[tid] = 0;
-  }
+  if (tid < k) mine[tid] = e_my;
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; r++)
@@ -301,23 +298,29 @@ __global__ __launch_bounds__(256) void route_quantize_kernel(
       if (i < E) counts[i] = hist[i];
     }
   }
-  // rank of copy j = number of slots f < f0 + j routed to the same expert; only rounds holding
-  // such slots take part
+  // rank of copy j = number of slots f < f0 + j routed to the same expert: each wave counts its own
+  // slots with ballots (only rounds holding such slots take part) for 8 copies at a time, and the
+  // wave counts are added after one barrier
   const int nr = (int)((f0 + k + 255) / 256);
-  for (int j = 0; j < k; j++) {
-    const int ej = mine[j];  // uniform over the workgroup
-    if (ej < 0) continue;
-    int c = 0;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int ej[8];
 #pragma unroll
-    for (int r = 0; r < R; r++)
-      if (r < nr) c += __builtin_popcountll(__ballot(ev[r] == ej && tid + (int64_t)r * 256 < f0 + j));
-    if (lane == 0 && c) atomicAdd(&rank[j], c);
+    for (int u = 0; u < 8; u++) ej[u] = j0 + u < k ? mine[j0 + u] : -1;  // uniform over the workgroup
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      if (ej[u] < 0) continue;
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < R; r++)
+        if (r < nr) c += __builtin_popcountll(__ballot(ev[r] == ej[u] && tid + (int64_t)r * 256 < f0 + j0 + u));
+      if (lane == 0) wcnt[w][j0 + u] = c;
+    }
   }
   __syncthreads();
   if (tid < k) {
     int32_t p = -1;
     if (e_my >= 0) {
-      p = pos[e_my] + rank[tid];
+      p = pos[e_my] + wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
       sorted_slot[p] = (int32_t)(f0 + tid);
     } else if (dev_status) {
       *dev_status = MOESQ_ERR_INVALID_ARG;
