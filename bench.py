@@ -384,7 +384,19 @@ def cpu_baseline(wl, orc, gen, max_reps=3):
     t = float(np.median(times))
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": tflops_eff(N, K, n_rows, t), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample + ", median of %d run(s), %.3f s each" % (len(times), t)}
+            "sample": sample + ", median of %d run(s), %.3f s each" % (len(times), t), "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # Kernel sweep of the pages' Appendix D.2 (Table 8 layer shapes, per-expert token counts following the
