@@ -432,6 +432,46 @@ def test_grouped_gemm_deterministic_and_variants_agree():
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_every_call_deterministic(kernel):
+    """Every call of the path, run twice on the same inputs, gives bitwise-identical outputs (no
+    atomics decide a result): routing + quantization (fixed and dynamic scale), the one-call decode
+    step, the MLP on both kernel families (with its fp32 gate_up dump and the h codes) and the
+    combine."""
+    cfg = gen.CONFIGS["t_mlp"]
+    say("determinism", kernel)
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    x = dev(gen.activations(cfg, 0, T, H))
+    ids, wts = gen.routing(cfg)
+    ids_d, wts_d = dev(ids), dev(wts)
+    ga = mq.moesq_global_scale(x).expand(E).contiguous()
+    gh = torch.full((E,), cfg.gamma_h, dtype=torch.float32, device=DEV)
+
+    def run():
+        out = {}
+        rt, q, s, xk = mq.moesq_route_quantize(ids_d, E, x, ga, xk=True)
+        out.update(q=q, s=s, xk=xk.view(torch.int16), slot_pos=rt["slot_pos"], offsets=rt["offsets"])
+        rtd, qd, sd, gd = mq.moesq_route_quantize_dyn(ids_d, E, x)
+        out.update(qd=qd, sd=sd, gd=gd)
+        y2, ws = mq.moesq_expert_mlp(W13, W2, q, s, ga, gh, rt["offsets"], y_dtype=torch.float32,
+                                     flags=mq.F_DUMP_GATEUP | kf)
+        hq, hs, dump = mq.mlp_workspace_views(ws, T * k, I, dump=True)
+        out.update(y2=y2, hq=hq.clone(), hs=hs.clone(), dump=dump.clone())
+        out["comb"] = mq.moesq_unpermute_combine(y2, rt["slot_pos"], wts_d, out_dtype=torch.float32)
+        rtg, qg, sg, yg = mq.moesq_route_quantize_gemm(ids_d[:1], x[:1], ga, W13)
+        out.update(yg=yg.view(torch.int16), qg=qg)
+        torch.cuda.synchronize()
+        return {key: host(v).copy() for key, v in out.items()}
+
+    a, b = run(), run()
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_grouped_gemm_edge_cases():
     """All rows to one expert, T = 1 / k = 1, all-zero activations."""
     c = single_case("c0")
