@@ -38,6 +38,8 @@ if ROOT not in sys.path:
 METRIC = "grouped sparse-NVFP4 GEMM eff. TFLOP/s + HBM GB/s (decode & prefill, 1 GPU)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16 MFMA; the 2:4 sparse MFMA does kept products at this rate x2 eff
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 / FP6 MFMA
 BITS_PER_WEIGHT = 2.75       # paper Appendix A, Eq. 7
 
 
@@ -628,6 +630,12 @@ def main(argv=None):
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
                 "kernel_ms": round(kms, 5)}
+    if bound == "mfma":
+        # the same launch against the chip's dense FP8 and FP4 peaks, on dense-equivalent flops
+        # (2 x the kept flops)
+        roofline["dense_equivalent_tflops"] = round(2 * achieved, 1)
+        roofline["frac_of_fp8_dense_peak"] = round(2 * achieved / FP8_PEAK_TFLOPS, 4)
+        roofline["frac_of_fp4_dense_peak"] = round(2 * achieved / FP4_PEAK_TFLOPS, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
