@@ -99,15 +99,17 @@ def calibrate_copy(torch, iters=5):
     print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "iters": iters}))
 
 
-def _pmc_means(csv_path, match):
+def _pmc_means(csv_path, match, grid=None):
     """Mean per-dispatch value (KiB) and dispatch count of every counter in a rocprofv3 counter CSV,
-    per kernel whose name contains `match`."""
+    per kernel whose name contains `match` (and, with `grid`, only dispatches of that many work-items)."""
     import csv
     acc = {}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             k = r["Kernel_Name"]
             if match not in k:
+                continue
+            if grid is not None and "gemm_" in k and int(r["Grid_Size"]) != grid:
                 continue
             key = (k.split("(")[0], r["Counter_Name"])
             acc.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -119,8 +121,13 @@ def summarize_pmc(argv):
     kernels' FETCH_SIZE / WRITE_SIZE by the copy calibration and record bytes per dominant launch in
     profiles/traffic.json (keyed by workload and kernel, tagged with the kernel source hash)."""
     wl, fcsv, wcsv, cf, cw = argv
-    fetch = _pmc_means(fcsv, "gemm_")
-    write = _pmc_means(wcsv, "gemm_")
+    import gen
+    cfg = gen.CONFIGS[wl]
+    # two projections with the same weight-streaming kernel: keep the first (gate_up) launches, told
+    # apart by their grid (N/64 x E workgroups of 256 threads)
+    grid = (cfg.N // 64) * cfg.E * 256 if cfg.N2 and not cfg.mlp else None
+    fetch = _pmc_means(fcsv, "gemm_", grid)
+    write = _pmc_means(wcsv, "gemm_", grid)
     # the calibration run's copy launch is the one that reads the most (the fill before it reads nothing)
     cf_all = {k: v for (k, c), v in _pmc_means(cf, "").items() if c == "FETCH_SIZE"}
     copy_name = max(cf_all, key=lambda k: cf_all[k][0])
