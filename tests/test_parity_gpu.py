@@ -586,6 +586,27 @@ def test_route_quantize_gemm_edges():
     case(8, 2, 16, 64, 2304)                     # K > 2048: two calls
 
 
+def test_empty_batch_one_call_and_dynamic_scale():
+    """T = 0 through the one-call step and the dynamic-scale dispatch: counts and offsets are written
+    as zeros, nothing else is touched, the dynamic scale of an empty tensor is Eq. 5's 1."""
+    say("empty batch: route_quantize_gemm, route_quantize_dyn")
+    c = single_case("c0")
+    E, K = c["E"], c["K"]
+    empty = lambda *shape: torch.empty(shape, dtype=torch.int32, device=DEV)  # noqa: E731
+    for call in ("gemm", "dyn"):
+        cnt = torch.full((E,), 5, dtype=torch.int32, device=DEV)
+        off = torch.full((E + 1,), 5, dtype=torch.int32, device=DEV)
+        rt = dict(counts=cnt, offsets=off, sorted_slot=empty(0), slot_pos=empty(0))
+        x = torch.zeros((0, K), device=DEV)
+        if call == "gemm":
+            mq.moesq_route_quantize_gemm(empty(0, c["k"]), x, dev(c["ga"]), c["Wd"], rt=rt)
+        else:
+            g = torch.full((E,), 7.0, device=DEV)
+            mq.moesq_route_quantize_dyn(empty(0, c["k"]), E, x, gamma_out=g, rt=rt)
+            assert np.all(host(g) == 1.0)
+        assert not host(cnt).any() and not host(off).any(), call
+
+
 @pytest.mark.parametrize("T", [2, 16])
 def test_route_quantize_gemm_graph_replays(T):
     """The one-call step (one launch at 2 tokens, two at 16) captured in a HIP graph and replayed with
