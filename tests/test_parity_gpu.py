@@ -711,6 +711,37 @@ def test_mlp_parity_tiny(kernel):
     assert orc.rel_frobenius(host(out), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("I", [512, 1024])
+def test_mlp_streaming_block_renumbering(I):
+    """The weight-streaming MLP gate_up renumbers its workgroups (pairs sharing a unit's mask and scale
+    lines on one XCD) when I/32 is a multiple of 16: its smallest cases (16 and 32 column blocks)
+    against the oracle, gate_up outputs and the requantized h."""
+    E, H, T, k = 4, 256, 32, 2
+    say("mlp streaming renumbering I", I)
+    rng = np.random.default_rng(I)
+    w13 = (rng.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    W13o, W2o = orc.compress(w13), orc.compress(w2)
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    x = gen.student_t(70, gen.act_stream(I), T * H).reshape(T, H)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    R = orc.route(ids, E)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, R["offsets"], ga)
+    # gamma_h calibrated on this h (Eq. 5 over the oracle's SwiGLU output)
+    h = orc.swiglu(orc.grouped_gemm(W13o, qo, so, ga, R["offsets"]))
+    gh = np.full(E, orc.global_scale(float(np.abs(h).max())), np.float32)
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"])
+    rows = int(R["offsets"][-1])
+    y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
+                                flags=mq.F_DUMP_GATEUP | mq.F_FORCE_DECODE)
+    hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
+    assert orc.rel_frobenius(host(dump), M["y13"]) <= GEMM_TOL
+    assert np.mean(host(hs) != M["hs"]) <= 1e-3
+    assert np.mean(orc.dequant(host(hq), host(hs)) != orc.dequant(M["hq"], M["hs"])) <= 2e-3
+    assert orc.rel_frobenius(host(y), M["y2"]) <= 1e-2
+
+
 @pytest.mark.parametrize("kernel", ["streaming", "tiled"])
 def test_split_tensor_scales(kernel):
     """Gate and up kept as separate linears, each with its own Eq. 5 tensor scale (the model card's
