@@ -548,7 +548,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--operand", choices=["auto", "nvfp4", "f16"], default="auto",
                     help="activation operand of the GEMMs: NVFP4 codes decoded in the kernel, or the quantizer's "
-                         "f16 copy; auto = f16 for single-projection weight-streaming (decode) workloads, NVFP4 "
+                         "f16 copy; auto = f16 for weight-streaming (decode-sized) workloads, NVFP4 "
                          "otherwise")
     ap.add_argument("--dispatch", choices=["fused", "separate"], default="fused",
                     help="decode step of a single projection: routing, quantization and the GEMM in one launch "
@@ -593,9 +593,8 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     cfgw = gen.CONFIGS[args.workload]
-    # the f16 copy pays off in the single-projection weight-streaming kernel; the MLP kernels keep the
-    # NVFP4 codes (the MLP epilogue's registers leave the f16-operand form at 2 waves per SIMD)
-    decode_shaped = not cfgw.mlp and cfgw.T * cfgw.k <= 16 * cfgw.E
+    # the f16 copy pays off in the weight-streaming kernels; the tiled kernels keep the NVFP4 codes
+    decode_shaped = cfgw.T * cfgw.k <= 16 * cfgw.E
     fused = args.dispatch == "fused" and fused_eligible(cfgw) and args.act_scale == "static"
     # the one-launch step builds its f16 operand in LDS and writes no copy
     f16_operand = args.operand == "f16" or (args.operand == "auto" and decode_shaped and not fused)

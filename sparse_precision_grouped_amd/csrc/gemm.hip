@@ -475,10 +475,13 @@ MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib,
 // the gate and up sums of 32 intermediate columns, one 32-block per token: SwiGLU and the NVFP4
 // requantization of h run in the same epilogue as the tiled kernel's.
 // Weight streaming here is bound by the bytes a CU keeps in flight, so the register budget is capped
-// at 168 VGPRs for 3 waves per SIMD (no spills; the f16-operand forms of the dense control and of the
-// MLP epilogue need more and keep 2).
+// at 168 VGPRs for 3 waves per SIMD (no spills). The f16-operand forms of the dense control and of the
+// MLP epilogue need more with two activation stages, so they hold one: each step's activations are
+// reloaded right after that step's MFMAs, while the weights stay double-buffered.
 template <int MF, int KS, int RG, bool XK, bool DENSE, bool MLP = false>
-__global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((DENSE || MLP) && XK ? 1 : 3, (DENSE || MLP) && XK ? 8 : 3))) void gemm_decode_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3, 3))) void gemm_decode_kernel(GemmArgs a) {
+  // the f16-operand forms of the dense control and of the MLP epilogue hold one activation stage
+  constexpr bool kOneX = (DENSE || MLP) && XK;
   static_assert(!MLP || (MF == 4 && RG == 1 && KS > 1 && !DENSE), "MLP epilogue: 32 gate + 32 up rows per workgroup");
   __shared__ f32x4 red[KS > 1 ? KS * RG : 1][MF][64];
   const int e = blockIdx.y;
@@ -536,19 +539,33 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu((D
       w0.load(rw, src, lane, ss);
       x0.load(rq, rs, voq, vos, vox, ss);
     }
-    while (ss < nss) {
-      const int s1 = ss + KS, s2 = ss + 2 * KS;
-      if (s1 < nss) {
-        w1.load(rw, src, lane, s1);
-        x1.load(rq, rs, voq, vos, vox, s1);
+    if constexpr (kOneX) {
+      // one activation stage, reloaded as soon as a step has used it; the weights stay double-buffered
+      while (ss < nss) {
+        const int s1 = ss + KS, s2 = ss + 2 * KS;
+        if (s1 < nss) w1.load(rw, src, lane, s1);
+        stage_mma(acc, w0, x0);
+        if (s1 < nss) x0.load(rq, rs, voq, vos, vox, s1);
+        if (s2 < nss) w0.load(rw, src, lane, s2);
+        if (s1 < nss) stage_mma(acc, w1, x0);
+        if (s2 < nss) x0.load(rq, rs, voq, vos, vox, s2);
+        ss = s2;
       }
-      stage_mma(acc, w0, x0);
-      if (s2 < nss) {
-        w0.load(rw, src, lane, s2);
-        x0.load(rq, rs, voq, vos, vox, s2);
+    } else {
+      while (ss < nss) {
+        const int s1 = ss + KS, s2 = ss + 2 * KS;
+        if (s1 < nss) {
+          w1.load(rw, src, lane, s1);
+          x1.load(rq, rs, voq, vos, vox, s1);
+        }
+        stage_mma(acc, w0, x0);
+        if (s2 < nss) {
+          w0.load(rw, src, lane, s2);
+          x0.load(rq, rs, voq, vos, vox, s2);
+        }
+        if (s1 < nss) stage_mma(acc, w1, x1);
+        ss = s2;
       }
-      if (s1 < nss) stage_mma(acc, w1, x1);
-      ss = s2;
     }
     if (KS == 1) {
       if (tv) {

@@ -715,7 +715,8 @@ def test_mlp_parity_tiny(kernel):
 def test_mlp_streaming_block_renumbering(I):
     """The weight-streaming MLP gate_up renumbers its workgroups (pairs sharing a unit's mask and scale
     lines on one XCD) when I/32 is a multiple of 16: its smallest cases (16 and 32 column blocks)
-    against the oracle, gate_up outputs and the requantized h."""
+    against the oracle, gate_up outputs and the requantized h, with the NVFP4 codes and the f16
+    operand copy."""
     E, H, T, k = 4, 256, 32, 2
     say("mlp streaming renumbering I", I)
     rng = np.random.default_rng(I)
@@ -740,6 +741,10 @@ def test_mlp_streaming_block_renumbering(I):
     assert np.mean(host(hs) != M["hs"]) <= 1e-3
     assert np.mean(orc.dequant(host(hq), host(hs)) != orc.dequant(M["hq"], M["hs"])) <= 2e-3
     assert orc.rel_frobenius(host(y), M["y2"]) <= 1e-2
+    # the f16-operand form (one activation stage in registers): the same operands, the same result bits
+    y_xk, _ = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]),
+                                  y_dtype=torch.float32, xk=dev(_xk_reference(qo, so)), flags=mq.F_FORCE_DECODE)
+    assert np.array_equal(host(y_xk), host(y))
 
 
 @pytest.mark.parametrize("kernel", ["streaming", "tiled"])
