@@ -1035,7 +1035,7 @@ MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* 
 template <int MF>
 struct TileCtx {
   int e, off, ne, tb, rb, nv;
-  float alpha, alpha_u, gh;
+  float alpha;
   rsrc_t rw;          // expert's weights (kernel layout)
   WSrc src;           // the wave's m-fragments in the kernel layout
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
@@ -1080,8 +1080,6 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   // alpha_e: the MLP tile's gate and up rows take the two tensor scales, a plain wave its row half's
   const int half = MLP ? 0 : (min(c.rb * 512 + 64 * w, N - 64) >= N / 2);
   c.alpha = 1.0f / (wscale(a, c.e, half) * a.gamma_a[c.e]);
-  c.alpha_u = MLP ? 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]) : c.alpha;
-  c.gh = MLP ? a.gamma_h[c.e] : 0.0f;
   if (XK) {
     c.rq = make_rsrc((const uint8_t*)a.xk + (size_t)c.off * K * 2, (uint32_t)c.ne * K * 2);
     c.rs = c.rq;
@@ -1183,11 +1181,13 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
     return;
   }
   const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
+  const float alpha_u = 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]);  // the up rows' alpha_e
+  const float gh = a.gamma_h[c.e];
 #pragma unroll
   for (int n = 0; n < NF; n++) {
     if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
-    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, c.alpha_u, c.gh, acc[0][n], acc[1][n], acc[2][n],
+    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, alpha_u, gh, acc[0][n], acc[1][n], acc[2][n],
                        acc[3][n]);
   }
 }
