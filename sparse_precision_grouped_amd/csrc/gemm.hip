@@ -1201,6 +1201,7 @@ template <bool MLP, bool XK, bool DENSE = false>
 __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = kTileNF;
   constexpr int BBYTES = kBTileBytes;
+  constexpr bool kOneW = DENSE;  // the dense control's larger weight stage is held once
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int32_t part[kTileThreads];
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, cc = lane >> 4;
@@ -1250,10 +1251,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     if (has_n) {
-      wn.load(nxt.rw, nxt.src, lane, ss_n);
+      if (!kOneW) wn.load(nxt.rw, nxt.src, lane, ss_n);
       issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
     }
     wc.template mma<NF, XK>(acc, Bc, r16, cc, cur.nv);
+    if (kOneW && has_n) wc.load(nxt.rw, nxt.src, lane, ss_n);  // the one weight stage, reloaded after use
     if (ss == nss - 1) {
       tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
 #pragma unroll
@@ -1269,7 +1271,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
       lds_barrier();  // epilogue stores may still be in flight
     }
     if (!has_n) break;
-    wc = wn;
+    if (!kOneW) wc = wn;
     cur = nxt;
     t = t_n;
     ss = ss_n;
