@@ -897,10 +897,15 @@ MOESQ_DEV void lds_step(f32x4 (&acc)[MF][NF], const WStage<MF>& w, const WMeta (
 #pragma unroll
   for (int n0 = 0; n0 < NF; n0 += G) {
     if (G == NF || n0 < nv) {
+      // the next n-fragment's B is read from LDS while this one's MFMAs issue
+      f16x16 Bn = concat_x(*(const u32x4*)b_chunk(Bs, n0 * 16 + r16, g1), *(const u32x4*)b_chunk(Bs, n0 * 16 + r16, g1 + 16));
 #pragma unroll
       for (int n = n0; n < n0 + G; n++) {
-        const int r = n * 16 + r16;
-        const f16x16 B = concat_x(*(const u32x4*)b_chunk(Bs, r, g1), *(const u32x4*)b_chunk(Bs, r, g1 + 16));
+        const f16x16 B = Bn;
+        if (n + 1 < n0 + G) {
+          const int r = (n + 1) * 16 + r16;
+          Bn = concat_x(*(const u32x4*)b_chunk(Bs, r, g1), *(const u32x4*)b_chunk(Bs, r, g1 + 16));
+        }
 #pragma unroll
         for (int f = 0; f < MF; f++) acc[f][n] = smfmac_step<S>(A[f], B, acc[f][n], m[f]);
       }
@@ -1195,13 +1200,14 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
 // Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the
 // workgroups of XCD x (blockIdx % 8 == x) take the x-th contiguous eighth of the tile list, slot j
 // handling tiles start + j, + J, ... The super-steps of all the workgroup's tiles form one
-// pipeline: while step i computes, the weights (registers) and activations (LDS) of step i+1 --
-// possibly the first step of the next tile -- are in flight; one barrier per step.
+// pipeline: while step i computes, the activations (LDS) of step i+1 -- possibly the first step of
+// the next tile -- are in flight, and its weights are loaded into the one register stage as soon as
+// step i's MFMAs have read it; one barrier per step. (One weight stage measured as fast as two; the
+// registers it frees hold the B read-ahead of the sparse kernels and the dense control's larger stage.)
 template <bool MLP, bool XK, bool DENSE = false>
 __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = kTileNF;
   constexpr int BBYTES = kBTileBytes;
-  constexpr bool kOneW = DENSE;  // the dense control's larger weight stage is held once
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int32_t part[kTileThreads];
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, cc = lane >> 4;
@@ -1229,7 +1235,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   TileCtx<MF> cur = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t, w);
-  TWS<MF, MLP, DENSE> wc, wn;
+  TWS<MF, MLP, DENSE> wc;
   PStage p;
   wc.load(cur.rw, cur.src, lane, 0);
   issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
@@ -1250,12 +1256,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
-    if (has_n) {
-      if (!kOneW) wn.load(nxt.rw, nxt.src, lane, ss_n);
-      issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
-    }
+    if (has_n) issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
     wc.template mma<NF, XK>(acc, Bc, r16, cc, cur.nv);
-    if (kOneW && has_n) wc.load(nxt.rw, nxt.src, lane, ss_n);  // the one weight stage, reloaded after use
+    if (has_n) wc.load(nxt.rw, nxt.src, lane, ss_n);  // the weight stage, reloaded once read
     if (ss == nss - 1) {
       tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
 #pragma unroll
@@ -1271,7 +1274,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
       lds_barrier();  // epilogue stores may still be in flight
     }
     if (!has_n) break;
-    if (!kOneW) wc = wn;
     cur = nxt;
     t = t_n;
     ss = ss_n;
