@@ -495,6 +495,39 @@ def test_grouped_gemm_edge_cases():
     assert np.all(host(y) == 0)
 
 
+@pytest.mark.parametrize("flags", ["decode", "decode_xk", "prefill", "prefill_xk"])
+def test_grouped_gemm_token_count_boundaries(flags):
+    """Experts whose token counts sit on and around every block boundary of both kernels (16-token
+    fragments, the 64-token skip groups and 128-token tiles of the tiled kernel, its B read-ahead
+    within a group) and an empty expert, with N = 640 (a partial 512-row block) and K = 512: each
+    configuration against the oracle."""
+    counts = np.array([0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257], np.int64)
+    E, K, N = counts.size, 512, 640
+    say("gemm token-count boundaries", flags)
+    rng = np.random.default_rng(77)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    Wo, Wd = orc.compress(w), mq.moesq_compress_weights(dev(w))
+    rows = int(counts.sum())
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)
+    R = orc.route(ids, E)
+    x = gen.student_t(71, gen.act_stream(3), rows * K).reshape(rows, K)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], 1, R["offsets"], ga)
+    fl = mq.F_FORCE_DECODE if flags.startswith("decode") else mq.F_FORCE_PREFILL
+    xk = dev(_xk_reference(qo, so)) if flags.endswith("_xk") else None
+    y = mq.moesq_grouped_gemm(Wd, dev(qo), dev(so), dev(ga), dev(R["offsets"]), y_dtype=torch.float32, flags=fl,
+                              xk=xk)
+    ref = orc.grouped_gemm(Wo, qo, so, ga, R["offsets"])
+    err = orc.rel_frobenius(host(y), ref)
+    say("rel-Frobenius", err)
+    assert err <= GEMM_TOL
+    # every expert on its own (a small expert's error is not hidden by the large ones)
+    off = R["offsets"]
+    for e in range(E):
+        if counts[e]:
+            assert orc.rel_frobenius(host(y)[off[e]:off[e + 1]], ref[off[e]:off[e + 1]]) <= GEMM_TOL, e
+
+
 # ------------------------------------------------- dispatch + GEMM in one call --------------
 def _rqg_check(ids, x, E, ga, Wd, Wo=None, bf16=False, y_dtype=torch.float32, oracle_rows=None):
     """moesq_route_quantize_gemm byte for byte against moesq_route_quantize + moesq_grouped_gemm (the
