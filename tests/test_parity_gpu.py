@@ -781,6 +781,41 @@ def test_mlp_streaming_block_renumbering(I):
 
 
 @pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_mlp_token_count_boundaries(kernel):
+    """The routed-expert MLP with expert token counts on and around the kernels' block boundaries
+    (16, 64, 128 tokens) and an empty expert: gate_up outputs, requantized h and the chain against
+    the oracle, with the NVFP4 codes and the f16 operand copy (bit-identical to each other)."""
+    counts = np.array([0, 1, 16, 17, 63, 64, 65, 127, 128, 129, 200], np.int64)
+    E, H, I = counts.size, 256, 512
+    say("mlp token-count boundaries", kernel)
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    rng = np.random.default_rng(78)
+    w13 = (rng.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    W13o, W2o = orc.compress(w13), orc.compress(w2)
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    rows = int(counts.sum())
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)
+    R = orc.route(ids, E)
+    x = gen.student_t(72, gen.act_stream(5), rows * H).reshape(rows, H)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], 1, R["offsets"], ga)
+    h = orc.swiglu(orc.grouped_gemm(W13o, qo, so, ga, R["offsets"]))
+    gh = np.full(E, orc.global_scale(float(np.abs(h).max())), np.float32)
+    M = orc.expert_mlp(W13o, W2o, qo, so, ga, gh, R["offsets"])
+    y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]), y_dtype=torch.float32,
+                                flags=mq.F_DUMP_GATEUP | kf)
+    hq, hs, dump = mq.mlp_workspace_views(ws, rows, I, dump=True)
+    assert orc.rel_frobenius(host(dump), M["y13"]) <= GEMM_TOL
+    assert np.mean(host(hs) != M["hs"]) <= 1e-3
+    assert np.mean(orc.dequant(host(hq), host(hs)) != orc.dequant(M["hq"], M["hs"])) <= 2e-3
+    assert orc.rel_frobenius(host(y), M["y2"]) <= 1e-2
+    y_xk, _ = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(R["offsets"]),
+                                  y_dtype=torch.float32, xk=dev(_xk_reference(qo, so)), flags=kf)
+    assert np.array_equal(host(y_xk), host(y))
+
+
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
 def test_split_tensor_scales(kernel):
     """Gate and up kept as separate linears, each with its own Eq. 5 tensor scale (the model card's
     checkpoint): device compression of the [2E, N/2, K] view against the oracle's compress_split
