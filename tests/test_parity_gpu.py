@@ -1114,14 +1114,15 @@ def test_dense_kernel_on_unpacked_sparse_weights_matches_sparse_kernel():
 
 
 # ---------------------------------------------------------------- graph replay -----------------
-@pytest.mark.parametrize("fused", [False, True])
-def test_graph_replays_match_eager_step(fused):
+@pytest.mark.parametrize("fused,streaming_xk", [(False, False), (True, False), (True, True)])
+def test_graph_replays_match_eager_step(fused, streaming_xk):
     """The benchmark times HIP-graph replays of a whole step. Capture the t_mlp chain (route ->
-    scatter-quantize -> MLP -> combine; routing and quantization as two calls or as one) once,
-    replay it several times with eager work and synchronization in between, and compare every
-    replay with the eager result, bit for bit."""
+    scatter-quantize -> MLP -> combine; routing and quantization as two calls or as one; the tiled
+    MLP on the NVFP4 codes, or the weight-streaming MLP on the quantizer's f16 copy as the decode
+    layer runs it) once, replay it several times with eager work and synchronization in between, and
+    compare every replay with the eager result, bit for bit."""
     cfg = gen.CONFIGS["t_mlp"]
-    say("graph replay t_mlp fused", fused)
+    say("graph replay t_mlp fused", fused, "streaming_xk", streaming_xk)
     E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
     w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
     w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
@@ -1138,14 +1139,16 @@ def test_graph_replays_match_eager_step(fused):
     ws = mq.mlp_workspace(rows, I, False, DEV)
     y2 = torch.empty((rows, H), dtype=torch.bfloat16, device=DEV)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    xk = torch.empty((rows, H), dtype=torch.float16, device=DEV) if streaming_xk else None
+    kf = mq.F_FORCE_DECODE if streaming_xk else 0
 
     def step():
         if fused:
-            mq.moesq_route_quantize(ids_d, E, x, ga, rt=rt, q=q, s=s)
+            mq.moesq_route_quantize(ids_d, E, x, ga, rt=rt, q=q, s=s, xk=xk)
         else:
             mq.moesq_route_permute(ids_d, E, rt["counts"], rt["offsets"], rt["sorted_slot"], rt["slot_pos"])
             mq.moesq_quantize_act(x, ga, slot_pos=rt["slot_pos"], k=k, offsets=rt["offsets"], q=q, s=s)
-        mq.moesq_expert_mlp(W13, W2, q, s, ga, gh, rt["offsets"], y=y2, workspace=ws)
+        mq.moesq_expert_mlp(W13, W2, q, s, ga, gh, rt["offsets"], y=y2, workspace=ws, xk=xk, flags=kf)
         mq.moesq_unpermute_combine(y2, rt["slot_pos"], wts_d, out=out)
 
     step()
