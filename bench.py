@@ -69,6 +69,7 @@ def fused_step_bytes(n_active, N, K, T, k, E, x_bytes=4):
 
 FUSED_KERNEL = "dispatch_gemm_kernel"
 MLP_KEY = "moesq_expert_mlp (gate_up+SwiGLU+requant, down)"
+GATEUP_KERNEL = "gemm_tile_kernel<MLP> (gate_up + SwiGLU + requant)"
 
 
 def fused_eligible(cfg):
@@ -239,8 +240,24 @@ class Workload:
                 sl["y2"] = torch.empty((self.rows, cfg.N2), dtype=torch.bfloat16, device=dev)
                 sl["out"] = torch.empty((T, cfg.N2), dtype=torch.bfloat16, device=dev)
             self.slots.append(sl)
+        if self.kind == "mlp":
+            self._calibrate()
         torch.cuda.synchronize()
         self.graphs = []
+
+    def _calibrate(self):
+        """Per-expert tensor scales of the intermediate h (the model card's stored per-expert input scale,
+        Eq. 5 over the expert's amax of h), calibrated on the device on the first batch before anything
+        is timed, then kept for every batch: moesq_expert_mlp with MOESQ_F_CALIBRATE."""
+        mq, cfg, sl = self.mq, self.cfg, self.slots[0]
+        mq.moesq_route_quantize(sl["ids"], cfg.E, sl["x"], sl["ga"], rt=sl["rt"], q=sl["q"], s=sl["s"], xk=sl["xk"],
+                                workspace=sl["ws_route"])
+        gam, amax = mq.moesq_calibrate_gamma_h(self.W, self.W2, sl["q"], sl["s"], sl["ga"], sl["rt"]["offsets"],
+                                               xk=sl["xk"])
+        for slr in self.slots:
+            slr["gh"].copy_(gam)
+        g = gam.cpu().numpy()
+        self.gamma_h_range = (float(g.min()), float(g.max()))
 
     def _weights(self, proj, N, K):
         torch, gen, mq, cfg = self.torch, self.gen, self.mq, self.cfg
@@ -300,6 +317,15 @@ class Workload:
                                 y=sl["y2"], workspace=sl["ws_mlp"], xk=sl["xk"])
         else:
             mq.moesq_grouped_gemm(self.Wc[r], sl["q"], sl["s"], sl["ga"], rt["offsets"], y=sl["y"], xk=sl["xk"])
+
+    def down_only(self, r):
+        """The MLP's down GEMM alone (the same kernel and operands as the second launch of
+        moesq_expert_mlp: the requantized h codes and their f16 copy from the workspace)."""
+        mq, cfg, sl = self.mq, self.cfg, self.slots[r]
+        I = cfg.N // 2
+        hq, hs, _ = mq.mlp_workspace_views(sl["ws_mlp"], self.rows, I)
+        hk = mq.mlp_hk_view(sl["ws_mlp"], self.rows, I)
+        mq.moesq_grouped_gemm(self.W2c[r], hq, hs, sl["gh"], sl["rt"]["offsets"], y=sl["y2"], xk=hk)
 
     def capture(self):
         torch = self.torch
@@ -366,19 +392,17 @@ class Workload:
 def cpu_baseline(wl, orc, gen, max_reps=3):
     """The oracle's step on the host cores, on a bounded sample of the same workload."""
     cfg = wl.cfg
+    if wl.kind != "single" or cfg.E * cfg.N * cfg.K > 512 * 1024 * 1024:
+        return cpu_baseline_sampled(wl, orc, gen, max_reps)
     E, T, k, N, K = cfg.E, cfg.T, cfg.k, cfg.N, cfg.K
     ids, wts = gen.routing(cfg)
     x = gen.activations(cfg, 0, T, K)
     rows = T * k
-    R = orc.route(ids, E)
-    if wl.kind == "single" and cfg.E * cfg.N * cfg.K <= 512 * 1024 * 1024:
-        w = np.stack([gen.weights_expert(cfg, 0, e, N, K) for e in range(E)])
-        Wo = orc.compress(w)
-        row_list = None if rows <= 4096 else np.linspace(0, rows - 1, 512).astype(np.int64)
-        sample = "full step (route, dispatch-quantize, GEMM) on %s" % (
-            "all %d rows" % rows if row_list is None else "512 of %d rows (GEMM), all rows (route, quantize)" % rows)
-    else:
-        return None
+    w = np.stack([gen.weights_expert(cfg, 0, e, N, K) for e in range(E)])
+    Wo = orc.compress(w)
+    row_list = None if rows <= 4096 else np.linspace(0, rows - 1, 512).astype(np.int64)
+    sample = "full step (route, dispatch-quantize, GEMM) on %s" % (
+        "all %d rows" % rows if row_list is None else "512 of %d rows (GEMM), all rows (route, quantize)" % rows)
     ga = np.full(E, orc.global_scale_of(x), np.float32)
     times = []
     n_rows = rows if row_list is None else row_list.size
@@ -394,6 +418,106 @@ def cpu_baseline(wl, orc, gen, max_reps=3):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": tflops_eff(N, K, n_rows, t), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": sample + ", median of %d run(s), %.3f s each" % (len(times), t), "cpu_model": _cpu_model()}
+
+
+# rows of the expert sample per workload kind: the Kimi decode workloads route 1-2 rows to an expert,
+# the prefill MLP a few hundred
+CPU_SAMPLE = {"pair": (16, 64), "mlp_decode": (16, 64), "mlp": (8, 512)}   # (max experts, max rows)
+
+
+def _sub_weights(gen, orc, cfg, proj, N, K, experts):
+    """The oracle's compression of the sampled experts' weights (host draw), as a grouped problem of
+    its own (expert i of the sample = experts[i])."""
+    return orc.compress(np.stack([gen.weights_expert(cfg, proj, int(e), N, K) for e in experts]))
+
+
+def cpu_baseline_sampled(wl, orc, gen, max_reps=3):
+    """Workloads too large for the oracle in seconds (the Kimi shapes: 10-15 MB of weights per expert,
+    29.4 M multiply-adds per routed row of the gate_up): the oracle runs the whole step's per-token parts
+    (routing, dispatch quantization, for the MLP the combine) on the full batch, and the per-row GEMM
+    chain (gate_up, SwiGLU, requantization, down) on the routed rows of a seeded sample of experts,
+    which it computes as a grouped problem of its own. The full step's time is extrapolated linearly
+    in the rows (the GEMM chain costs the same per row): t = t_per_token_parts + t_sample * rows /
+    sample_rows, and value = TFLOP/s_eff of the full step over that time. Weight compression is setup
+    (untimed), as in the GPU measurement."""
+    cfg = wl.cfg
+    E, T, k = cfg.E, cfg.T, cfg.k
+    rows = T * k
+    decode = rows <= 16 * E
+    kind = "mlp_decode" if (wl.kind == "mlp" and decode) else wl.kind
+    max_e, max_rows = CPU_SAMPLE[kind]
+    ids, wts = gen.routing(cfg)
+    x = gen.activations(cfg, 0, T, cfg.K)
+    if cfg.x_bf16:
+        import torch  # the bf16 hand-over of the tokens, as on the device
+        x = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    R = orc.route(ids, E)
+    off = np.asarray(R["offsets"])
+    counts = np.diff(off)
+    rng = np.random.default_rng(cfg.seed)
+    experts, n = [], 0
+    for e in rng.permutation(np.flatnonzero(counts > 0)):
+        if len(experts) == max_e or n >= max_rows:
+            break
+        experts.append(int(e))
+        n += int(min(counts[e], max_rows - n))
+    experts = np.array(experts)
+    take = [np.arange(off[e], off[e] + min(counts[e], max_rows)) for e in experts]
+    per = np.array([t.size for t in take])
+    total = int(per.sum())
+    while total > max_rows:             # trim the last expert to the row budget
+        per[-1] -= total - max_rows
+        take[-1] = take[-1][:per[-1]]
+        total = int(per.sum())
+    sel = np.concatenate(take)
+    sub_off = np.concatenate([[0], np.cumsum(per)]).astype(np.int32)
+    N, K = cfg.N, cfg.K
+    W1 = _sub_weights(gen, orc, cfg, 0, N, K, experts)
+    W2 = _sub_weights(gen, orc, cfg, 1, cfg.N2, cfg.K2, experts) if cfg.N2 else None
+    x2 = gen.activations(cfg, 1, T, cfg.K2) if wl.kind == "pair" else None
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    ga2 = np.full(E, orc.global_scale_of(x2), np.float32) if x2 is not None else None
+    t_tok, t_rows = [], []
+    for _ in range(max_reps):
+        t0 = time.perf_counter()
+        Rr = orc.route(ids, E)
+        q, s = orc.dispatch_quantize(x, Rr["sorted_slot"], k, Rr["offsets"], ga)
+        if x2 is not None:
+            q2, s2 = orc.dispatch_quantize(x2, Rr["sorted_slot"], k, Rr["offsets"], ga2)
+        t1 = time.perf_counter()
+        y1 = orc.grouped_gemm(W1, q[sel], s[sel], ga[experts], sub_off)
+        if wl.kind == "pair":
+            y2 = orc.grouped_gemm(W2, q2[sel], s2[sel], ga2[experts], sub_off)
+        elif wl.kind == "mlp":
+            h = orc.swiglu(y1).astype(np.float32)
+            ex = orc.expert_of_rows(sub_off, np.arange(total))
+            amax = np.zeros(len(experts), np.float32)
+            np.maximum.at(amax, ex, np.abs(h).max(axis=1))
+            gh = np.array([orc.global_scale(float(v)) for v in amax], np.float32)
+            hq, hs = orc.quantize_rows(h, gh, ex)
+            y2 = orc.grouped_gemm(W2, hq, hs, gh, sub_off)
+        t2 = time.perf_counter()
+        if wl.kind == "mlp":
+            yfull = np.zeros((rows, cfg.N2), np.float64)
+            yfull[sel] = y2
+            orc.combine(yfull, Rr["slot_pos"], wts)
+        t3 = time.perf_counter()
+        t_tok.append((t1 - t0) + (t3 - t2))
+        t_rows.append(t2 - t1)
+        if sum(t_tok) + sum(t_rows) > 25:
+            break
+    tt, tr = float(np.median(t_tok)), float(np.median(t_rows))
+    t_full = tt + tr * rows / total
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    flops = wl.eff_flops_per_step()
+    parts = {"pair": "routing, dispatch quantization of both projections' inputs",
+             "mlp": "routing, dispatch quantization, combine"}[wl.kind]
+    chain = {"pair": "gate_up GEMM, down GEMM", "mlp": "gate_up GEMM, SwiGLU, requantization, down GEMM"}[wl.kind]
+    sample = ("%s on the full batch (%.3f s); %s on the %d routed rows of %d seeded-random experts (%.3f s), "
+              "extrapolated x%.1f to all %d rows: %.2f s per step; median of %d run(s)" % (
+                  parts, tt, chain, total, len(experts), tr, rows / total, rows, t_full, len(t_rows)))
+    return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "extrapolated": True, "cpu_model": _cpu_model()}
 
 
 def _cpu_model():
@@ -542,7 +666,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4", "c3_mlp"])
+    ap.add_argument("--workload", default="c4", choices=["c0", "c1", "c2", "c3", "c4", "c3_mlp"])
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -623,22 +747,41 @@ def main(argv=None):
 
     # dominant kernel: one pair of HIP events on the launch stream around kernel_iters back-to-back
     # launches (rotating weight copies), the mean per launch; the median of 3 such blocks
-    blocks = []
-    for _ in range(3):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(st)
-        for i in range(args.kernel_iters):
-            wl.dominant(i % wl.R)
-        b.record(st)
-        torch.cuda.synchronize()
-        blocks.append(a.elapsed_time(b) / args.kernel_iters)
-    kms = float(np.median(blocks))
+    def block_ms(fn, iters):
+        out = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for i in range(iters):
+                fn(i % wl.R)
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / iters)
+        return float(np.median(out))
+
+    kms = block_ms(wl.dominant, args.kernel_iters)
     bound, units, unit, peak, kname = wl.roofline_units()
+    mlp_split = None
+    if wl.kind == "mlp" and bound == "mfma":
+        # the prefill MLP is two launches (gate_up + SwiGLU + requant, then down): the dominant one is the
+        # gate_up; its time is the MLP call's minus the down GEMM's, timed alone on the same operands
+        cfg = wl.cfg
+        down_ms = block_ms(wl.down_only, args.kernel_iters)
+        kept_gu, kept_dn = cfg.N * cfg.K * wl.rows / 1e12, cfg.N2 * cfg.K2 * wl.rows / 1e12
+        mlp_split = {"kernel": MLP_KEY, "kernel_ms": round(kms, 5), "achieved": round((kept_gu + kept_dn) / (kms * 1e-3), 2),
+                     "frac": round((kept_gu + kept_dn) / (kms * 1e-3) / peak, 4),
+                     "down_kernel_ms": round(down_ms, 5),
+                     "down_frac": round(kept_dn / (down_ms * 1e-3) / peak, 4),
+                     "traffic": _traffic("%s:%s" % (args.workload, MLP_KEY))}
+        kms = kms - down_ms
+        units, kname = kept_gu, GATEUP_KERNEL
     achieved = units / (kms * 1e-3)
     traffic = _traffic("%s:%s" % (args.workload, kname))
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
                 "kernel_ms": round(kms, 5)}
+    if mlp_split:
+        roofline["mlp_two_gemms"] = mlp_split
     if bound == "mfma":
         # the same launch against the chip's dense FP8 and FP4 peaks, on dense-equivalent flops
         # (2 x the kept flops)
@@ -663,6 +806,11 @@ def main(argv=None):
     elif wl.kind == "pair":
         step_gbps = round((gemm_bytes(n_act, cfg.N, cfg.K, wl.rows, cfg.E) +
                            gemm_bytes(n_act, cfg.N2, cfg.K2, wl.rows, cfg.E)) / t / 1e9, 1)
+    if wl.kind == "mlp":
+        cfgd_extra = {"gamma_h": "per expert, calibrated on the device (Eq. 5 over each expert's amax of h), "
+                                 "range %.4g..%.4g" % wl.gamma_h_range}
+    else:
+        cfgd_extra = {}
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak",
@@ -676,7 +824,7 @@ def main(argv=None):
             "dispatch": "one launch (route+quantize+GEMM)" if wl.fused else "separate launches",
             "activation_scale": ("dynamic: Eq. 5 over the step's tokens, on the device" if wl.dyn_scale else
                                  "static per-expert constant"),
-            "step_gbps_algorithmic": step_gbps, "step_us_p10_p50_p90": pcts},
+            "step_gbps_algorithmic": step_gbps, "step_us_p10_p50_p90": pcts, **cfgd_extra},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -54,6 +54,11 @@ extern "C" {
 #define MOESQ_F_FORCE_DECODE 2u  /* moesq_grouped_gemm: use the weight-streaming (decode) kernel */
 #define MOESQ_F_FORCE_PREFILL 4u /* moesq_grouped_gemm: use the tiled (prefill) kernel; without either
                                     flag the kernel is chosen from rows / E (<= 16: decode) */
+#define MOESQ_F_DUMP_H 16u       /* moesq_expert_mlp: also write the fp32 h = SiLU(g) * u that the gate_up
+                                    epilogue requantizes, to the workspace region described at
+                                    moesq_expert_mlp (for checking the requantization on identical inputs) */
+#define MOESQ_F_CALIBRATE 32u    /* moesq_expert_mlp: calibrate the intermediate tensor scales instead of
+                                    running the MLP (see moesq_expert_mlp) */
 #define MOESQ_F_CAPACITY 8u      /* moesq_grouped_gemm, moesq_expert_mlp, moesq_dense_grouped_gemm: the
                                     activations and outputs are in the fixed-capacity layout of paper
                                     Appendix D.1 (expert e owns rows [e*C, (e+1)*C), C = rows / E, rows
@@ -68,6 +73,7 @@ extern "C" {
 #define MOESQ_WS_MLP_DUMP 3
 #define MOESQ_WS_COMPRESS 4
 #define MOESQ_WS_ROUTE_CAPACITY 5
+#define MOESQ_WS_MLP_CALIBRATE 6
 
 /*
  * Compressed weights of one projection for E experts, pair-bitmask v1 layout (model card, "Sparse
@@ -245,8 +251,19 @@ int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, c
  * xk is the optional f16 copy of (q, s) from moesq_quantize_act.
  * Workspace: moesq_workspace_bytes(MOESQ_WS_MLP, ..., rows, k=0, E, K=H, N=0, I) bytes; it holds, each
  *   region starting on a 256-byte boundary, h_q [rows][I/2], h_s [rows][I/32] and h_k [rows][I] (the
- *   f16 copy of the requantized h read by the down GEMM). With MOESQ_F_DUMP_GATEUP the size is
- *   moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and the fp32 gate_up outputs [rows][2I] follow.
+ *   f16 copy of the requantized h read by the down GEMM). With MOESQ_F_DUMP_GATEUP and/or
+ *   MOESQ_F_DUMP_H the size is moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and two more regions
+ *   follow: the fp32 gate_up outputs [rows][2I] (written with MOESQ_F_DUMP_GATEUP), then the fp32 h
+ *   [rows][I] the requantization read (written with MOESQ_F_DUMP_H). Rows no expert owns are not
+ *   written.
+ * Calibration (MOESQ_F_CALIBRATE; model card: the input scale is stored per expert linear, Eq. 5 over
+ *   the tensor's amax): only the gate_up GEMM and SwiGLU run; the call writes, at the start of the
+ *   workspace, amax_h [E] (fp32, the largest |h| over each expert's rows, 0 for an expert without
+ *   rows) and, at the next 256-byte boundary, gamma_h [E] = Eq. 5 of amax_h (1 where amax_h is 0).
+ *   Workspace: moesq_workspace_bytes(MOESQ_WS_MLP_CALIBRATE, ..., E, ...) bytes. gamma_h is not read
+ *   (may be NULL) and y is not written; the dump flags are invalid with it. The amax is a max, so the
+ *   result does not depend on the kernel's order of work; it depends on the kernel family only
+ *   through the fp32 accumulation order of h.
  * Kernels: with rows <= 16 E both GEMMs stream the weights (the gate_up epilogue computes SwiGLU and
  * the requantization per 32 intermediate columns), otherwise both are tiled; MOESQ_F_FORCE_DECODE /
  * MOESQ_F_FORCE_PREFILL pick one. Both produce the same results up to fp32 accumulation order.
@@ -337,7 +354,7 @@ int moesq_unpack_weights(void *stream, const moesq_weights *W, uint8_t *dense_nv
 
 /*
  * Workspace size in bytes for a call kind (MOESQ_WS_*). Arguments not used by a kind are ignored:
- *   ROUTE: T, k, E.   MLP / MLP_DUMP: T = rows, E, K = H, I.   COMPRESS: E.
+ *   ROUTE: T, k, E.   MLP / MLP_DUMP: T = rows, E, K = H, I.   MLP_CALIBRATE: E.   COMPRESS: E.
  */
 size_t moesq_workspace_bytes(int32_t kind, int64_t T, int32_t k, int32_t E, int32_t K, int32_t N, int32_t I);
 

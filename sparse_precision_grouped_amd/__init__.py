@@ -18,8 +18,9 @@ __all__ = [
     "moesq_expert_mlp", "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights",
     "moesq_workspace_bytes", "moesq_status_str", "moesq_version", "moesq_global_scale",
     "moesq_prepack_weights", "moesq_kernel_layout_bytes",
-    "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL", "F_CAPACITY",
-    "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS", "WS_ROUTE_CAPACITY", "moesq_route_capacity",
+    "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL", "F_CAPACITY", "F_DUMP_H", "F_CALIBRATE",
+    "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS", "WS_ROUTE_CAPACITY", "WS_MLP_CALIBRATE",
+    "moesq_route_capacity", "moesq_calibrate_gamma_h",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,8 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libmoesq.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_PATTERN, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL, F_CAPACITY = 1, 2, 4, 8
-WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS, WS_ROUTE_CAPACITY = 1, 2, 3, 4, 5
+F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL, F_CAPACITY, F_DUMP_H, F_CALIBRATE = 1, 2, 4, 8, 16, 32
+WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS, WS_ROUTE_CAPACITY, WS_MLP_CALIBRATE = 1, 2, 3, 4, 5, 6
 
 
 class MoesqError(RuntimeError):
@@ -128,6 +129,49 @@ def _dev(t):
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
     return t
+
+
+def _need(t, name, shape, dtype, device=None):
+    """A caller-supplied tensor must be a contiguous tensor of the given shape and dtype (the C ABI takes
+    bare pointers and cannot check sizes: an undersized buffer would be written out of bounds). Where it
+    lives is checked separately (_on_device), after every tensor of a call has passed this check."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+
+
+def _need_bytes(t, name, nbytes):
+    """A byte buffer (workspace) of at least nbytes, contiguous."""
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s: %d bytes, need %d" % (name, t.numel() * t.element_size(), nbytes))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+
+
+def _on_device(**tensors):
+    """Every given tensor is a device tensor, all on one device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s: expected a device tensor" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s: on %s, expected %s" % (name, t.device, dev))
+
+
+def _check_codes(q, s, rows, K, xk=None):
+    """Expert-sorted activation codes q [rows, K/2] u8, scales s [rows, K/32] u8, optional f16 copy [rows, K]."""
+    _need(q, "q", (rows, K // 2), torch.uint8)
+    _need(s, "s", (rows, K // 32), torch.uint8)
+    _need(xk, "xk", (rows, K), torch.float16)
 
 
 class Weights:
@@ -342,8 +386,19 @@ def moesq_route_quantize_gemm(topk_ids, x, gamma_a, W, rt=None, q=None, s=None, 
     return (rt, q, s, xk, y) if want_xk else (rt, q, s, y)
 
 
-def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):
+def _check_gemm_io(W, q, s, gamma_a, offsets, xk, flags, y=None, N=None):
     rows = q.shape[0]
+    _check_codes(q, s, rows, W.K, xk)
+    _need(gamma_a, "gamma_a", (W.E,), torch.float32)
+    _need(offsets, "offsets", (W.E,) if flags & F_CAPACITY else (W.E + 1,), torch.int32)
+    if y is not None:
+        _need(y, "y", (rows, W.N if N is None else N), y.dtype)
+    _on_device(q=q, s=s, xk=xk, gamma_a=gamma_a, offsets=offsets, y=y)
+    return rows
+
+
+def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):
+    rows = _check_gemm_io(W, q, s, gamma_a, offsets, xk, flags, y)
     if y is None:
         y = torch.empty((rows, W.N), dtype=y_dtype, device=q.device)
     c = W.cstruct()
@@ -353,32 +408,64 @@ def moesq_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16
     return y
 
 
+_DUMPS = F_DUMP_GATEUP | F_DUMP_H
+
+
 def mlp_workspace(rows, I, dump=False, device="cuda"):
     nb = moesq_workspace_bytes(WS_MLP_DUMP if dump else WS_MLP, rows, 0, 0, 0, 0, I)
     return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
 def mlp_workspace_views(ws, rows, I, dump=False):
     """(h_q [rows, I/2], h_s [rows, I/32], gate_up fp32 [rows, 2I] or None) inside an MLP workspace
     (the f16 copy of h sits between h_s and the gate_up dump)."""
-    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     hq = ws[:rows * (I // 2)].view(rows, I // 2)
-    o = a(rows * (I // 2))
+    o = _a256(rows * (I // 2))
     hs = ws[o:o + rows * (I // 32)].view(rows, I // 32)
-    o += a(rows * (I // 32))
-    o += a(rows * I * 2)
+    o += _a256(rows * (I // 32))
+    o += _a256(rows * I * 2)
     d = ws[o:o + rows * 2 * I * 4].view(torch.float32).view(rows, 2 * I) if dump else None
     return hq, hs, d
 
 
+def mlp_hk_view(ws, rows, I):
+    """h_k f16 [rows, I] inside an MLP workspace: the down GEMM's operand copy of the requantized h
+    (moesq_quantize_act's f16 copy format)."""
+    o = _a256(rows * (I // 2)) + _a256(rows * (I // 32))
+    return ws[o:o + rows * I * 2].view(torch.float16).view(rows, I)
+
+
+def mlp_h_views(ws, rows, I):
+    """(h_k f16 [rows, I], and the fp32 h [rows, I] that the requantization read, written with F_DUMP_H)
+    inside a dump-sized MLP workspace."""
+    o = _a256(rows * (I // 2)) + _a256(rows * (I // 32)) + _a256(rows * I * 2) + _a256(rows * 2 * I * 4)
+    h = ws[o:o + rows * I * 4].view(torch.float32).view(rows, I)
+    return mlp_hk_view(ws, rows, I), h
+
+
 def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=torch.bfloat16, workspace=None,
                      flags=0, xk=None):
-    rows = q.shape[0]
+    if flags & F_CALIBRATE:
+        raise ValueError("calibration: use moesq_calibrate_gamma_h")
+    if not (W13.N % 2 == 0 and W2.K == W13.N // 2 and W2.E == W13.E):
+        raise ValueError("W13 [E, 2I, H] and W2 [E, H, I] do not match")
     I = W13.N // 2
+    rows = q.shape[0]
+    dump = bool(flags & _DUMPS)
+    _need(gamma_h, "gamma_h", (W13.E,), torch.float32)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace",
+                    moesq_workspace_bytes(WS_MLP_DUMP if dump else WS_MLP, rows, 0, 0, 0, 0, I))
+    _check_gemm_io(W13, q, s, gamma_a, offsets, xk, flags, y, W2.N)
+    _on_device(q=q, gamma_h=gamma_h, workspace=workspace)
     if y is None:
         y = torch.empty((rows, W2.N), dtype=y_dtype, device=q.device)
     if workspace is None:
-        workspace = mlp_workspace(rows, I, bool(flags & F_DUMP_GATEUP), q.device)
+        workspace = mlp_workspace(rows, I, dump, q.device)
     a, b = W13.cstruct(), W2.cstruct()
     _check("moesq_expert_mlp",
            lib().moesq_expert_mlp(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(xk), _p(gamma_a),
@@ -387,9 +474,38 @@ def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=t
     return y, workspace
 
 
+def moesq_calibrate_gamma_h(W13, W2, q, s, gamma_a, offsets, flags=0, xk=None, workspace=None):
+    """The intermediate tensor scales of the routed-expert MLP (moesq_expert_mlp with F_CALIBRATE):
+    gate_up + SwiGLU on the given rows, per-expert amax(h) and Eq. 5. Returns (gamma_h [E], amax_h [E])
+    as views into the workspace (float32)."""
+    E = W13.E
+    nb = moesq_workspace_bytes(WS_MLP_CALIBRATE, 0, 0, E)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", nb)
+    rows = _check_gemm_io(W13, q, s, gamma_a, offsets, xk, flags)
+    _on_device(q=q, workspace=workspace)
+    if workspace is None:
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    a, b = W13.cstruct(), W2.cstruct()
+    _check("moesq_expert_mlp",
+           lib().moesq_expert_mlp(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(xk), _p(gamma_a),
+                                  None, _p(offsets), rows, None, F32, _p(workspace), workspace.numel(),
+                                  flags | F_CALIBRATE))
+    amax = workspace[:4 * E].view(torch.float32)
+    o = _a256(4 * E)
+    gamma = workspace[o:o + 4 * E].view(torch.float32)
+    return gamma, amax
+
+
 def moesq_unpermute_combine(y_sorted, slot_pos, topk_w, out=None, out_dtype=torch.bfloat16):
     T, k = topk_w.shape
     H = y_sorted.shape[1]
+    _need(y_sorted, "y_sorted", (y_sorted.shape[0], H), y_sorted.dtype)
+    _need(slot_pos, "slot_pos", (T * k,), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    if out is not None:
+        _need(out, "out", (T, H), out.dtype)
+    _on_device(y_sorted=y_sorted, slot_pos=slot_pos, topk_w=topk_w, out=out)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y_sorted.device)
     _check("moesq_unpermute_combine",
@@ -497,7 +613,7 @@ def compress_dense_weights(w, prepack=True):
 
 
 def moesq_dense_grouped_gemm(W, q, s, gamma_a, offsets, y=None, y_dtype=torch.bfloat16, flags=0, xk=None):
-    rows = q.shape[0]
+    rows = _check_gemm_io(W, q, s, gamma_a, offsets, xk, flags, y)
     if y is None:
         y = torch.empty((rows, W.N), dtype=y_dtype, device=q.device)
     c = W.cstruct()

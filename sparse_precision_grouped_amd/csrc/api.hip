@@ -24,13 +24,18 @@ static size_t route_capacity_ws(int64_t n, int32_t E) {
   return align256(route_workspace_bytes(n, E)) + align256((size_t)(E + 1) * 4) + 2 * align256((size_t)n * 4);
 }
 
-// MLP workspace: h_q [rows][I/2], h_s [rows][I/32], h_k [rows][I] f16, then (dump) fp32 [rows][2I],
-// each region starting on a 256-byte boundary.
+// MLP workspace: h_q [rows][I/2], h_s [rows][I/32], h_k [rows][I] f16, then (dumps) the fp32 gate_up
+// outputs [rows][2I] and the fp32 h [rows][I], each region starting on a 256-byte boundary.
+size_t mlp_ws_base(int64_t rows, int32_t I) {
+  return align256((size_t)rows * (I / 2)) + align256((size_t)rows * (I / 32)) + align256((size_t)rows * I * 2);
+}
 size_t mlp_ws(int64_t rows, int32_t I, bool dump) {
-  size_t b = align256((size_t)rows * (I / 2)) + align256((size_t)rows * (I / 32)) + align256((size_t)rows * I * 2);
-  if (dump) b += (size_t)rows * 2 * I * sizeof(float);
+  size_t b = mlp_ws_base(rows, I);
+  if (dump) b += align256((size_t)rows * 2 * I * sizeof(float)) + (size_t)rows * I * sizeof(float);
   return b;
 }
+// Calibration workspace: amax_h [E] f32, then gamma_h [E] f32 at the next 256-byte boundary.
+size_t mlp_calib_ws(int32_t E) { return align256((size_t)E * 4) + (size_t)E * 4; }
 
 }  // namespace
 
@@ -59,6 +64,7 @@ size_t moesq_workspace_bytes(int32_t kind, int64_t T, int32_t k, int32_t E, int3
     case MOESQ_WS_MLP_DUMP: return T >= 0 && I > 0 ? mlp_ws(T, I, true) : 0;
     case MOESQ_WS_COMPRESS: return E > 0 ? (size_t)E * sizeof(uint32_t) : 0;
     case MOESQ_WS_ROUTE_CAPACITY: return (T >= 0 && k > 0 && E > 0) ? route_capacity_ws(T * k, E) : 0;
+    case MOESQ_WS_MLP_CALIBRATE: return E > 0 ? mlp_calib_ws(E) : 0;
     default: return 0;
   }
 }
@@ -251,11 +257,16 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
                      const uint8_t* s, const void* xk, const float* gamma_a, const float* gamma_h,
                      const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype, void* workspace,
                      size_t workspace_bytes, uint32_t flags) {
+  const bool calib = (flags & MOESQ_F_CALIBRATE) != 0;
+  const bool dump = (flags & (MOESQ_F_DUMP_GATEUP | MOESQ_F_DUMP_H)) != 0;
   if (y_dtype != MOESQ_F32 && y_dtype != MOESQ_BF16) return MOESQ_ERR_INVALID_ARG;
-  if (!weights_ok(W13) || !weights_ok(W2) || !gamma_h) return MOESQ_ERR_INVALID_ARG;
+  if (!weights_ok(W13) || !weights_ok(W2) || (!gamma_h && !calib)) return MOESQ_ERR_INVALID_ARG;
+  if (calib && dump) return MOESQ_ERR_INVALID_ARG;
   const int32_t I = W13->N / 2;
   if (W13->N % 2 != 0 || W2->K != I || W2->E != W13->E) return MOESQ_ERR_INVALID_ARG;
-  int rc = gemm_common(W13, q, s, xk, gamma_a, offsets, rows, y);
+  // y is neither read nor written in calibration: a host placeholder stands in for the common checks
+  alignas(16) static const float no_output[4] = {0.f, 0.f, 0.f, 0.f};
+  int rc = gemm_common(W13, q, s, xk, gamma_a, offsets, rows, calib ? (void*)no_output : y);
   if (rc != MOESQ_OK) return rc;
   if (I % 256 != 0 || W13->K % 256 != 0 || W2->N % 64 != 0) return MOESQ_ERR_UNSUPPORTED;
   if (W2->gscale_split != 0 && W2->gscale_split != 1) return MOESQ_ERR_INVALID_ARG;
@@ -263,25 +274,32 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   if (!aligned(W2->kl, 16)) return MOESQ_ERR_UNSUPPORTED;
   if ((int64_t)W2->N * W2->K / 32 * 11 >= ((int64_t)1 << 31) || rows * (I / 2) >= ((int64_t)1 << 31))
     return MOESQ_ERR_UNSUPPORTED;
-  const bool dump = (flags & MOESQ_F_DUMP_GATEUP) != 0;
-  const size_t need = mlp_ws(rows, I, dump);
-  if (rows > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MOESQ_ERR_WORKSPACE;
-  if (rows == 0) return MOESQ_OK;
+  const size_t need = calib ? mlp_calib_ws(W13->E) : mlp_ws(rows, I, dump);
+  if ((rows > 0 || calib) && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return MOESQ_ERR_WORKSPACE;
   if (rows * (int64_t)I * 2 >= ((int64_t)1 << 31)) return MOESQ_ERR_UNSUPPORTED;
-  uint8_t* hq = (uint8_t*)workspace;
-  uint8_t* hs = hq + align256((size_t)rows * (I / 2));
-  uint8_t* hk = hs + align256((size_t)rows * (I / 32));
-  float* dumpp = dump ? (float*)(hk + align256((size_t)rows * I * 2)) : nullptr;
   GemmArgs a{};
   a.kl = W13->kl; a.gscale = W13->gscale;
   a.q = q; a.s = s; a.xk = xk; a.gamma_a = gamma_a; a.offsets = offsets; a.y = nullptr;
   a.E = W13->E; a.N = W13->N; a.K = W13->K; a.y_bf16 = 0; a.gsplit = W13->gscale_split;
   if (capacity_of(flags, W13->E, rows, a.cap) != MOESQ_OK) return MOESQ_ERR_INVALID_ARG;
-  a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk; a.dump = dumpp;
   // few tokens per expert: both GEMMs stream the weights; otherwise both are tiled
   int variant = rows <= (int64_t)16 * W13->E ? 0 : 1;
   if (flags & MOESQ_F_FORCE_DECODE) variant = 0;
   if (flags & MOESQ_F_FORCE_PREFILL) variant = 1;
+  if (calib) {
+    uint32_t* amax = (uint32_t*)workspace;
+    float* gam = (float*)((uint8_t*)workspace + align256((size_t)W13->E * 4));
+    return launch_calibrate_h((hipStream_t)stream, a, rows, variant, amax, gam);
+  }
+  if (rows == 0) return MOESQ_OK;
+  uint8_t* hq = (uint8_t*)workspace;
+  uint8_t* hs = hq + align256((size_t)rows * (I / 2));
+  uint8_t* hk = hs + align256((size_t)rows * (I / 32));
+  uint8_t* dumps = (uint8_t*)workspace + mlp_ws_base(rows, I);
+  a.gamma_h = gamma_h; a.h_q = hq; a.h_s = hs; a.h_k = hk;
+  a.dump = (flags & MOESQ_F_DUMP_GATEUP) ? (float*)dumps : nullptr;
+  a.hdump = (flags & MOESQ_F_DUMP_H) ? (float*)(dumps + align256((size_t)rows * 2 * I * sizeof(float))) : nullptr;
   rc = launch_gemm_variant((hipStream_t)stream, a, rows, variant);
   if (rc != MOESQ_OK) return rc;
   GemmArgs b{};

@@ -403,11 +403,13 @@ MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<t
 // MLP gate_up epilogue for one token (permuted row p; tv: the row is a real token): g0, g1 are the two
 // gate fragments and u0, u1 the matching up fragments of the 32 intermediate columns [ib, ib + 32);
 // lane (r16, cc) holds columns 16 f + 4 cc .. + 3 of fragment f. h = SiLU(g) * u in fp32 (the optional
-// fp32 dump keeps g and u; alpha and alpha_u are the gate and up alpha_e, equal unless the weights carry
-// split tensor scales), then the NVFP4 requantization of the 32-block with the expert's gamma_h
+// fp32 dumps keep g and u, and h; alpha and alpha_u are the gate and up alpha_e, equal unless the weights
+// carry split tensor scales), then the NVFP4 requantization of the 32-block with the expert's gamma_h
 // (amax over the 4 lanes cc = 0..3: xor 16, 32), and the h codes, block scale and optional f16 copy.
-MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float alpha_u,
-                                  float gh, f32x4 g0, f32x4 g1, f32x4 u0, f32x4 u1) {
+// Returns the block's amax(h) for a real token (0 otherwise); in calibration (a.amax_h) nothing but the
+// dumps is written and gh is not used.
+MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float alpha_u,
+                                   float gh, f32x4 g0, f32x4 g1, f32x4 u0, f32x4 u1) {
   const int N = a.N, I = N / 2;
   const f32x4 gg[2] = {g0, g1}, uu[2] = {u0, u1};
   float h[8];
@@ -427,12 +429,18 @@ MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib,
       *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
       *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
     }
+    if (tv && a.hdump) {
+      float4 hv;
+      hv.x = h[4 * f]; hv.y = h[4 * f + 1]; hv.z = h[4 * f + 2]; hv.w = h[4 * f + 3];
+      *(float4*)(a.hdump + p * I + ib + 16 * f + 4 * cc) = hv;
+    }
   }
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
   am = __builtin_fmaxf(am, __shfl_xor(am, 16));
   am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+  if (a.amax_h) return tv ? am : 0.0f;
   const float t = gh * am;
   const float uq = t / 6.0f;
   const uint32_t sc = e4m3_encode(uq);
@@ -461,6 +469,16 @@ MOESQ_DEV void mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib,
     }
     if (cc == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
   }
+  return tv ? am : 0.0f;
+}
+
+// Calibration: the largest of the wave's per-token block amax values goes to the expert's word by one
+// device atomic max on its float bits (non-negative floats order like their bit patterns, so the result
+// does not depend on the order of the atomics).
+MOESQ_DEV void calib_amax_commit(uint32_t* amax_h, int e, float m) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(&amax_h[e], __float_as_uint(m));
 }
 
 // ============================================================================ decode kernel =====
@@ -522,6 +540,7 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
   // tensor scale, a plain wave the scale of its row half
   const float alpha = 1.0f / (wscale(a, e, MLP ? 0 : (n0 >= N / 2)) * a.gamma_a[e]);
   const float alpha_u = MLP ? 1.0f / (wscale(a, e, 1) * a.gamma_a[e]) : alpha;
+  float amx = 0.0f;  // MLP calibration: running amax(h) of this lane's tokens
   for (int tb = 0; tb < ne; tb += 16) {
     f32x4 acc[MF];
 #pragma unroll
@@ -585,8 +604,9 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
 #pragma unroll
             for (int v = 1; v < KS; v++) sum[f] = sum[f] + red[v][f][lane];
           }
-          mlp_epilogue_token(a, off + tok, tv, 32 * bx, c, alpha, alpha_u, a.gamma_h[e], sum[0], sum[1], sum[2],
-                             sum[3]);
+          const float gh = a.amax_h ? 1.0f : a.gamma_h[e];
+          amx = __builtin_fmaxf(amx, mlp_epilogue_token(a, off + tok, tv, 32 * bx, c, alpha, alpha_u, gh, sum[0],
+                                                        sum[1], sum[2], sum[3]));
         }
       } else {
         for (int f = kw; f < MF; f += KS) {
@@ -599,6 +619,7 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
       __syncthreads();
     }
   }
+  if (MLP && a.amax_h && kw == 0) calib_amax_commit(a.amax_h, e, amx);
 }
 
 // ==================================================== dispatch + GEMM in one launch (decode) =====
@@ -1187,14 +1208,16 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   }
   const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
   const float alpha_u = 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]);  // the up rows' alpha_e
-  const float gh = a.gamma_h[c.e];
+  const float gh = a.amax_h ? 1.0f : a.gamma_h[c.e];
+  float amx = 0.0f;
 #pragma unroll
   for (int n = 0; n < NF; n++) {
     if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
-    mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, alpha_u, gh, acc[0][n], acc[1][n], acc[2][n],
-                       acc[3][n]);
+    amx = __builtin_fmaxf(amx, mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, alpha_u, gh, acc[0][n],
+                                                  acc[1][n], acc[2][n], acc[3][n]));
   }
+  if (a.amax_h) calib_amax_commit(a.amax_h, c.e, amx);
 }
 
 // Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the
@@ -1322,7 +1345,8 @@ static bool launch_decode(hipStream_t st, const GemmArgs& a) {
 
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
   if (rows == 0) return MOESQ_OK;
-  if (variant == 0 && a.gamma_h) {
+  const bool mlp = a.gamma_h != nullptr || a.amax_h != nullptr;  // the gate_up GEMM of the MLP
+  if (variant == 0 && mlp) {
     // MLP gate_up by weight streaming: 32 gate + 32 up rows per workgroup
     if (a.xk)
       hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, true>), dim3(a.N / 64, a.E), dim3(256), 0, st, a);
@@ -1345,7 +1369,7 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
     const int grid = 8 * ((device_cu_count() + 7) / 8);
     const bool xk = a.xk != nullptr;
     const size_t lds = tile_lds_bytes(a.E);
-    if (a.gamma_h) {
+    if (mlp) {
       if (xk) hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
       else hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
     } else {
@@ -1367,6 +1391,30 @@ int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int varia
     if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
     else hipLaunchKernelGGL((gemm_tile_kernel<false, false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
   }
+  return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
+}
+
+// gamma_h[e] = Eq. 5 of the expert's amax(h) (float bits); 1 for an expert without tokens (amax 0).
+__global__ void calib_gamma_kernel(const uint32_t* __restrict__ amax_bits, float* __restrict__ gamma_h, int32_t E) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) gamma_h[e] = global_scale_from_amax(__uint_as_float(amax_bits[e]));
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+int launch_calibrate_h(hipStream_t st, GemmArgs a, int64_t rows, int variant, uint32_t* amax_bits, float* gamma_h) {
+  const unsigned nb = (unsigned)((a.E + 255) / 256);
+  // a fill kernel, not a memset: the call may be captured in a graph
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(nb), dim3(256), 0, st, amax_bits, a.E);
+  a.gamma_h = nullptr;
+  a.amax_h = amax_bits;
+  a.h_q = nullptr; a.h_s = nullptr; a.h_k = nullptr;
+  int rc = launch_gemm_variant(st, a, rows, variant);
+  if (rc != MOESQ_OK) return rc;
+  hipLaunchKernelGGL(calib_gamma_kernel, dim3(nb), dim3(256), 0, st, amax_bits, gamma_h, a.E);
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
 

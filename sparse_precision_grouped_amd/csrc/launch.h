@@ -35,6 +35,9 @@ struct GemmArgs {
   uint8_t* h_s;
   void* h_k;              // [rows][I] f16 copy of the requantized h in the kernel's group order, or nullptr
   float* dump;            // [rows][N] fp32 gate_up outputs, or nullptr
+  float* hdump;           // [rows][I] fp32 h = SiLU(g) * u (the values the requantization reads), or nullptr
+  uint32_t* amax_h;       // calibration: [E] per-expert amax(h) as float bits (atomic max; zeroed by the caller);
+                          // when set the epilogue writes no h codes, scales or copies
 };
 
 size_t route_workspace_bytes(int64_t n, int32_t E);
@@ -79,6 +82,9 @@ int launch_unpack(hipStream_t st, const uint8_t* packed, const uint8_t* mask, in
 int launch_gemm(hipStream_t st, const GemmArgs& a, int64_t rows);
 // variant 0 = decode (weight streaming; with gamma_h the MLP gate_up epilogue), 1 = prefill (tiled).
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant);
+// Calibration of the intermediate tensor scales: zero amax_bits [E], run the MLP gate_up GEMM of `a`
+// (a.amax_h = amax_bits) with the given variant, then gamma_h[e] = Eq. 5 of amax_bits[e].
+int launch_calibrate_h(hipStream_t st, GemmArgs a, int64_t rows, int variant, uint32_t* amax_bits, float* gamma_h);
 
 // Route + quantize + decode GEMM in one launch for small decode batches (dispatch_gemm_fused): the
 // same outputs as launch_route_quantize followed by the default weight-streaming GEMM with xk.

@@ -3,6 +3,7 @@
 path; large weight tensors are drawn on the device by the generator's device build, which is
 bit-identical to its host build (checked by test_gen_device_bitexact), and the oracle compresses
 the host draw of the experts it needs."""
+import os
 import sys
 
 import numpy as np
@@ -140,3 +141,53 @@ def sample_expert_rows(offsets, n_experts=3, per_expert=48, seed=0):
                 break
             rows.add(int(r))
     return np.array(sorted(rows), np.int64), sorted(pick)
+
+
+def sample_tile_rows(offsets, n_experts=16, per_expert=64, seed=0, tile=128):
+    """Rows of n_experts experts: the busiest one in full tile coverage (the first and last row of every
+    `tile`-token tile, its last row, plus random rows), the least busy nonempty one and random others
+    (their first rows, last row and random rows, at most per_expert each). Returns (rows, experts)."""
+    offsets = np.asarray(offsets)
+    counts = np.diff(offsets)
+    nz = np.flatnonzero(counts > 0)
+    rng = np.random.default_rng(seed)
+    busiest = int(nz[np.argmax(counts[nz])])
+    pick = [busiest, int(nz[np.argmin(counts[nz])])]
+    pick += [int(e) for e in rng.permutation(nz) if int(e) not in pick][:max(0, n_experts - 2)]
+    rows = set()
+    lo, hi = int(offsets[busiest]), int(offsets[busiest + 1])
+    for t0 in range(lo, hi, tile):
+        rows.update((t0, min(hi, t0 + tile) - 1))
+    rows.update(int(r) for r in rng.choice(np.arange(lo, hi), size=min(hi - lo, per_expert), replace=False))
+    for e in pick[1:]:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        mine = set(range(lo, min(hi, lo + 4))) | {hi - 1}
+        extra = rng.choice(np.arange(lo, hi), size=min(hi - lo, per_expert), replace=False)
+        for r in extra:
+            if len(mine) >= per_expert:
+                break
+            mine.add(int(r))
+        rows |= mine
+    return np.array(sorted(rows), np.int64), sorted(pick)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def gamma_h_table(name):
+    """The per-expert tensor scale of the MLP intermediate for a workload, written by the oracle-only
+    script golden/make_gamma_h.py: (gamma_h [E] float32, amax_h [E] float32, routed rows [E])."""
+    ent = {}
+    with open(os.path.join(GOLDEN, "gamma_h.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            w = line.split()
+            if w[0] == name:
+                ent[int(w[1])] = (float.fromhex(w[3]), float.fromhex(w[2]), int(w[4]))
+    E = len(ent)
+    assert sorted(ent) == list(range(E)), "gamma_h table of %s is incomplete" % name
+    g = np.array([ent[e][0] for e in range(E)], np.float32)
+    a = np.array([ent[e][1] for e in range(E)], np.float32)
+    n = np.array([ent[e][2] for e in range(E)], np.int64)
+    return g, a, n

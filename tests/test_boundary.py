@@ -223,13 +223,19 @@ def test_gemm_and_mlp_validation(L):
                   ctypes.c_int32, vp, ctypes.c_size_t, ctypes.c_uint32]
     W13 = CW(4, 512, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
     W2 = CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)
-    mc = lambda a, b, ws=FAKE, wsb=1 << 30: m(None, ctypes.byref(a), ctypes.byref(b), _p(FAKE), _p(FAKE),  # noqa
-                                             None, _p(FAKE), _p(FAKE), _p(FAKE), 16, _p(FAKE), 0,
-                                             _p(ws) if ws else None, wsb, 0)
+    mc = lambda a, b, ws=FAKE, wsb=1 << 30, gh=FAKE, fl=0: m(  # noqa: E731
+        None, ctypes.byref(a), ctypes.byref(b), _p(FAKE), _p(FAKE), None, _p(FAKE), _p(gh) if gh else None, _p(FAKE),
+        16, _p(FAKE), 0, _p(ws) if ws else None, wsb, fl)
     assert mc(W13, CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # W2.K != I
     assert mc(W13, CW(3, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE)) == EARG   # expert count mismatch
     assert mc(W13, W2, ws=0) == EWS
     assert mc(W13, W2, wsb=10) == EWS
+    assert mc(W13, W2, gh=0) == EARG                                         # gamma_h is required ...
+    CAL, DUMP_G, DUMP_H = 32, 1, 16
+    assert mc(W13, W2, gh=0, fl=CAL, wsb=10) == EWS                         # ... except in calibration
+    assert mc(W13, W2, gh=0, fl=CAL, ws=0) == EWS
+    assert mc(W13, W2, fl=CAL | DUMP_G) == EARG                              # no dumps in calibration
+    assert mc(W13, W2, fl=CAL | DUMP_H) == EARG
     assert mc(CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE), CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS  # I = 128
 
 
@@ -273,5 +279,9 @@ def test_workspace_sizes(L):
     rows, I = 1000, 2048
     base = a(rows * I // 2) + a(rows * I // 32) + a(rows * I * 2)
     assert ws(2, rows, 0, 384, 7168, 0, I) == base
-    assert ws(3, rows, 0, 384, 7168, 0, I) == base + rows * 2 * I * 4
+    # the dumps: fp32 gate_up [rows][2I], then fp32 h [rows][I], each region 256-byte aligned
+    assert ws(3, rows, 0, 384, 7168, 0, I) == base + a(rows * 2 * I * 4) + rows * I * 4
     assert ws(4, E=384) == 384 * 4
+    # calibration: amax_h [E] f32, then gamma_h [E] f32 at the next 256-byte boundary
+    assert ws(6, E=384) == a(384 * 4) + 384 * 4
+    assert ws(6, E=0) == 0
