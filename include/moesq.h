@@ -275,6 +275,27 @@ int moesq_expert_mlp(void *stream, const moesq_weights *W13, const moesq_weights
                      size_t workspace_bytes, uint32_t flags);
 
 /*
+ * moesq_expert_mlp for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same call, arguments and results, without the
+ * workspace argument. Its workspace is a static device array of MOESQ_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; its device address is looked up on the first call
+ * on each device (make that first call outside graph capture). The call itself allocates nothing.
+ *   Limit: the call's workspace, moesq_workspace_bytes(MOESQ_WS_MLP, rows, 0, E, H, 0, I), must fit in
+ *   MOESQ_NOALLOC_SCRATCH_BYTES, else MOESQ_ERR_WORKSPACE and nothing is launched (I = 2048: up to
+ *   6472 rows; the decode-sized batches this is for take a few hundred).
+ *   Every call on one GPU uses that GPU's one array: calls that may overlap on one GPU (different
+ *   streams without ordering) race and must not be issued; calls ordered on one stream are safe. The
+ *   array keeps the last call's contents; nothing in it needs to start at zero.
+ * Errors: as moesq_expert_mlp; MOESQ_ERR_INVALID_ARG with MOESQ_F_DUMP_GATEUP, MOESQ_F_DUMP_H or
+ * MOESQ_F_CALIBRATE (their results would stay in the array); MOESQ_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+#define MOESQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moesq_expert_mlp_noalloc(void *stream, const moesq_weights *W13, const moesq_weights *W2, const uint8_t *q,
+                             const uint8_t *s, const void *xk, const float *gamma_a, const float *gamma_h,
+                             const int32_t *offsets, int64_t rows, void *y, int32_t y_dtype, uint32_t flags);
+
+/*
  * Router-weighted unpermute + combine (paper Appendix D.1, token combination):
  *   out[t][c] = sum over j = 0..k-1 (in that order, fp32) of topk_w[t][j] * y_sorted[slot_pos[t*k+j]][c]
  * Slots with slot_pos = -1 contribute nothing. out is fp32 or bf16 (round to nearest even).

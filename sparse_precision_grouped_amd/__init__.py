@@ -20,7 +20,7 @@ __all__ = [
     "moesq_prepack_weights", "moesq_kernel_layout_bytes",
     "F32", "BF16", "F_DUMP_GATEUP", "F_FORCE_DECODE", "F_FORCE_PREFILL", "F_CAPACITY", "F_DUMP_H", "F_CALIBRATE",
     "WS_ROUTE", "WS_MLP", "WS_MLP_DUMP", "WS_COMPRESS", "WS_ROUTE_CAPACITY", "WS_MLP_CALIBRATE",
-    "moesq_route_capacity", "moesq_calibrate_gamma_h",
+    "moesq_route_capacity", "moesq_calibrate_gamma_h", "moesq_expert_mlp_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_PATTERN, ERR_HIP = 0, -
 F32, BF16 = 0, 1
 F_DUMP_GATEUP, F_FORCE_DECODE, F_FORCE_PREFILL, F_CAPACITY, F_DUMP_H, F_CALIBRATE = 1, 2, 4, 8, 16, 32
 WS_ROUTE, WS_MLP, WS_MLP_DUMP, WS_COMPRESS, WS_ROUTE_CAPACITY, WS_MLP_CALIBRATE = 1, 2, 3, 4, 5, 6
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOESQ_NOALLOC_SCRATCH_BYTES
 
 
 class MoesqError(RuntimeError):
@@ -67,6 +68,7 @@ def lib():
         L.moesq_route_quantize_gemm.argtypes = [vp, vp, i64, i32, i32, vp, i32, i32, i64, vp, W, vp, vp, vp,
                                                 vp, vp, sz, vp, vp, vp, vp, i32, vp]
         L.moesq_expert_mlp.argtypes = [vp, W, W, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, u32]
+        L.moesq_expert_mlp_noalloc.argtypes = [vp, W, W, vp, vp, vp, vp, vp, vp, i64, vp, i32, u32]
         L.moesq_unpermute_combine.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, vp, i32]
         L.moesq_compress_weights.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moesq_unpack_weights.argtypes = [vp, W, vp, vp]
@@ -84,7 +86,7 @@ def lib():
         L.moesq_status_str.restype = ctypes.c_char_p
         L.moesq_version.restype = i32
         for name in ("moesq_route_permute", "moesq_route_capacity", "moesq_quantize_act", "moesq_route_quantize", "moesq_route_quantize_dyn", "moesq_route_quantize_gemm", "moesq_grouped_gemm",
-                     "moesq_expert_mlp",
+                     "moesq_expert_mlp", "moesq_expert_mlp_noalloc",
                      "moesq_unpermute_combine", "moesq_compress_weights", "moesq_unpack_weights", "moesq_global_scale",
                      "moesq_prepack_weights"):
             getattr(L, name).restype = ctypes.c_int
@@ -472,6 +474,23 @@ def moesq_expert_mlp(W13, W2, q, s, gamma_a, gamma_h, offsets, y=None, y_dtype=t
                                   _p(gamma_h), _p(offsets), rows, _p(y), _dtype_code(y.dtype), _p(workspace),
                                   workspace.numel(), flags))
     return y, workspace
+
+
+def moesq_expert_mlp_noalloc(W13, W2, q, s, gamma_a, gamma_h, offsets, y, flags=0, xk=None):
+    """moesq_expert_mlp without a workspace argument: the library's static per-GPU scratch array holds the
+    intermediate h (for callers that cannot allocate; the caller passes the output y). Calls that may
+    overlap on one GPU race on that array."""
+    if not (W13.N % 2 == 0 and W2.K == W13.N // 2 and W2.E == W13.E):
+        raise ValueError("W13 [E, 2I, H] and W2 [E, H, I] do not match")
+    _need(gamma_h, "gamma_h", (W13.E,), torch.float32)
+    rows = _check_gemm_io(W13, q, s, gamma_a, offsets, xk, flags, y, W2.N)
+    _on_device(q=q, gamma_h=gamma_h, y=y)
+    a, b = W13.cstruct(), W2.cstruct()
+    _check("moesq_expert_mlp_noalloc",
+           lib().moesq_expert_mlp_noalloc(_stream(), ctypes.byref(a), ctypes.byref(b), _p(q), _p(s), _p(xk),
+                                          _p(gamma_a), _p(gamma_h), _p(offsets), rows, _p(y), _dtype_code(y.dtype),
+                                          flags))
+    return y
 
 
 def moesq_calibrate_gamma_h(W13, W2, q, s, gamma_a, offsets, flags=0, xk=None, workspace=None):

@@ -4,9 +4,38 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 using namespace moesq;
+
+// Workspace of moesq_expert_mlp_noalloc: a file-scope device array, one copy per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, not the device copy: its device
+// address comes from hipGetSymbolAddress, once per device with that device current, and only that
+// address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOESQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device), or nullptr.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -308,6 +337,19 @@ int moesq_expert_mlp(void* stream, const moesq_weights* W13, const moesq_weights
   b.E = W2->E; b.N = W2->N; b.K = W2->K; b.y_bf16 = y_dtype == MOESQ_BF16; b.gsplit = W2->gscale_split;
   b.cap = a.cap;
   return launch_gemm_variant((hipStream_t)stream, b, rows, variant);
+}
+
+int moesq_expert_mlp_noalloc(void* stream, const moesq_weights* W13, const moesq_weights* W2, const uint8_t* q,
+                             const uint8_t* s, const void* xk, const float* gamma_a, const float* gamma_h,
+                             const int32_t* offsets, int64_t rows, void* y, int32_t y_dtype, uint32_t flags) {
+  if (!W13 || W13->N <= 0 || W13->N % 2 != 0 || rows < 0) return MOESQ_ERR_INVALID_ARG;
+  // the dumps and the calibration write into the workspace, which the caller cannot see here
+  if (flags & (MOESQ_F_DUMP_GATEUP | MOESQ_F_DUMP_H | MOESQ_F_CALIBRATE)) return MOESQ_ERR_INVALID_ARG;
+  if (mlp_ws(rows, W13->N / 2, false) > (size_t)MOESQ_NOALLOC_SCRATCH_BYTES) return MOESQ_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOESQ_ERR_HIP;
+  return moesq_expert_mlp(stream, W13, W2, q, s, xk, gamma_a, gamma_h, offsets, rows, y, y_dtype, ws,
+                          MOESQ_NOALLOC_SCRATCH_BYTES, flags);
 }
 
 int moesq_unpermute_combine(void* stream, const void* y_sorted, int32_t y_dtype, const int32_t* slot_pos,

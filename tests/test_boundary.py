@@ -236,6 +236,17 @@ def test_gemm_and_mlp_validation(L):
     assert mc(W13, W2, gh=0, fl=CAL, ws=0) == EWS
     assert mc(W13, W2, fl=CAL | DUMP_G) == EARG                              # no dumps in calibration
     assert mc(W13, W2, fl=CAL | DUMP_H) == EARG
+    # the no-allocation form: batches beyond its static workspace, and the dump / calibration flags
+    na = L.moesq_expert_mlp_noalloc
+    na.argtypes = [vp, ctypes.POINTER(CW), ctypes.POINTER(CW), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+                   ctypes.c_int32, ctypes.c_uint32]
+    K13, K2 = CW(384, 4096, 7168, FAKE, FAKE, FAKE, FAKE, FAKE), CW(384, 7168, 2048, FAKE, FAKE, FAKE, FAKE, FAKE)
+    nc = lambda rows, fl=0: na(None, ctypes.byref(K13), ctypes.byref(K2), _p(FAKE), _p(FAKE), None,  # noqa: E731
+                               _p(FAKE), _p(FAKE), _p(FAKE), rows, _p(FAKE), 0, fl)
+    assert nc(6473) == EWS                      # I = 2048: 6472 rows fit in 32 MiB, 6473 do not
+    assert nc(100000) == EWS
+    for fl in (DUMP_G, DUMP_H, CAL):
+        assert nc(16, fl) == EARG
     assert mc(CW(4, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE), CW(4, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE)) == EUNS  # I = 128
 
 
