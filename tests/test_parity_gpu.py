@@ -22,6 +22,10 @@ ROW_TOL = 1e-5    # relative error of every single fp32 output row: a few wrong 
                   # here even where the block's norm would hide them (fp32 accumulation alone: ~1e-7)
 
 
+def bf16_round(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def gemm_gate(got, ref, what="gemm"):
     """fp32 GEMM outputs against the fp64 oracle: the block's rel-Frobenius error <= GEMM_TOL and each
     row's own relative error <= ROW_TOL (a row whose reference is zero must be zero)."""
