@@ -94,10 +94,12 @@ MOESQ_DEV void quant8_block4(const float v[8], float gamma, uint32_t& codes, uin
 MOESQ_DEV uint32_t f16x2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 MOESQ_DEV f16x2 bits_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 
-// Two UE4M3 codes in the low 16 bits of w -> (v0, v0) and (v1, v1) as f16x2 (exact: the gfx950
-// FP8 convert with unit scale, on the bytes duplicated by a perm).
-MOESQ_DEV void e4m3_pair_f16x2(uint32_t w, f16x2& s0, f16x2& s1) {
-  const uint32_t d = __builtin_amdgcn_perm(0u, w, 0x01010000u);  // bytes (b0, b0, b1, b1)
+// Two UE4M3 codes in the low 16 bits of w (hi: the high 16 bits) -> (v0, v0) and (v1, v1) as f16x2
+// (exact: the gfx950 FP8 convert with unit scale, on the bytes duplicated by a perm). Selecting the
+// half in the perm, not by a shift where the word is loaded, keeps a freshly loaded word untouched
+// until it is used, so its load is not waited for early.
+MOESQ_DEV void e4m3_pair_f16x2(uint32_t w, f16x2& s0, f16x2& s1, bool hi = false) {
+  const uint32_t d = __builtin_amdgcn_perm(0u, w, hi ? 0x03030202u : 0x01010000u);  // (b0, b0, b1, b1)
   s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, false);
   s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
 }

@@ -69,6 +69,10 @@ MOESQ_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// s_waitcnt operand that waits until at most n (< 16) vector-memory operations are outstanding and does
+// not wait on the other counters (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
+
 // Workgroup barrier that orders LDS accesses only: global loads and stores issued before it stay in
 // flight (a plain __syncthreads waits for every outstanding memory operation of the wave).
 MOESQ_DEV void lds_barrier() {
@@ -77,7 +81,10 @@ MOESQ_DEV void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One 256-K super-step of MF A fragments (16 rows each) for one lane.
+// One 256-K super-step of MF A fragments (16 rows each) for one lane. sw[f] holds fragment f's two
+// scale codes in its low half (load_w, the weight-streaming kernel's loads), or, from the tiled kernel's
+// half-stage loads, the loaded word itself with the codes in its high half for odd f (a freshly loaded
+// word is then not touched until it is used, so its load is not waited for early).
 template <int MF>
 struct WStage {
   u32x4 pk[MF];
@@ -136,10 +143,10 @@ struct WMeta {
 };
 
 template <int MF>
-MOESQ_DEV WMeta w_meta(const WStage<MF>& w, int f) {
+MOESQ_DEV WMeta w_meta(const WStage<MF>& w, int f, bool odd_high = false) {
   WMeta m;
   sparse_index_words(w.mk[f], m.i02, m.i13);
-  e4m3_pair_f16x2(w.sw[f], m.s01, m.s23);
+  e4m3_pair_f16x2(w.sw[f], m.s01, m.s23, odd_high && (f & 1) != 0);
   return m;
 }
 
@@ -323,7 +330,7 @@ template <int MF>
 MOESQ_DEV DMeta dense_meta(const DWStage<MF>& w, int f) {
   DMeta m;
   e4m3_pair_f16x2(w.sc[f], m.lo01, m.hi01);
-  e4m3_pair_f16x2(w.sc[f] >> 16, m.lo23, m.hi23);
+  e4m3_pair_f16x2(w.sc[f], m.lo23, m.hi23, true);
   return m;
 }
 
@@ -400,14 +407,22 @@ MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<f
 template <int MF>
 MOESQ_DEV void stage_mma(f32x4 (&acc)[MF], const WS<MF, true>& w, const DStage<true>& x) { dense_superstep_xk(acc, w.w, x.x); }
 
+// Epilogue forms of the GEMM kernels, fixed at compile time so that the production kernels carry no
+// dump or calibration code (the weight-streaming MLP kernel runs at its register cap).
+constexpr int kEpiPlain = 0;    // plain GEMM output (alpha_e, fp32 or bf16 store)
+constexpr int kEpiMlp = 1;      // gate_up of the MLP: SwiGLU + NVFP4 requantization of h
+constexpr int kEpiMlpDump = 2;  // kEpiMlp plus the fp32 gate_up and h dumps (GemmArgs::dump / hdump)
+constexpr int kEpiCalib = 3;    // gate_up + SwiGLU, per-expert amax(h) only (GemmArgs::amax_h)
+
 // MLP gate_up epilogue for one token (permuted row p; tv: the row is a real token): g0, g1 are the two
 // gate fragments and u0, u1 the matching up fragments of the 32 intermediate columns [ib, ib + 32);
 // lane (r16, cc) holds columns 16 f + 4 cc .. + 3 of fragment f. h = SiLU(g) * u in fp32 (the optional
 // fp32 dumps keep g and u, and h; alpha and alpha_u are the gate and up alpha_e, equal unless the weights
 // carry split tensor scales), then the NVFP4 requantization of the 32-block with the expert's gamma_h
 // (amax over the 4 lanes cc = 0..3: xor 16, 32), and the h codes, block scale and optional f16 copy.
-// Returns the block's amax(h) for a real token (0 otherwise); in calibration (a.amax_h) nothing but the
-// dumps is written and gh is not used.
+// Returns the block's amax(h) for a real token (0 otherwise); in calibration (EPI = kEpiCalib) nothing
+// is written and gh is not used.
+template <int EPI>
 MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib, int cc, float alpha, float alpha_u,
                                    float gh, f32x4 g0, f32x4 g1, f32x4 u0, f32x4 u1) {
   const int N = a.N, I = N / 2;
@@ -421,7 +436,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
       const float u = uu[f][r] * alpha_u;
       h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
     }
-    if (tv && a.dump) {
+    if (EPI == kEpiMlpDump && tv && a.dump) {
       const int64_t rowo = p * N;
       float4 gv, uv;
       gv.x = gg[f][0] * alpha; gv.y = gg[f][1] * alpha; gv.z = gg[f][2] * alpha; gv.w = gg[f][3] * alpha;
@@ -429,7 +444,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
       *(float4*)(a.dump + rowo + ib + 16 * f + 4 * cc) = gv;
       *(float4*)(a.dump + rowo + I + ib + 16 * f + 4 * cc) = uv;
     }
-    if (tv && a.hdump) {
+    if (EPI == kEpiMlpDump && tv && a.hdump) {
       float4 hv;
       hv.x = h[4 * f]; hv.y = h[4 * f + 1]; hv.z = h[4 * f + 2]; hv.w = h[4 * f + 3];
       *(float4*)(a.hdump + p * I + ib + 16 * f + 4 * cc) = hv;
@@ -440,7 +455,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
   for (int i = 0; i < 8; i++) am = __builtin_fmaxf(am, __builtin_fabsf(h[i]));
   am = __builtin_fmaxf(am, __shfl_xor(am, 16));
   am = __builtin_fmaxf(am, __shfl_xor(am, 32));
-  if (a.amax_h) return tv ? am : 0.0f;
+  if (EPI == kEpiCalib) return tv ? am : 0.0f;
   const float t = gh * am;
   const float uq = t / 6.0f;
   const uint32_t sc = e4m3_encode(uq);
@@ -496,7 +511,7 @@ MOESQ_DEV void calib_amax_commit(uint32_t* amax_h, int e, float m) {
 // at 168 VGPRs for 3 waves per SIMD (no spills). The f16-operand forms of the dense control and of the
 // MLP epilogue need more with two activation stages, so they hold one: each step's activations are
 // reloaded right after that step's MFMAs, while the weights stay double-buffered.
-template <int MF, int KS, int RG, bool XK, bool DENSE, bool MLP = false>
+template <int MF, int KS, int RG, bool XK, bool DENSE, int MLP = kEpiPlain>
 __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3, 3))) void gemm_decode_kernel(GemmArgs a) {
   // the f16-operand forms of the dense control and of the MLP epilogue hold one activation stage
   constexpr bool kOneX = (DENSE || MLP) && XK;
@@ -540,7 +555,6 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
   // tensor scale, a plain wave the scale of its row half
   const float alpha = 1.0f / (wscale(a, e, MLP ? 0 : (n0 >= N / 2)) * a.gamma_a[e]);
   const float alpha_u = MLP ? 1.0f / (wscale(a, e, 1) * a.gamma_a[e]) : alpha;
-  float amx = 0.0f;  // MLP calibration: running amax(h) of this lane's tokens
   for (int tb = 0; tb < ne; tb += 16) {
     f32x4 acc[MF];
 #pragma unroll
@@ -551,7 +565,7 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
     const uint32_t voq = (uint32_t)tok * (K / 2) + 32u * (c >> 1) + 4u * (c & 1);
     const uint32_t vos = (uint32_t)tok * (K / 32) + 2u * (c >> 1);
     const uint32_t vox = (uint32_t)tok * (uint32_t)(2 * K) + 16u * (8u * (c >> 1) + (c & 1));
-    WS<MF, DENSE, MLP> w0, w1;
+    WS<MF, DENSE, (MLP != kEpiPlain)> w0, w1;
     DStage<XK> x0, x1;
     int ss = kw;
     if (ss < nss) {
@@ -604,9 +618,11 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
 #pragma unroll
             for (int v = 1; v < KS; v++) sum[f] = sum[f] + red[v][f][lane];
           }
-          const float gh = a.amax_h ? 1.0f : a.gamma_h[e];
-          amx = __builtin_fmaxf(amx, mlp_epilogue_token(a, off + tok, tv, 32 * bx, c, alpha, alpha_u, gh, sum[0],
-                                                        sum[1], sum[2], sum[3]));
+          const float gh = MLP == kEpiCalib ? 1.0f : a.gamma_h[e];
+          const float am = mlp_epilogue_token<MLP>(a, off + tok, tv, 32 * bx, c, alpha, alpha_u, gh, sum[0], sum[1],
+                                                   sum[2], sum[3]);
+          // calibration: one atomic max per 16-token block (nothing carried across the block loop)
+          if (MLP == kEpiCalib) calib_amax_commit(a.amax_h, e, am);
         }
       } else {
         for (int f = kw; f < MF; f += KS) {
@@ -619,7 +635,6 @@ __global__ __launch_bounds__(64 * KS * RG) __attribute__((amdgpu_waves_per_eu(3,
       __syncthreads();
     }
   }
-  if (MLP && a.amax_h && kw == 0) calib_amax_commit(a.amax_h, e, amx);
 }
 
 // ==================================================== dispatch + GEMM in one launch (decode) =====
@@ -990,24 +1005,91 @@ MOESQ_DEV void dense_superstep_lds(f32x4 (&acc)[MF][NF], const DWStage<MF>& w, c
 }
 
 // Weight stage of the tiled kernel: the sparse layout or the dense control.
+// The sparse weights of a super-step in two halves: half 0 = the packed bytes of steps 0-1 of every
+// fragment (8 of the lane's 16 bytes) plus the super-step's index and scale codes, half 1 = the packed
+// bytes of steps 2-3. Half 0 of the next super-step is loaded as soon as steps 0-1 have decoded theirs
+// (the index and scale codes live on in the decoded metadata), half 1 after steps 2-3: each load has
+// half a super-step of MFMAs to arrive in, with no more registers than one full stage.
+template <int MF, bool SPLIT>
+MOESQ_DEV void load_w_half0(WStage<MF>& st, rsrc_t rw, const WSrc& src, int lane, int ss) {
+  const uint32_t go = src.g0 + (uint32_t)ss * kGroupBytes;
+  auto pk01 = [&](int f, uint32_t g, int j) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(g + 1024u * j + 16u * lane), 0, 0);
+    st.pk[f].x = v[0];
+    st.pk[f].y = v[1];
+  };
+  if (MF == 4 && !SPLIT) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) pk01(j, go, j);
+    const u32x4 m = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(go + 4096u + 16u * lane), 0, 0));
+    st.mk[0] = m.x; st.mk[1] = m.y; st.mk[2] = m.z; st.mk[3] = m.w;
+    const auto sc = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(go + 5120u + 8u * lane), 0, 0);
+    st.sw[0] = sc[0]; st.sw[1] = sc[0]; st.sw[2] = sc[1]; st.sw[3] = sc[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < (MF == 4 ? 2 : 1); h++) {
+      const uint32_t g = (h == 0 ? src.g0 : src.g1) + (uint32_t)ss * kGroupBytes;
+      const int j = h == 0 ? src.j0 : src.j1;
+      pk01(2 * h, g, j);
+      pk01(2 * h + 1, g, j + 1);
+      const auto m = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(g + 4096u + 16u * lane + 4u * j), 0, 0);
+      st.mk[2 * h] = m[0];
+      st.mk[2 * h + 1] = m[1];
+      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)(g + 5120u + 8u * lane + 2u * j), 0, 0);
+      st.sw[2 * h] = sc;
+      st.sw[2 * h + 1] = sc;
+    }
+  }
+}
+
+template <int MF, bool SPLIT>
+MOESQ_DEV void load_w_half1(WStage<MF>& st, rsrc_t rw, const WSrc& src, int lane, int ss) {
+#pragma unroll
+  for (int f = 0; f < MF; f++) {
+    const bool second = SPLIT && f >= 2;
+    const uint32_t g = (second ? src.g1 : src.g0) + (uint32_t)ss * kGroupBytes;
+    const int j = SPLIT ? (second ? src.j1 + f - 2 : src.j0 + f) : src.j0 + f;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(g + 1024u * j + 16u * lane + 8u), 0, 0);
+    st.pk[f].z = v[0];
+    st.pk[f].w = v[1];
+  }
+}
+
+// Weight stage of the tiled kernel, driven as two halves: load0 / load1 fetch a super-step's halves,
+// half<0> runs steps 0-1 (decoding the super-step's metadata first) and half<1> steps 2-3. kLoads1 is
+// the number of vector-memory loads load1 issues per wave.
 template <int MF, bool MLP, bool DENSE>
 struct TWS;
 template <int MF, bool MLP>
 struct TWS<MF, MLP, false> {
+  static constexpr int kLoads1 = MF;
   WStage<MF> w;
-  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w<MF, MLP>(w, rw, src, lane, ss); }
-  template <int NF, bool XK>
-  MOESQ_DEV void mma(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) const {
-    mma_superstep_lds<MF, NF, XK>(acc, w, Bs, r16, c, nv);
+  WMeta m[MF];
+  MOESQ_DEV void load0(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w_half0<MF, MLP>(w, rw, src, lane, ss); }
+  MOESQ_DEV void load1(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w_half1<MF, MLP>(w, rw, src, lane, ss); }
+  template <int H, int NF, bool XK>
+  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
+    if (H == 0) {
+#pragma unroll
+      for (int f = 0; f < MF; f++) m[f] = w_meta(w, f, true);
+      lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+      lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+    } else {
+      lds_step<2, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+      lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+    }
   }
 };
+// The dense control keeps one stage: the whole super-step in half 0, loaded after it.
 template <int MF, bool MLP>
 struct TWS<MF, MLP, true> {
+  static constexpr int kLoads1 = 0;
   DWStage<MF> w;
-  MOESQ_DEV void load(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
-  template <int NF, bool XK>
-  MOESQ_DEV void mma(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) const {
-    dense_superstep_lds<MF, NF>(acc, w, Bs, r16, c, nv);
+  MOESQ_DEV void load0(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
+  MOESQ_DEV void load1(rsrc_t, const WSrc&, int, int) {}
+  template <int H, int NF, bool XK>
+  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
+    if (H == 0) dense_superstep_lds<MF, NF>(acc, w, Bs, r16, c, nv);
   }
 };
 
@@ -1157,7 +1239,7 @@ MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int
 MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) { stage_p(p, Bs, (int)ba.tok, (int)ba.qtr); }
 
 // Epilogue of a finished tile.
-template <int MF, int NF, bool MLP>
+template <int MF, int NF, int MLP>
 MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc) {
   const int N = a.N;
   const float alpha = c.alpha;
@@ -1208,16 +1290,16 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   }
   const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
   const float alpha_u = 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]);  // the up rows' alpha_e
-  const float gh = a.amax_h ? 1.0f : a.gamma_h[c.e];
+  const float gh = MLP == kEpiCalib ? 1.0f : a.gamma_h[c.e];
   float amx = 0.0f;
 #pragma unroll
   for (int n = 0; n < NF; n++) {
     if (n >= c.nv) break;
     const int tok = c.tb + n * 16 + r16;
-    amx = __builtin_fmaxf(amx, mlp_epilogue_token(a, c.off + tok, tok < c.ne, ib, cc, alpha, alpha_u, gh, acc[0][n],
-                                                  acc[1][n], acc[2][n], acc[3][n]));
+    amx = __builtin_fmaxf(amx, mlp_epilogue_token<MLP>(a, c.off + tok, tok < c.ne, ib, cc, alpha, alpha_u, gh,
+                                                       acc[0][n], acc[1][n], acc[2][n], acc[3][n]));
   }
-  if (a.amax_h) calib_amax_commit(a.amax_h, c.e, amx);
+  if (MLP == kEpiCalib) calib_amax_commit(a.amax_h, c.e, amx);
 }
 
 // Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the
@@ -1227,7 +1309,7 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
 // the next tile -- are in flight, and its weights are loaded into the one register stage as soon as
 // step i's MFMAs have read it; one barrier per step. (One weight stage measured as fast as two; the
 // registers it frees hold the B read-ahead of the sparse kernels and the dense control's larger stage.)
-template <bool MLP, bool XK, bool DENSE = false>
+template <int MLP, bool XK, bool DENSE = false>
 __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) {
   constexpr int MF = 4, NF = kTileNF;
   constexpr int BBYTES = kBTileBytes;
@@ -1257,10 +1339,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
 #pragma unroll
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  TileCtx<MF> cur = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t, w);
-  TWS<MF, MLP, DENSE> wc;
+  constexpr bool kMlp = MLP != kEpiPlain;
+  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t, w);
+  TWS<MF, kMlp, DENSE> wc;
   PStage p;
-  wc.load(cur.rw, cur.src, lane, 0);
+  wc.load0(cur.rw, cur.src, lane, 0);
+  wc.load1(cur.rw, cur.src, lane, 0);
   issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
   if (!XK) stage_b(p, Bs0, ba);
   __builtin_amdgcn_s_waitcnt(0);
@@ -1276,22 +1360,30 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     }
     const bool has_n = t_n < tend;
     TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, MLP, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     if (has_n) issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
-    wc.template mma<NF, XK>(acc, Bc, r16, cc, cur.nv);
-    if (has_n) wc.load(nxt.rw, nxt.src, lane, ss_n);  // the weight stage, reloaded once read
-    if (ss == nss - 1) {
+    wc.template half<0, NF, XK>(acc, Bc, r16, cc, cur.nv);
+    if (has_n) wc.load0(nxt.rw, nxt.src, lane, ss_n);  // half 0 of the next super-step, its registers read
+    wc.template half<1, NF, XK>(acc, Bc, r16, cc, cur.nv);
+    const bool tile_end = ss == nss - 1;
+    if (tile_end) {
       tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
 #pragma unroll
       for (int f = 0; f < MF; f++)
 #pragma unroll
         for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
+    if (has_n) wc.load1(nxt.rw, nxt.src, lane, ss_n);
     if (has_n && !XK) stage_b(p, Bn, ba);
     if (XK) {
-      __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next step
+      // the direct-to-LDS loads of the next step (issued first) must have landed; the kLoads1 weight
+      // loads issued last may stay in flight. Loads complete in issue order, so waiting until at most
+      // kLoads1 vector-memory operations are outstanding is enough; after an epilogue (stores in flight,
+      // which need not complete in order with the loads) everything is waited for.
+      if (tile_end || !has_n) __builtin_amdgcn_s_waitcnt(0);
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(TWS<MF, kMlp, DENSE>::kLoads1));
       __syncthreads();
     } else {
       lds_barrier();  // epilogue stores may still be in flight
@@ -1345,13 +1437,22 @@ static bool launch_decode(hipStream_t st, const GemmArgs& a) {
 
 int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int variant) {
   if (rows == 0) return MOESQ_OK;
-  const bool mlp = a.gamma_h != nullptr || a.amax_h != nullptr;  // the gate_up GEMM of the MLP
-  if (variant == 0 && mlp) {
+  // the gate_up GEMM of the MLP: its epilogue form
+  const int epi = a.amax_h ? kEpiCalib : (a.dump || a.hdump) ? kEpiMlpDump : a.gamma_h ? kEpiMlp : kEpiPlain;
+  if (variant == 0 && epi != kEpiPlain) {
     // MLP gate_up by weight streaming: 32 gate + 32 up rows per workgroup
-    if (a.xk)
-      hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, true>), dim3(a.N / 64, a.E), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, false, false, true>), dim3(a.N / 64, a.E), dim3(256), 0, st, a);
+    const dim3 grid(a.N / 64, a.E), block(256);
+    if (a.xk) {
+      if (epi == kEpiMlp) hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, kEpiMlp>), grid, block, 0, st, a);
+      else if (epi == kEpiMlpDump)
+        hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, kEpiMlpDump>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, true, false, kEpiCalib>), grid, block, 0, st, a);
+    } else {
+      if (epi == kEpiMlp) hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, false, false, kEpiMlp>), grid, block, 0, st, a);
+      else if (epi == kEpiMlpDump)
+        hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, false, false, kEpiMlpDump>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((gemm_decode_kernel<4, 4, 1, false, false, kEpiCalib>), grid, block, 0, st, a);
+    }
   } else if (variant == 0) {
     bool ok = false;
     switch (decode_variant_default()) {
@@ -1369,12 +1470,21 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
     const int grid = 8 * ((device_cu_count() + 7) / 8);
     const bool xk = a.xk != nullptr;
     const size_t lds = tile_lds_bytes(a.E);
-    if (mlp) {
-      if (xk) hipLaunchKernelGGL((gemm_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
-      else hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
+    const dim3 g(grid), b(kTileThreads);
+    if (xk) {
+      switch (epi) {
+        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, true>), g, b, lds, st, a); break;
+        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, true>), g, b, lds, st, a); break;
+        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, true>), g, b, lds, st, a); break;
+        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true>), g, b, lds, st, a); break;
+      }
     } else {
-      if (xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
-      else hipLaunchKernelGGL((gemm_tile_kernel<false, false>), dim3(grid), dim3(kTileThreads), lds, st, a);
+      switch (epi) {
+        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, false>), g, b, lds, st, a); break;
+        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, false>), g, b, lds, st, a); break;
+        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, false>), g, b, lds, st, a); break;
+        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false>), g, b, lds, st, a); break;
+      }
     }
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
@@ -1388,8 +1498,8 @@ int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int varia
   } else {
     const int grid = 8 * ((device_cu_count() + 7) / 8);
     const size_t lds = tile_lds_bytes(a.E);
-    if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<false, true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
-    else hipLaunchKernelGGL((gemm_tile_kernel<false, false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+    if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+    else hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }
