@@ -73,6 +73,15 @@ MOESQ_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // not wait on the other counters (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
 
+// Workgroup barrier after the caller's own s_waitcnt: the empty asm statements keep the compiler from
+// moving memory accesses across it, and no fence is emitted, so loads still in flight stay in flight (a
+// fence with direct-to-LDS loads outstanding makes the compiler wait for every vector-memory operation).
+MOESQ_DEV void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads and stores issued before it stay in
 // flight (a plain __syncthreads waits for every outstanding memory operation of the wave).
 MOESQ_DEV void lds_barrier() {
@@ -1067,11 +1076,19 @@ struct TWS<MF, MLP, false> {
   WMeta m[MF];
   MOESQ_DEV void load0(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w_half0<MF, MLP>(w, rw, src, lane, ss); }
   MOESQ_DEV void load1(rsrc_t rw, const WSrc& src, int lane, int ss) { load_w_half1<MF, MLP>(w, rw, src, lane, ss); }
+  // the super-step's index words and block scales, from half 0 (before the next B prefetch is issued, so
+  // that waiting for half 0 does not also wait for that prefetch)
+  MOESQ_DEV void meta() {
+#pragma unroll
+    for (int f = 0; f < MF; f++) {
+      m[f] = w_meta(w, f, true);
+      // computed here, not sunk past the prefetch issued next by the scheduler
+      asm volatile("" ::"v"(m[f].i02), "v"(m[f].i13), "v"(f16x2_bits(m[f].s01)), "v"(f16x2_bits(m[f].s23)));
+    }
+  }
   template <int H, int NF, bool XK>
   MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
     if (H == 0) {
-#pragma unroll
-      for (int f = 0; f < MF; f++) m[f] = w_meta(w, f, true);
       lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
       lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
     } else {
@@ -1087,6 +1104,7 @@ struct TWS<MF, MLP, true> {
   DWStage<MF> w;
   MOESQ_DEV void load0(rsrc_t rw, const WSrc& src, int lane, int ss) { load_dw<MF>(w, rw, src.g0, src.j0, lane, ss); }
   MOESQ_DEV void load1(rsrc_t, const WSrc&, int, int) {}
+  MOESQ_DEV void meta() {}
   template <int H, int NF, bool XK>
   MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
     if (H == 0) dense_superstep_lds<MF, NF>(acc, w, Bs, r16, c, nv);
@@ -1094,10 +1112,14 @@ struct TWS<MF, MLP, true> {
 };
 
 // Per-expert tile counts ceil(n_e / kTileTok) -> exclusive prefix tile_pre[0..E] in LDS (E+1
-// entries), each expert's first row off_l[e] and row count ne_l[e] (E entries). part: LDS scratch of
-// THREADS ints.
+// entries), each expert's first row off_l[e] and row count ne_l[e] (E entries), and its epilogue
+// scalars scal_l[3E]: alpha_e of the rows below N/2 [0, E), of the rows from N/2 [E, 2E) (the same
+// unless the weights carry split tensor scales; the MLP's gate and up rows), and gamma_h [2E, 3E) for
+// the MLP. Read once per workgroup here, so that the per-tile work reads LDS, not global memory (a
+// vector load there makes the wave wait for every load in flight, the prefetches included).
+// part: LDS scratch of THREADS ints.
 template <int THREADS>
-MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* off_l, int32_t* ne_l,
+MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* off_l, int32_t* ne_l, float* scal_l,
                                  int32_t* part) {
   constexpr int PER_LANE = THREADS / 64;
   const int tid = threadIdx.x;
@@ -1107,6 +1129,10 @@ MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* 
     expert_rows(a, i, off, ne);
     off_l[i] = off;
     ne_l[i] = max(ne, 0);
+    const float ga = a.gamma_a[i];
+    scal_l[i] = 1.0f / (wscale(a, i, 0) * ga);
+    scal_l[E + i] = 1.0f / (wscale(a, i, 1) * ga);
+    scal_l[2 * E + i] = a.gamma_h ? a.gamma_h[i] : 1.0f;
   }
   __syncthreads();
   const int per = (E + THREADS - 1) / THREADS;
@@ -1153,8 +1179,7 @@ struct TileCtx {
 // XCD that run neighbouring tiles share the activation tile in L2.
 template <int MF, bool MLP, bool XK, bool DENSE>
 MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, const int32_t* ne_l,
-                                int RB, int t,
-                                int w) {
+                                const float* scal_l, int RB, int t, int w) {
   TileCtx<MF> c;
   int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] * RB <= t
   while (lo < hi) {
@@ -1187,7 +1212,7 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, cons
   }
   // alpha_e: the MLP tile's gate and up rows take the two tensor scales, a plain wave its row half's
   const int half = MLP ? 0 : (min(c.rb * 512 + 64 * w, N - 64) >= N / 2);
-  c.alpha = 1.0f / (wscale(a, c.e, half) * a.gamma_a[c.e]);
+  c.alpha = scal_l[half * a.E + c.e];
   if (XK) {
     c.rq = make_rsrc((const uint8_t*)a.xk + (size_t)c.off * K * 2, (uint32_t)c.ne * K * 2);
     c.rs = c.rq;
@@ -1240,7 +1265,8 @@ MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) { stage_p(
 
 // Epilogue of a finished tile.
 template <int MF, int NF, int MLP>
-MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc) {
+MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc,
+                             const float* scal_l) {
   const int N = a.N;
   const float alpha = c.alpha;
   if (!MLP) {
@@ -1289,8 +1315,8 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
     return;
   }
   const int ib = c.rb * 256 + 32 * w;  // first intermediate column of this wave (one 32-block)
-  const float alpha_u = 1.0f / (wscale(a, c.e, 1) * a.gamma_a[c.e]);  // the up rows' alpha_e
-  const float gh = MLP == kEpiCalib ? 1.0f : a.gamma_h[c.e];
+  const float alpha_u = scal_l[a.E + c.e];  // the up rows' alpha_e
+  const float gh = scal_l[2 * a.E + c.e];
   float amx = 0.0f;
 #pragma unroll
   for (int n = 0; n < NF; n++) {
@@ -1322,7 +1348,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   int32_t* tile_pre = (int32_t*)(dyn + 2 * BBYTES);      // [E+1]
   int32_t* off_l = tile_pre + a.E + 1;                   // [E+1]
   int32_t* ne_l = off_l + a.E + 1;                       // [E]
-  build_tile_prefix<kTileThreads>(a, tile_pre, off_l, ne_l, part);
+  float* scal_l = (float*)(ne_l + a.E);                  // [3E]
+  build_tile_prefix<kTileThreads>(a, tile_pre, off_l, ne_l, scal_l, part);
   const int K = a.K, nss = K / 256;
   const int RB = MLP ? a.N / 512 : (a.N + 511) / 512;   // MLP: 256 gate + 256 up rows per tile
   const int T = tile_pre[a.E] * RB;
@@ -1340,7 +1367,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   constexpr bool kMlp = MLP != kEpiPlain;
-  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t, w);
+  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, scal_l, RB, t, w);
   TWS<MF, kMlp, DENSE> wc;
   PStage p;
   wc.load0(cur.rw, cur.src, lane, 0);
@@ -1360,31 +1387,37 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     }
     const bool has_n = t_n < tend;
     TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, scal_l, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
-    if (has_n) issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
+    // The prefetches below are issued on every super-step, the last one too (there they read the current
+    // tile's first super-step again: in range, and never used), so that no branch around them leaves the
+    // compiler's wait bookkeeping unsure of how many loads are in flight.
+    wc.meta();
+    issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
     wc.template half<0, NF, XK>(acc, Bc, r16, cc, cur.nv);
-    if (has_n) wc.load0(nxt.rw, nxt.src, lane, ss_n);  // half 0 of the next super-step, its registers read
+    wc.load0(nxt.rw, nxt.src, lane, ss_n);  // half 0 of the next super-step, its registers read
     wc.template half<1, NF, XK>(acc, Bc, r16, cc, cur.nv);
     const bool tile_end = ss == nss - 1;
     if (tile_end) {
-      tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc);
+      tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc, scal_l);
 #pragma unroll
       for (int f = 0; f < MF; f++)
 #pragma unroll
         for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    if (has_n) wc.load1(nxt.rw, nxt.src, lane, ss_n);
-    if (has_n && !XK) stage_b(p, Bn, ba);
+    wc.load1(nxt.rw, nxt.src, lane, ss_n);
+    if (!XK) stage_b(p, Bn, ba);
     if (XK) {
       // the direct-to-LDS loads of the next step (issued first) must have landed; the kLoads1 weight
       // loads issued last may stay in flight. Loads complete in issue order, so waiting until at most
       // kLoads1 vector-memory operations are outstanding is enough; after an epilogue (stores in flight,
       // which need not complete in order with the loads) everything is waited for.
+      // (The direct-to-LDS data is in LDS once its load is counted complete, and every wave's LDS reads
+      // of the current tile completed before it got here: a bare barrier suffices.)
       if (tile_end || !has_n) __builtin_amdgcn_s_waitcnt(0);
       else __builtin_amdgcn_s_waitcnt(vmcnt_only(TWS<MF, kMlp, DENSE>::kLoads1));
-      __syncthreads();
+      bare_barrier();
     } else {
       lds_barrier();  // epilogue stores may still be in flight
     }
@@ -1396,7 +1429,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   }
 }
 
-static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (2 * (size_t)(E + 1) + (size_t)E) * 4; }
+static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (2 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
 
 static int device_cu_count() {
   static int cus[64] = {0};
