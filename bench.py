@@ -144,23 +144,87 @@ def summarize_pmc(argv):
     for (k, c), (v, n) in write.items():
         if c == "WRITE_SIZE":
             per_kernel.setdefault(k, {})["write_bytes"] = v * 1024.0 * f_write
+    entries = {}
     if wl in ("c4", "c3_mlp"):
         # one moesq_expert_mlp call: its gate_up and down kernels (distinct template instances)
         key = MLP_KEY
+        # the production forms only: the calibration and dump forms (epilogue template argument 3 or 2) run
+        # once at set-up
+        import re
+        side = re.compile(r"gemm_tile_kernel<[23],|gemm_decode_kernel<.*, [23]>$")
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items()
-                    if "gemm_tile_kernel" in k or "gemm_decode_kernel" in k)
+                    if ("gemm_tile_kernel" in k or "gemm_decode_kernel" in k) and not side.search(k))
+        # the prefill gate_up launch alone (the tiled kernel with the MLP epilogue, template argument 1)
+        gu = [d for k, d in per_kernel.items() if "gemm_tile_kernel<1," in k]
+        if gu:
+            entries[GATEUP_KERNEL] = gu[0]["fetch_bytes"] + gu[0]["write_bytes"]
     else:
         key = next((n for n in (FUSED_KERNEL, "gemm_decode_kernel") if any(n in k for k in per_kernel)),
                    "gemm_tile_kernel")
         total = sum(d["fetch_bytes"] + d["write_bytes"] for k, d in per_kernel.items() if key in k)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     t = json.load(open(path)) if os.path.exists(path) else {}
-    t["%s:%s" % (wl, key)] = {"bytes_per_launch": round(total), "src_hash": _src_hash(), "copy_kernel": copy_name,
-                              "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
-                              "kernels": {k: {kk: round(vv) for kk, vv in d.items()} for k, d in per_kernel.items()}}
+    entries[key] = total
+    for kk, tot in entries.items():
+        t["%s:%s" % (wl, kk)] = {"bytes_per_launch": round(tot), "src_hash": _src_hash(), "copy_kernel": copy_name,
+                                 "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
+                                 "kernels": {k: {kv: round(vv) for kv, vv in d.items()} for k, d in per_kernel.items()}}
     with open(path, "w") as f:
         json.dump(t, f, indent=1, sort_keys=True)
     print(json.dumps(t["%s:%s" % (wl, key)]))
+
+
+# MI355X: 8 XCDs x 32 CUs x 4 SIMDs
+N_XCD, N_SIMD = 8, 1024
+
+
+def summarize_sq(paths):
+    """--summarize-sq CSV [CSV ...]: per-dispatch means of the SQ / GRBM counters of the GEMM kernels in
+    rocprofv3 counter CSVs (one pass per file), with derived ratios, as a markdown table."""
+    import csv
+    acc, dur = {}, {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"].split("(")[0]
+                if "gemm_" not in k:
+                    continue
+                acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                dur.setdefault(k, {})[(p, r["Correlation_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    for k, cs in acc.items():
+        m = {c: float(np.mean(v)) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        t = float(np.mean(list(dur[k].values())))
+        print("\n`%s` (%d dispatches per pass, mean duration %.1f us under the profiler)\n" % (k, n, t * 1e6))
+        print("| counter | mean per dispatch |\n|---|---|")
+        for c in sorted(m):
+            print("| %s | %.4g |" % (c, m[c]))
+        gui = m.get("GRBM_GUI_ACTIVE")
+        rows = []
+        if gui:
+            rows.append(("GRBM_GUI_ACTIVE / %d XCDs / duration (clock the GUI counter ran at)" % N_XCD,
+                         "%.2f GHz" % (gui / N_XCD / t / 1e9)))
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                rows.append(("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x GUI cycles per XCD)" % N_SIMD,
+                             "%.3f" % (m["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * gui / N_XCD))))
+        if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
+            rows.append(("SQ_INSTS_VALU / SQ_INSTS_MFMA (VALU count includes the MFMAs)",
+                         "%.2f" % (m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"])))
+        if "SQ_INSTS_LDS" in m and "SQ_INSTS_MFMA" in m:
+            rows.append(("SQ_INSTS_LDS / SQ_INSTS_MFMA", "%.2f" % (m["SQ_INSTS_LDS"] / m["SQ_INSTS_MFMA"])))
+        if "SQ_INSTS_SALU" in m and "SQ_INSTS_MFMA" in m:
+            rows.append(("SQ_INSTS_SALU / SQ_INSTS_MFMA", "%.2f" % (m["SQ_INSTS_SALU"] / m["SQ_INSTS_MFMA"])))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            rows.append(("SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES",
+                         "%.3f" % (m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"])))
+        for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU"):
+            if c in m and "SQ_WAVE_CYCLES" in m:
+                scale = 1.0 if c.startswith("SQ_WAIT") else 0.25  # wait counters and wave cycles in quad-cycles
+                rows.append(("%s / SQ_WAVE_CYCLES" % c, "%.3f" % (scale * m[c] / m["SQ_WAVE_CYCLES"])))
+        if rows:
+            print("\n| derived | value |\n|---|---|")
+            for a, b in rows:
+                print("| %s | %s |" % (a, b))
 
 
 def _traffic(kernel_key):
@@ -691,9 +755,14 @@ def main(argv=None):
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                          "COPY_WRITE_CSV"),
                     help="host only: write profiles/traffic.json from rocprofv3 counter CSVs")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="CSV",
+                    help="host only: SQ / GRBM counter table of the GEMM kernels from rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
