@@ -1111,16 +1111,18 @@ struct TWS<MF, MLP, true> {
   }
 };
 
-// Per-expert tile counts ceil(n_e / kTileTok) -> exclusive prefix tile_pre[0..E] in LDS (E+1
-// entries), each expert's first row off_l[e] and row count ne_l[e] (E entries), and its epilogue
-// scalars scal_l[3E]: alpha_e of the rows below N/2 [0, E), of the rows from N/2 [E, 2E) (the same
-// unless the weights carry split tensor scales; the MLP's gate and up rows), and gamma_h [2E, 3E) for
-// the MLP. Read once per workgroup here, so that the per-tile work reads LDS, not global memory (a
+// The tile list in LDS: the full token tiles first (exclusive prefix full_pre[0..E] of the per-expert
+// counts floor(n_e / kTileTok), E+1 entries), then the experts' partial last tiles, largest first
+// (plist[0..P): the experts ordered by the partial tile's 16-token fragment count, descending, then by
+// expert; plist[E] = P). Also each expert's first row off_l[e] and row count ne_l[e] (E entries), and its
+// epilogue scalars scal_l[3E]: alpha_e of the rows below N/2 [0, E), of the rows from N/2 [E, 2E) (the
+// same unless the weights carry split tensor scales; the MLP's gate and up rows), and gamma_h [2E, 3E)
+// for the MLP. Read once per workgroup here, so that the per-tile work reads LDS, not global memory (a
 // vector load there makes the wave wait for every load in flight, the prefetches included).
 // part: LDS scratch of THREADS ints.
 template <int THREADS>
-MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* off_l, int32_t* ne_l, float* scal_l,
-                                 int32_t* part) {
+MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* full_pre, int32_t* off_l, int32_t* ne_l, float* scal_l,
+                                 int32_t* plist, int32_t* part) {
   constexpr int PER_LANE = THREADS / 64;
   const int tid = threadIdx.x;
   const int E = a.E;
@@ -1138,8 +1140,24 @@ MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* 
   const int per = (E + THREADS - 1) / THREADS;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
   int sum = 0;
-  for (int e = lo; e < hi; e++) sum += (ne_l[e] + kTileTok - 1) / kTileTok;
+  for (int e = lo; e < hi; e++) sum += ne_l[e] / kTileTok;
   part[tid] = sum;
+  if (tid >= THREADS - 64) {
+    // the last wave lists the partial tiles: one ballot per 64 experts and fragment count
+    const int lane = tid & 63;
+    int base = 0;
+    for (int b = kTileTok / 16; b >= 1; b--) {
+      for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int r = e < E ? ne_l[e] % kTileTok : 0;
+        const bool m = r > 0 && (r + 15) / 16 == b;
+        const uint64_t bal = __ballot(m);
+        if (m) plist[base + __popcll(bal & ((1ull << lane) - 1ull))] = e;
+        base += __popcll(bal);
+      }
+    }
+    if (lane == 0) plist[E] = base;
+  }
   __syncthreads();
   if (tid < 64) {  // wave 0 scans the partial sums (PER_LANE per lane)
     int v[PER_LANE], s = 0;
@@ -1158,10 +1176,10 @@ MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* tile_pre, int32_t* 
   __syncthreads();
   int run = part[tid];
   for (int e = lo; e < hi; e++) {
-    tile_pre[e] = run;
-    run += (ne_l[e] + kTileTok - 1) / kTileTok;
+    full_pre[e] = run;
+    run += ne_l[e] / kTileTok;
   }
-  if (hi == E && lo < hi) tile_pre[E] = run;
+  if (hi == E && lo < hi) full_pre[E] = run;
   __syncthreads();
 }
 
@@ -1175,21 +1193,30 @@ struct TileCtx {
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
 };
 
-// Tile t of the list ordered expert -> token tile -> row block (row block fastest): workgroups of one
-// XCD that run neighbouring tiles share the activation tile in L2.
+// Tile t of the list: the full token tiles ordered expert -> token tile -> row block (row block
+// fastest: workgroups of one XCD that run neighbouring tiles share the activation tile in L2), then the
+// partial last tiles in plist order, each with its RB row blocks.
 template <int MF, bool MLP, bool XK, bool DENSE>
-MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* tile_pre, const int32_t* off_l, const int32_t* ne_l,
-                                const float* scal_l, int RB, int t, int w) {
+MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* full_pre, const int32_t* off_l, const int32_t* ne_l,
+                                const float* scal_l, const int32_t* plist, int RB, int t, int w) {
   TileCtx<MF> c;
-  int lo = 0, hi = a.E - 1;  // largest e with tile_pre[e] * RB <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_pre[mid] * RB <= t) lo = mid; else hi = mid - 1;
+  const int TA = __builtin_amdgcn_readfirstlane(full_pre[a.E]) * RB;
+  if (t < TA) {
+    int lo = 0, hi = a.E - 1;  // largest e with full_pre[e] * RB <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (full_pre[mid] * RB <= t) lo = mid; else hi = mid - 1;
+    }
+    c.e = __builtin_amdgcn_readfirstlane(lo);
+    const int local = t - __builtin_amdgcn_readfirstlane(full_pre[c.e]) * RB;
+    c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kTileTok);
+    c.rb = __builtin_amdgcn_readfirstlane(local % RB);
+  } else {
+    const int u = t - TA;
+    c.e = __builtin_amdgcn_readfirstlane(plist[u / RB]);
+    c.tb = __builtin_amdgcn_readfirstlane((ne_l[c.e] / kTileTok) * kTileTok);
+    c.rb = __builtin_amdgcn_readfirstlane(u % RB);
   }
-  c.e = __builtin_amdgcn_readfirstlane(lo);
-  const int local = t - __builtin_amdgcn_readfirstlane(tile_pre[c.e]) * RB;
-  c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kTileTok);
-  c.rb = __builtin_amdgcn_readfirstlane(local % RB);
   c.off = __builtin_amdgcn_readfirstlane(off_l[c.e]);
   c.ne = __builtin_amdgcn_readfirstlane(ne_l[c.e]);
   c.nv = min(kTileNF, (c.ne - c.tb + 15) / 16);
@@ -1328,9 +1355,9 @@ MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&ac
   if (MLP == kEpiCalib) calib_amax_commit(a.amax_h, c.e, amx);
 }
 
-// Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the
-// workgroups of XCD x (blockIdx % 8 == x) take the x-th contiguous eighth of the tile list, slot j
-// handling tiles start + j, + J, ... The super-steps of all the workgroup's tiles form one
+// Persistent tiled kernel, one 8-wave workgroup per CU. The grid holds 8*J workgroups; the tile list
+// (full token tiles, then the partial ones, largest first) is dealt to the XCDs in groups of J
+// consecutive tiles, slot j of XCD x handling tiles x J + j, + 8 J, ... The super-steps of all the workgroup's tiles form one
 // pipeline: while step i computes, the activations (LDS) of step i+1 -- possibly the first step of
 // the next tile -- are in flight, and its weights are loaded into the one register stage as soon as
 // step i's MFMAs have read it; one barrier per step. (One weight stage measured as fast as two; the
@@ -1345,18 +1372,21 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t* Bs0 = dyn;                                    // two activation tiles
   uint8_t* Bs1 = dyn + BBYTES;
-  int32_t* tile_pre = (int32_t*)(dyn + 2 * BBYTES);      // [E+1]
-  int32_t* off_l = tile_pre + a.E + 1;                   // [E+1]
+  int32_t* full_pre = (int32_t*)(dyn + 2 * BBYTES);      // [E+1]
+  int32_t* off_l = full_pre + a.E + 1;                   // [E+1]
   int32_t* ne_l = off_l + a.E + 1;                       // [E]
   float* scal_l = (float*)(ne_l + a.E);                  // [3E]
-  build_tile_prefix<kTileThreads>(a, tile_pre, off_l, ne_l, scal_l, part);
+  int32_t* plist = (int32_t*)(scal_l + 3 * a.E);         // [E+1]
+  build_tile_prefix<kTileThreads>(a, full_pre, off_l, ne_l, scal_l, plist, part);
   const int K = a.K, nss = K / 256;
   const int RB = MLP ? a.N / 512 : (a.N + 511) / 512;   // MLP: 256 gate + 256 up rows per tile
-  const int T = tile_pre[a.E] * RB;
+  const int T = (full_pre[a.E] + plist[a.E]) * RB;
+  // groups of J consecutive tiles are dealt to the 8 XCDs in turn (workgroup x + 8 j runs on XCD x):
+  // slot j of XCD x takes tiles (8 k + x) J + j, k = 0, 1, ... Neighbouring tiles still run side by side
+  // on one XCD, and every XCD gets a share of the full tiles and of the cheaper partial tiles at the end.
   const int J = gridDim.x >> 3, x = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int chunk = (T + 7) / 8;
-  const int tend = min(T, (x + 1) * chunk);
-  int t = x * chunk + j;
+  const int tend = T;
+  int t = x * J + j;
   if (t >= tend) return;
   const BAddr ba = make_baddr(w, lane);
 
@@ -1367,7 +1397,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   constexpr bool kMlp = MLP != kEpiPlain;
-  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, scal_l, RB, t, w);
+  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, RB, t, w);
   TWS<MF, kMlp, DENSE> wc;
   PStage p;
   wc.load0(cur.rw, cur.src, lane, 0);
@@ -1383,11 +1413,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     int ss_n = ss + 1, t_n = t;
     if (ss_n == nss) {
       ss_n = 0;
-      t_n = t + J;
+      t_n = t + 8 * J;
     }
     const bool has_n = t_n < tend;
     TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, tile_pre, off_l, ne_l, scal_l, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     // The prefetches below are issued on every super-step, the last one too (there they read the current
@@ -1429,7 +1459,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   }
 }
 
-static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (2 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
+static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (3 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
 
 static int device_cu_count() {
   static int cus[64] = {0};
