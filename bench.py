@@ -486,7 +486,7 @@ def cpu_baseline(wl, orc, gen, max_reps=3):
 
 # rows of the expert sample per workload kind: the Kimi decode workloads route 1-2 rows to an expert,
 # the prefill MLP a few hundred
-CPU_SAMPLE = {"pair": (16, 64), "mlp_decode": (16, 64), "mlp": (8, 512)}   # (max experts, max rows)
+CPU_SAMPLE = {"pair": (16, 64), "mlp_decode": (16, 64), "mlp": (16, 2048)}   # (max experts, max rows)
 
 
 def _sub_weights(gen, orc, cfg, proj, N, K, experts):
