@@ -29,8 +29,9 @@ class Config:
     K2: int = 0
     mlp: bool = False      # gate_up -> SiLU(gate)*up -> requant -> down -> combine
     x_bf16: bool = False   # tokens handed over in bf16 (else fp32)
-    gamma_h: float = 0.0   # static tensor scale of the intermediate h (MLP only): 448 / (amax_h / 6) for a
-                           # calibrated amax_h (t_mlp: 2.0, c4: 64.0)
+    gamma_h: float = 0.0   # one hand-set tensor scale of the intermediate h (MLP only), 448 / (amax_h / 6)
+                           # for amax_h = 2.0 (t_mlp) or 64.0 (c4, c3_mlp); the Kimi workloads' per-expert
+                           # scales come from calibration (Eq. 5 of each expert's amax of h)
     desc: str = ""
 
     @property
@@ -49,8 +50,7 @@ CONFIGS = {
                  N2=7168, K2=2048, desc="Kimi-K2.5 gate_up + down, decode"),
     "c4": Config("c4", E=384, K=7168, N=4096, T=8192, k=8, routing="zipf", act_dist="student_t", seed=1238,
                  N2=7168, K2=2048, mlp=True, gamma_h=42.0, desc="Kimi-K2.5 routed-expert MLP, prefill"),
-    # the decode-size routed-expert MLP on the c3 shapes, bf16 tokens in and out (gamma_h: the c4
-    # calibration, same weight and token distributions)
+    # the decode-size routed-expert MLP on the c3 shapes, bf16 tokens in and out
     "c3_mlp": Config("c3_mlp", E=384, K=7168, N=4096, T=64, k=8, routing="uniform", act_dist="student_t",
                      seed=1239, N2=7168, K2=2048, mlp=True, gamma_h=42.0, x_bf16=True,
                      desc="Kimi-K2.5 routed-expert MLP, decode"),
