@@ -43,6 +43,9 @@ double orc_e2m1_decode(uint8_t code) {
 // the sign bit is set only for a nonzero magnitude, so -0 is never produced.
 uint8_t orc_e2m1_encode(float r) {
   double a = fabs((double)r);
+  // beyond 6 the nearest grid point is 6; clamping first keeps the distances below exact even where
+  // a - 4 and a - 6 would round to the same double (|r| past about 2^54)
+  if (a > 6.0) a = 6.0;
   int best = 0;
   double bestd = INFINITY;
   for (int c = 0; c < 8; c++) {

@@ -60,6 +60,15 @@ def test_e2m1_ties_follow_stated_reading(orc):
         assert orc.e2m1_encode(float(v)) == int(code), v
 
 
+def test_e2m1_saturates_for_any_magnitude(orc):
+    # every magnitude past 5 is nearest to 6 (code 7), however large, also where the distances to 4 and
+    # to 6 are not separable in double precision; NaN encodes to 0 (no comparison holds)
+    for x in (5.0000005, 6.0, 7.0, 1e10, 2.0 ** 54, 2.0 ** 60, 1e30, 3.4e38, float("inf")):
+        assert orc.e2m1_encode(x) == 7, x
+        assert orc.e2m1_encode(-x) == 15, x
+    assert orc.e2m1_encode(float("nan")) == 0
+
+
 def test_e2m1_idempotent_and_monotone(orc):
     for c in range(16):
         want = 0 if c == 8 else c
