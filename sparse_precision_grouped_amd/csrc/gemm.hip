@@ -443,7 +443,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
     for (int r = 0; r < 4; r++) {
       const float g = gg[f][r] * alpha;
       const float u = uu[f][r] * alpha_u;
-      h[4 * f + r] = g / (1.0f + __expf(-g)) * u;
+      h[4 * f + r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;  // SiLU(g) u (fast exp and reciprocal)
     }
     if (EPI == kEpiMlpDump && tv && a.dump) {
       const int64_t rowo = p * N;
@@ -472,12 +472,34 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
   if (tv) {
     f16x2 s01, s01b;
     e4m3_pair_f16x2(sc, s01, s01b);
+    // E2M1(h / sv) with h / sv the correctly rounded fp32 quotient, as the quantizer defines it, but
+    // without a full division per element: with r = RN(1/sv), q0 = RN(h r), e = h - sv q0 (exact by
+    // fma) and q = RN(q0 + e r) is RN(h / sv) (Markstein) unless h is so small that e underflows,
+    // i.e. |h / sv| < 2^-90, where every such quotient encodes to 0 anyway. The hardware FP4 convert
+    // rounds to nearest, ties to the even code, and saturates at 6, as E2M1 does; it returns -0 (code
+    // 8) where E2M1 gives +0, which the mask below clears. A block with a huge or non-finite amax takes
+    // the plain division and encoder.
+    const float r = sv != 0.0f ? 1.0f / sv : 0.0f;
+    const bool fast = am * r < 1e30f;
 #pragma unroll
     for (int f = 0; f < 2; f++) {
       uint32_t codes = 0u;
       if (sv != 0.0f) {
+        if (fast) {
+          float q[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) codes |= e2m1_encode(h[4 * f + r] / sv) << (4 * r);
+          for (int i = 0; i < 4; i++) {
+            const float x = h[4 * f + i];
+            const float q0 = x * r;
+            q[i] = __builtin_fmaf(__builtin_fmaf(-sv, q0, x), r, q0);
+          }
+          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, q[2], q[3], 1.0f, 1) & 0xFFFFu;
+          codes &= (((codes & 0x7777u) + 0x7777u) & 0x8888u) | 0x7777u;  // -0 -> +0
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i++) codes |= e2m1_encode(h[4 * f + i] / sv) << (4 * i);
+        }
       }
       const int i0 = ib + 16 * f + 4 * cc;  // 4 consecutive intermediate columns: half (cc & 1) of an 8-group
       *(uint16_t*)(a.h_q + p * (I / 2) + i0 / 2) = (uint16_t)codes;

@@ -932,6 +932,38 @@ def test_mlp_token_count_boundaries(kernel):
 
 
 @pytest.mark.parametrize("kernel", ["streaming", "tiled"])
+def test_requant_extreme_intermediate_scales(kernel):
+    """The requantization of h with intermediate scales far outside the calibrated range: expert 0's
+    gamma_h = 1e33 (every block scale saturates at 448 and h / s reaches ~1e30: the epilogue's
+    plain-division path), expert 1's 1e-38 (every block scale encodes to 0, so do the codes), the rest
+    calibrated. Codes, block scales and the f16 copy against the oracle's quantizer on the kernel's own
+    fp32 h, byte for byte, in both kernel families."""
+    cfg = gen.CONFIGS["t_mlp"]
+    say("requant extreme gamma_h", kernel)
+    kf = mq.F_FORCE_DECODE if kernel == "streaming" else mq.F_FORCE_PREFILL
+    E, H, I2, I, T, k = cfg.E, cfg.K, cfg.N, cfg.N // 2, cfg.T, cfg.k
+    w13 = np.stack([gen.weights_expert(cfg, 0, e, I2, H) for e in range(E)])
+    w2 = np.stack([gen.weights_expert(cfg, 1, e, H, I) for e in range(E)])
+    W13, W2 = mq.moesq_compress_weights(dev(w13)), mq.moesq_compress_weights(dev(w2))
+    x = gen.activations(cfg, 0, T, H)
+    ids, _ = gen.routing(cfg)
+    R = orc.route(ids, E)
+    off = R["offsets"]
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], k, off, ga)
+    gh = oracle_gamma_h(orc.compress(w13), qo, so, ga, off)
+    gh[0], gh[1] = np.float32(1e33), np.float32(1e-38)
+    rows = int(off[-1])
+    assert off[1] > off[0] and off[2] > off[1]
+    y, ws = mq.moesq_expert_mlp(W13, W2, dev(qo), dev(so), dev(ga), dev(gh), dev(off), y_dtype=torch.float32,
+                                flags=mq.F_DUMP_GATEUP | mq.F_DUMP_H | kf)
+    requant_gate(ws, rows, I, gh, np.arange(rows), orc.expert_of_rows(off, np.arange(rows)))
+    hq, hs, _ = mq.mlp_workspace_views(ws, rows, I, dump=True)
+    assert np.all(host(hs)[:off[1]] == 0x7E)                       # saturated block scales
+    assert not np.any(host(hs)[off[1]:off[2]]) and not np.any(host(hq)[off[1]:off[2]])  # zero scales, zero codes
+
+
+@pytest.mark.parametrize("kernel", ["streaming", "tiled"])
 def test_split_tensor_scales(kernel):
     """Gate and up kept as separate linears, each with its own Eq. 5 tensor scale (the model card's
     checkpoint): device compression of the [2E, N/2, K] view against the oracle's compress_split
