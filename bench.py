@@ -75,7 +75,7 @@ GATEUP_KERNEL = "gemm_tile_kernel<MLP> (gate_up + SwiGLU + requant)"
 def fused_eligible(cfg):
     """The library's one-launch condition for moesq_route_quantize_gemm."""
     rows = cfg.T * cfg.k
-    return not cfg.mlp and not cfg.N2 and rows <= 1024 and 8 * rows <= cfg.E and cfg.K <= 2048
+    return not cfg.mlp and not cfg.N2 and rows <= 1024 and 2 * rows <= cfg.E and cfg.K <= 2048
 
 
 def _src_hash():

@@ -211,7 +211,7 @@ int moesq_route_quantize_dyn(void *stream, const int32_t *topk_ids, int64_t T, i
  * moesq_route_quantize(topk_ids, T, k, E, x, ..., gamma = gamma_a, ...) followed by
  * moesq_grouped_gemm(W, q, s, xk, gamma_a, offsets, rows = T*k, y, y_dtype, flags = 0). Every output
  * (counts, offsets, sorted_slot, slot_pos, q, s, xk, y, *dev_status) is byte-identical to that pair of
- * calls. For the smallest decode batches (8 T*k <= E, K <= 2048) it is one kernel launch: each
+ * calls. For the smallest decode batches (2 T*k <= E, K <= 2048) it is one kernel launch: each
  * weight-streaming workgroup ranks the ids of its expert and quantizes that expert's tokens itself, so
  * no dispatch kernel runs before the GEMM; otherwise it enqueues the two calls (pass xk for the faster
  * weight-streaming GEMM there).

@@ -56,6 +56,29 @@ MOESQ_DEV float global_scale_from_amax(float amax) {
   return 448.0f / t;
 }
 
+// E2M1 codes of the correctly rounded quotients x[i] / s (element i in nibble i), given r = RN(1/s),
+// with no full division per element: q0 = RN(x r), e = x - s q0 (exact by fma), RN(q0 + e r) is
+// RN(x / s) (Markstein) unless e underflows, which needs |x / s| < 2^-90, where every quotient encodes
+// to 0 anyway. The hardware FP4 convert rounds to nearest, ties to the even code, and saturates at 6,
+// as E2M1 does (checked on every fp32 value in [-8, 8]), except that it gives -0 (code 8) where E2M1
+// gives +0: the last mask clears those sign bits. The caller keeps |x r| far below the fp32 range.
+MOESQ_DEV float quot_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-s, q0, x), r, q0);
+}
+MOESQ_DEV uint32_t e2m1_codes4(float x0, float x1, float x2, float x3, float s, float r) {
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot_rn(x0, s, r), quot_rn(x1, s, r), 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, quot_rn(x2, s, r), quot_rn(x3, s, r), 1.0f, 1) & 0xFFFFu;
+  return c & ((((c & 0x7777u) + 0x7777u) & 0x8888u) | 0x7777u);
+}
+MOESQ_DEV uint32_t e2m1_codes8(const float x[8], float s, float r) {
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, quot_rn(x[0], s, r), quot_rn(x[1], s, r), 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, quot_rn(x[2], s, r), quot_rn(x[3], s, r), 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, quot_rn(x[4], s, r), quot_rn(x[5], s, r), 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, quot_rn(x[6], s, r), quot_rn(x[7], s, r), 1.0f, 3);
+  return c & ((((c & 0x77777777u) + 0x77777777u) & 0x88888888u) | 0x77777777u);
+}
+
 // Quantize 8 consecutive values held by one lane; four consecutive lanes (lane % 4 = 0..3) form one
 // 32-element block. Returns the 8 E2M1 codes (element i in nibble i) and the block's UE4M3 code.
 // Eq. 5 order in fp32: t = gamma*amax; u = t/6; code = E4M3(u); s = value(code)/gamma; q = E2M1(x/s).
@@ -71,8 +94,13 @@ MOESQ_DEV void quant8_block4(const float v[8], float gamma, uint32_t& codes, uin
   const float s = e4m3_value(scode) / gamma;
   codes = 0u;
   if (s != 0.0f) {
+    const float r = 1.0f / s;
+    if (am * r < 1e30f) {
+      codes = e2m1_codes8(v, s, r);
+    } else {  // a huge or non-finite block: the plain division and encoder
 #pragma unroll
-    for (int i = 0; i < 8; i++) codes |= e2m1_encode(v[i] / s) << (4 * i);
+      for (int i = 0; i < 8; i++) codes |= e2m1_encode(v[i] / s) << (4 * i);
+    }
   }
 }
 

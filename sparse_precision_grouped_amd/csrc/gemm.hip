@@ -472,13 +472,8 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
   if (tv) {
     f16x2 s01, s01b;
     e4m3_pair_f16x2(sc, s01, s01b);
-    // E2M1(h / sv) with h / sv the correctly rounded fp32 quotient, as the quantizer defines it, but
-    // without a full division per element: with r = RN(1/sv), q0 = RN(h r), e = h - sv q0 (exact by
-    // fma) and q = RN(q0 + e r) is RN(h / sv) (Markstein) unless h is so small that e underflows,
-    // i.e. |h / sv| < 2^-90, where every such quotient encodes to 0 anyway. The hardware FP4 convert
-    // rounds to nearest, ties to the even code, and saturates at 6, as E2M1 does; it returns -0 (code
-    // 8) where E2M1 gives +0, which the mask below clears. A block with a huge or non-finite amax takes
-    // the plain division and encoder.
+    // E2M1(h / sv) of the correctly rounded quotients (e2m1_codes4); a block with a huge or non-finite
+    // amax takes the plain division and encoder
     const float r = sv != 0.0f ? 1.0f / sv : 0.0f;
     const bool fast = am * r < 1e30f;
 #pragma unroll
@@ -486,16 +481,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
       uint32_t codes = 0u;
       if (sv != 0.0f) {
         if (fast) {
-          float q[4];
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float x = h[4 * f + i];
-            const float q0 = x * r;
-            q[i] = __builtin_fmaf(__builtin_fmaf(-sv, q0, x), r, q0);
-          }
-          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
-          codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, q[2], q[3], 1.0f, 1) & 0xFFFFu;
-          codes &= (((codes & 0x7777u) + 0x7777u) & 0x8888u) | 0x7777u;  // -0 -> +0
+          codes = e2m1_codes4(h[4 * f], h[4 * f + 1], h[4 * f + 2], h[4 * f + 3], sv, r);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; i++) codes |= e2m1_encode(h[4 * f + i] / sv) << (4 * i);
@@ -890,7 +876,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // T*k = 8, equal at T*k = 32, 34.8 vs 29.2 us at T*k = 128).
 bool dispatch_gemm_fused(int64_t T, int32_t k, int32_t E, int32_t K) {
   const int64_t n = T * k;
-  return T > 0 && n <= kDispMaxSlots && 8 * n <= (int64_t)E && K <= kDispMaxK && E <= kMaxExpertsRoute;
+  return T > 0 && n <= kDispMaxSlots && 2 * n <= (int64_t)E && K <= kDispMaxK && E <= kMaxExpertsRoute;
 }
 
 int launch_dispatch_gemm(hipStream_t st, const GemmArgs& a, const int32_t* ids, int64_t T, int32_t k, const void* x,

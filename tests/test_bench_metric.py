@@ -54,6 +54,8 @@ def test_fused_eligibility_matches_the_library_limits():
     import gen
     import dataclasses
     assert bench.fused_eligible(dataclasses.replace(gen.CONFIGS["c1"], T=2))   # 16 rows, E = 128
+    assert bench.fused_eligible(dataclasses.replace(gen.CONFIGS["c1"], T=8))   # 64 rows: 2 T*k = E
+    assert not bench.fused_eligible(dataclasses.replace(gen.CONFIGS["c1"], T=9))
     assert not bench.fused_eligible(gen.CONFIGS["c1"])       # 128 rows: two launches are faster
     assert not bench.fused_eligible(gen.CONFIGS["c2"])       # prefill
     assert not bench.fused_eligible(gen.CONFIGS["c3"])       # two projections, K = 7168

@@ -691,7 +691,7 @@ def test_route_quantize_gemm_parity(name, T):
 
 def test_route_quantize_gemm_edges():
     """Multi-pass experts (more tokens than one LDS pass holds), bf16 input, split tensor scales,
-    invalid ids, the one-launch limits (8 T*k = E, K = 2048) and one past each (two calls), and the
+    invalid ids, the one-launch limits (2 T*k = E, K = 2048) and one past each (two calls), and the
     smallest K."""
     rng = np.random.default_rng(23)
 
@@ -718,11 +718,11 @@ def test_route_quantize_gemm_edges():
     case(2, 4, 64, 256, 2048, bf16=True)
     case(2, 8, 128, 256, 256, split=True)
     case(3, 3, 80, 64, 256, bad=True)             # ids outside [0, E)
-    case(12, 1, 96, 64, 2048)                     # 8 T*k = E: one launch
-    case(13, 1, 96, 64, 2048)                     # one token more: two calls
+    case(48, 1, 96, 64, 2048)                     # 2 T*k = E: one launch
+    case(49, 1, 96, 64, 2048)                     # one token more: two calls
     case(16, 8, 128, 64, 2048)                    # the decode benchmark's batch shape: two calls
     case(17, 4, 4, 64, 256)                       # T*k > 16 E: two calls, tiled GEMM
-    case(8, 2, 16, 64, 2304)                     # K > 2048: two calls
+    case(2, 4, 64, 64, 2304)                     # 2 T*k <= E but K > 2048: two calls
 
 
 def test_empty_batch_one_call_and_dynamic_scale():
