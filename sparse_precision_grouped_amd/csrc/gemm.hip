@@ -1468,6 +1468,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
 }
 
 static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (3 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
+// the tile tables of the largest expert count the GEMM calls accept fit one workgroup's 160 KiB of LDS
+static_assert(2 * kBTileBytes + (3 * (kMaxExpertsGemm + 1) + 4 * kMaxExpertsGemm) * 4 + kTileThreads * 4 <= 160 * 1024,
+              "tile tables for kMaxExpertsGemm experts exceed the LDS");
 
 static int device_cu_count() {
   static int cus[64] = {0};
