@@ -872,8 +872,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
 // One launch only where it is faster than the two: every workgroup of an expert repeats the
 // quantization of that expert's tokens, which outweighs the saved launch once the batch has more
-// than about one token per eight experts (measured at E = 128, K = 2048, N = 1536: 11.9 vs 14.3 us at
-// T*k = 8, equal at T*k = 32, 34.8 vs 29.2 us at T*k = 128).
+// than about one routed row per two experts (measured at E = 128, K = 2048, N = 1536, top-8:
+// 16.6 vs 17.7 us at T*k = 32, 22.0 vs 22.6 us at T*k = 64, 30.6 vs 27.7 us at T*k = 128).
 bool dispatch_gemm_fused(int64_t T, int32_t k, int32_t E, int32_t K) {
   const int64_t n = T * k;
   return T > 0 && n <= kDispMaxSlots && 2 * n <= (int64_t)E && K <= kDispMaxK && E <= kMaxExpertsRoute;
