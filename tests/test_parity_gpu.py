@@ -299,6 +299,12 @@ def test_quantize_plain_and_bf16_and_zero():
     q2, s2 = mq.moesq_quantize_act(xb.to(DEV), dev(np.array([g], np.float32)))
     qo2, so2 = orc.quantize_rows(xb.to(torch.float32).numpy(), g)
     assert np.array_equal(host(q2), qo2) and np.array_equal(host(s2), so2)
+    # tensor scales far outside the data's range: 1e33 saturates every block scale at 448 and puts the
+    # quotients near 1e30 (the quantizer's plain-division path), 1e-38 makes every scale and code 0
+    for gx in (1e33, 1e-38):
+        q3, s3 = mq.moesq_quantize_act(dev(x), dev(np.array([gx], np.float32)))
+        qo3, so3 = orc.quantize_rows(x, np.float32(gx))
+        assert np.array_equal(host(q3), qo3) and np.array_equal(host(s3), so3), gx
 
 
 def _route_quantize_check(ids, x, E, ga, xk=False, bf16=False):
