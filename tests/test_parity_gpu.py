@@ -637,6 +637,30 @@ def test_grouped_gemm_token_count_boundaries(flags):
             assert orc.rel_frobenius(host(y)[off[e]:off[e + 1]], ref[off[e]:off[e + 1]]) <= GEMM_TOL, e
 
 
+@pytest.mark.parametrize("flags", ["decode", "decode_xk", "prefill", "prefill_xk"])
+def test_grouped_gemm_smallest_shapes(flags):
+    """The smallest weight shapes the kernels take: N = 64 (one 64-row group: a single fragment group of
+    the streaming kernel, one wave's rows of a 512-row tile) and K = 256 (one super-step), with a single
+    expert (E = 1, three token tiles) and with an empty expert next to a 129-token one."""
+    say("gemm smallest shapes", flags)
+    rng = np.random.default_rng(123)
+    fl = mq.F_FORCE_DECODE if flags.startswith("decode") else mq.F_FORCE_PREFILL
+    for counts in (np.array([300]), np.array([0, 129])):
+        E, N, K = counts.size, 64, 256
+        w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+        Wo, Wd = orc.compress(w), mq.moesq_compress_weights(dev(w))
+        rows = int(counts.sum())
+        ids = np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)
+        R = orc.route(ids, E)
+        x = gen.student_t(91, gen.act_stream(E), rows * K).reshape(rows, K)
+        ga = np.full(E, orc.global_scale_of(x), np.float32)
+        qo, so = orc.dispatch_quantize(x, R["sorted_slot"], 1, R["offsets"], ga)
+        xk = dev(_xk_reference(qo, so)) if flags.endswith("_xk") else None
+        y = mq.moesq_grouped_gemm(Wd, dev(qo), dev(so), dev(ga), dev(R["offsets"]), y_dtype=torch.float32, flags=fl,
+                                  xk=xk)
+        gemm_gate(host(y), orc.grouped_gemm(Wo, qo, so, ga, R["offsets"]), "gemm E=%d N=64 K=256 %s" % (E, flags))
+
+
 # ------------------------------------------------- dispatch + GEMM in one call --------------
 def _rqg_check(ids, x, E, ga, Wd, Wo=None, bf16=False, y_dtype=torch.float32, oracle_rows=None):
     """moesq_route_quantize_gemm byte for byte against moesq_route_quantize + moesq_grouped_gemm (the
