@@ -815,18 +815,46 @@ def test_route_quantize_gemm_graph_replays(T):
 
 
 # ---------------------------------------------------------------- combine --------------------
+COMBINE_CASES = [
+    # (T, k, H, E, drop): drop marks copies that have no row (slot_pos = -1: an invalid id, or a slot
+    # over the capacity), which the combine skips
+    (50, 4, 512, 9, "none"),
+    (37, 10, 7168, 13, "some"),   # two groups of 8 copies, the second partial; the Kimi hidden size
+    (19, 8, 1032, 11, "groups"),  # a token with no row at all; 129 threads per token (a partial block)
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_CASES, ids=["k4", "k10_drops", "k8_empty_tokens"])
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
-def test_combine_parity(ydt):
-    say("combine", ydt)
-    T, k, H, E = 50, 4, 512, 9
+def test_combine_parity(ydt, case):
+    T, k, H, E, drop = case
+    say("combine", ydt, case)
     ids, w = gen.route_uniform(11, T, E, k)
     R = orc.route(ids, E)
+    sp = R["slot_pos"].reshape(T, k).copy()
+    if drop == "some":
+        sp[::3, 1] = -1          # dropped copies inside the first group of 8
+        sp[5, :] = -1            # a token with no row
+        sp[7, 8:] = -1           # the partial second group empty
+    elif drop == "groups":
+        sp[2, :] = -1
+        sp[3, ::2] = -1
+    sp = sp.reshape(-1)
     y = gen.normal(3, gen.act_stream(3), T * k * H).reshape(T * k, H)
     yt = torch.from_numpy(y).to(ydt)
-    out = mq.moesq_unpermute_combine(yt.to(DEV), dev(R["slot_pos"]), dev(w), out_dtype=torch.float32)
-    ref = orc.combine(yt.to(torch.float64).numpy(), R["slot_pos"], w)
-    assert orc.rel_frobenius(host(out), ref) <= 1e-6
-    outb = mq.moesq_unpermute_combine(yt.to(DEV), dev(R["slot_pos"]), dev(w), out_dtype=torch.bfloat16)
+    # the oracle on the same rows, a dropped copy pointing at an extra zero row
+    y64 = np.vstack([yt.to(torch.float64).numpy(), np.zeros((1, H))])
+    sp_ref = np.where(sp < 0, T * k, sp).astype(np.int32)
+    ref = orc.combine(y64, sp_ref, w)
+    out = mq.moesq_unpermute_combine(yt.to(DEV), dev(sp), dev(w), out_dtype=torch.float32)
+    got = host(out)
+    assert orc.rel_frobenius(got, ref) <= 1e-6
+    # per element: k fp32 products summed in fp32 are within (k + 1) 2^-24 of the sum of |products|
+    mag = orc.combine(np.abs(y64), sp_ref, np.abs(w))
+    assert np.all(np.abs(got - ref) <= (k + 1) * 2.0 ** -24 * mag)
+    empty = (sp.reshape(T, k) < 0).all(1)
+    assert empty.any() == (drop != "none") and np.all(got[empty] == 0.0)
+    outb = mq.moesq_unpermute_combine(yt.to(DEV), dev(sp), dev(w), out_dtype=torch.bfloat16)
     assert orc.rel_frobenius(host(outb.float()), bf16_round(ref)) <= 1e-3
 
 
