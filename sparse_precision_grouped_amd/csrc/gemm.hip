@@ -924,14 +924,17 @@ MOESQ_DEV void load_p(PStage& st, rsrc_t rq, rsrc_t rs, uint32_t voq, uint32_t v
   st.sc2 = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vos + 8u * ss), 0, 0);
 }
 
-// Decode the staged codes of token `tok`, groups 8 qtr .. 8 qtr + 7, into the swizzled tile.
-MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bs, int tok, int qtr) {
+// Decode the staged codes of token `tok`, groups 8 qtr + G0 .. 8 qtr + G1 - 1, into the swizzled tile.
+template <int G0, int G1>
+MOESQ_DEV void stage_p_part(const PStage& st, uint8_t* Bs, int tok, int qtr) {
   f16x2 s0, s1;
   e4m3_pair_f16x2(st.sc2, s0, s1);
   const uint32_t cw[8] = {st.cw0.x, st.cw0.y, st.cw0.z, st.cw0.w, st.cw1.x, st.cw1.y, st.cw1.z, st.cw1.w};
 #pragma unroll
-  for (int i = 0; i < 8; i++) *(u32x4*)b_chunk(Bs, tok, 8 * qtr + i) = decode_x_group(cw[i], i < 4 ? s0 : s1);
+  for (int i = G0; i < G1; i++) *(u32x4*)b_chunk(Bs, tok, 8 * qtr + i) = decode_x_group(cw[i], i < 4 ? s0 : s1);
 }
+
+MOESQ_DEV void stage_p(const PStage& st, uint8_t* Bs, int tok, int qtr) { stage_p_part<0, 8>(st, Bs, tok, qtr); }
 
 // One K-step (64 K) of the wave's MF x NF fragments. The n-fragments go in blocks of G; a block
 // whose first token lies past the expert's last token (n >= nv, wave uniform) is skipped, so a
@@ -1094,13 +1097,20 @@ struct TWS<MF, MLP, false> {
       asm volatile("" ::"v"(m[f].i02), "v"(m[f].i13), "v"(f16x2_bits(m[f].s01)), "v"(f16x2_bits(m[f].s23)));
     }
   }
+  // With the NVFP4 activation codes of the next step (p, loaded at the start of this one), the halves
+  // also decode them into the other LDS tile Bn: half of the groups after step 1, the rest after step
+  // 2. This VALU work then runs beside the MFMAs that the other wave of the SIMD issues, instead of in
+  // a phase of its own in which both waves stage.
   template <int H, int NF, bool XK>
-  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
+  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv, const PStage* p, uint8_t* Bn,
+                      int tok, int qtr) {
     if (H == 0) {
       lds_step<0, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
       lds_step<1, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+      if (!XK) stage_p_part<0, 4>(*p, Bn, tok, qtr);
     } else {
       lds_step<2, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
+      if (!XK) stage_p_part<4, 8>(*p, Bn, tok, qtr);
       lds_step<3, MF, NF, XK>(acc, w, m, Bs, r16, c, nv);
     }
   }
@@ -1114,7 +1124,8 @@ struct TWS<MF, MLP, true> {
   MOESQ_DEV void load1(rsrc_t, const WSrc&, int, int) {}
   MOESQ_DEV void meta() {}
   template <int H, int NF, bool XK>
-  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv) {
+  MOESQ_DEV void half(f32x4 (&acc)[MF][NF], const uint8_t* Bs, int r16, int c, int nv, const PStage*, uint8_t*, int,
+                      int) {
     if (H == 0) dense_superstep_lds<MF, NF>(acc, w, Bs, r16, c, nv);
   }
 };
@@ -1260,15 +1271,20 @@ MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* full_pre, cons
 
 // Per-lane parts of the activation addresses. FP4 path: token = lane + 64 (w & 1), quarter w / 2.
 // f16 path: the wave's 8 direct-to-LDS chunk loads j = 0..7 fill chunks q = (8 w + j) * 64 + lane of
-// the swizzled tile, chunk q holding token q / 32, group (q % 32) ^ (token % 32).
+// the swizzled tile, chunk q holding token r = q / 32 = 16 w + 2 j + h (h = lane / 32), group
+// (q % 32) ^ (r % 32). Its source offset r 2K + 16 (pq ^ (r % 32)) (pq = lane % 32) splits into this
+// lane's part xl = h 2K + 16 (pq ^ 16 (w & 1) ^ h), xor 32 j, plus the uniform (16 w + 2 j) 2K (for
+// K % 256 == 0 the bit fields do not overlap), so each load costs one xor and one add.
 struct BAddr {
-  uint32_t tok, qtr;
+  uint32_t tok, qtr, xl;
 };
 
-MOESQ_DEV BAddr make_baddr(int w, int lane) {
+MOESQ_DEV BAddr make_baddr(int w, int lane, int K) {
   BAddr b;
   b.tok = (uint32_t)(lane + 64 * (w & 1));
   b.qtr = (uint32_t)(w >> 1);
+  const uint32_t h = (uint32_t)lane >> 5, pq = (uint32_t)lane & 31u;
+  b.xl = h * (uint32_t)(2 * K) + 16u * (pq ^ (16u * (uint32_t)(w & 1)) ^ h);
   return b;
 }
 
@@ -1277,12 +1293,10 @@ MOESQ_DEV BAddr make_baddr(int w, int lane) {
 template <int MF, bool XK>
 MOESQ_DEV void issue_b(const TileCtx<MF>& c, int ss, uint8_t* Bs, PStage& p, int w, int lane, const BAddr& ba, int K) {
   if (XK) {
-    const uint32_t ub = (uint32_t)c.tb * (uint32_t)(2 * K) + 512u * ss;
-    const uint32_t h = (uint32_t)lane >> 5, pq = (uint32_t)lane & 31u;
+    const uint32_t ub = ((uint32_t)c.tb + 16u * (uint32_t)w) * (uint32_t)(2 * K) + 512u * ss;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const uint32_t r = 2u * (uint32_t)(8 * w + j) + h;
-      const uint32_t vo = r * (uint32_t)(2 * K) + 16u * (pq ^ (r & 31u)) + ub;
+      const uint32_t vo = (ba.xl ^ (32u * (uint32_t)j)) + (ub + (uint32_t)j * (uint32_t)(4 * K));
 #if defined(__HIP_DEVICE_COMPILE__)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (__attribute__((address_space(3))) void*)(Bs + (8 * w + j) * 1024),
                                                16, (int)vo, 0, 0, 0);
@@ -1396,7 +1410,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   const int tend = T;
   int t = x * J + j;
   if (t >= tend) return;
-  const BAddr ba = make_baddr(w, lane);
+  const BAddr ba = make_baddr(w, lane, K);
 
   f32x4 acc[MF][NF];
 #pragma unroll
@@ -1433,9 +1447,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     // compiler's wait bookkeeping unsure of how many loads are in flight.
     wc.meta();
     issue_b<MF, XK>(nxt, ss_n, Bn, p, w, lane, ba, K);
-    wc.template half<0, NF, XK>(acc, Bc, r16, cc, cur.nv);
+    wc.template half<0, NF, XK>(acc, Bc, r16, cc, cur.nv, &p, Bn, (int)ba.tok, (int)ba.qtr);
     wc.load0(nxt.rw, nxt.src, lane, ss_n);  // half 0 of the next super-step, its registers read
-    wc.template half<1, NF, XK>(acc, Bc, r16, cc, cur.nv);
+    wc.template half<1, NF, XK>(acc, Bc, r16, cc, cur.nv, &p, Bn, (int)ba.tok, (int)ba.qtr);
     const bool tile_end = ss == nss - 1;
     if (tile_end) {
       tile_epilogue<MF, NF, MLP>(a, cur, acc, w, r16, cc, scal_l);
@@ -1445,7 +1459,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
         for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     wc.load1(nxt.rw, nxt.src, lane, ss_n);
-    if (!XK) stage_b(p, Bn, ba);
+    if (!XK && DENSE) stage_b(p, Bn, ba);  // the sparse weight stage decodes it inside its halves
     if (XK) {
       // the direct-to-LDS loads of the next step (issued first) must have landed; the kLoads1 weight
       // loads issued last may stay in flight. Loads complete in issue order, so waiting until at most
