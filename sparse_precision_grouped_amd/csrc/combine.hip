@@ -15,11 +15,14 @@ struct Row8 {
   uint4 r[YBF16 ? 1 : 2];
 };
 
+// bf16 rows are read with the non-temporal hint: each is read once, and the hint measured 11% faster
+// at the Kimi prefill size (c4 combine 202 -> 179 us); fp32 rows measured no better with it.
 template <bool YBF16>
 MOESQ_DEV Row8<YBF16> combine_load(const void* __restrict__ y, int64_t p, int32_t H, int col) {
   Row8<YBF16> o;
   if (YBF16) {
-    o.r[0] = *(const uint4*)((const uint16_t*)y + p * H + col);
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)y + p * H + col));
+    o.r[0] = make_uint4(v.x, v.y, v.z, v.w);
   } else {
     o.r[0] = *(const uint4*)((const float*)y + p * H + col);
     o.r[YBF16 ? 0 : 1] = *(const uint4*)((const float*)y + p * H + col + 4);
