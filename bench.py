@@ -80,7 +80,7 @@ def fused_eligible(cfg):
 
 def _src_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in ("gemm.hip", "common.h", "api.hip", "launch.h"):  # the kernels and which operands they get
         with open(os.path.join(ROOT, "sparse_precision_grouped_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -384,11 +384,12 @@ class Workload:
 
     def down_only(self, r):
         """The MLP's down GEMM alone (the same kernel and operands as the second launch of
-        moesq_expert_mlp: the requantized h codes and their f16 copy from the workspace)."""
+        moesq_expert_mlp: the requantized h codes from the workspace, and for the weight-streaming
+        form (rows <= 16 E) their f16 copy; the tiled form stages h from the codes)."""
         mq, cfg, sl = self.mq, self.cfg, self.slots[r]
         I = cfg.N // 2
         hq, hs, _ = mq.mlp_workspace_views(sl["ws_mlp"], self.rows, I)
-        hk = mq.mlp_hk_view(sl["ws_mlp"], self.rows, I)
+        hk = mq.mlp_hk_view(sl["ws_mlp"], self.rows, I) if self.rows <= 16 * cfg.E else None
         mq.moesq_grouped_gemm(self.W2c[r], hq, hs, sl["gh"], sl["rt"]["offsets"], y=sl["y2"], xk=hk)
 
     def capture(self):

@@ -251,7 +251,8 @@ int moesq_grouped_gemm(void *stream, const moesq_weights *W, const uint8_t *q, c
  * xk is the optional f16 copy of (q, s) from moesq_quantize_act.
  * Workspace: moesq_workspace_bytes(MOESQ_WS_MLP, ..., rows, k=0, E, K=H, N=0, I) bytes; it holds, each
  *   region starting on a 256-byte boundary, h_q [rows][I/2], h_s [rows][I/32] and h_k [rows][I] (the
- *   f16 copy of the requantized h read by the down GEMM). With MOESQ_F_DUMP_GATEUP and/or
+ *   f16 copy of the requantized h, which the weight-streaming down GEMM reads; the tiled down GEMM
+ *   stages h from h_q/h_s, and the tiled kernels write h_k only with a dump flag). With MOESQ_F_DUMP_GATEUP and/or
  *   MOESQ_F_DUMP_H the size is moesq_workspace_bytes(MOESQ_WS_MLP_DUMP, ...) and two more regions
  *   follow: the fp32 gate_up outputs [rows][2I] (written with MOESQ_F_DUMP_GATEUP), then the fp32 h
  *   [rows][I] the requantization read (written with MOESQ_F_DUMP_H). Rows no expert owns are not
