@@ -482,6 +482,7 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
     // amax takes the plain division and encoder
     const float r = sv != 0.0f ? 1.0f / sv : 0.0f;
     const bool fast = am * r < 1e30f;
+    uint32_t cw[2];
 #pragma unroll
     for (int f = 0; f < 2; f++) {
       uint32_t codes = 0u;
@@ -493,8 +494,8 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
           for (int i = 0; i < 4; i++) codes |= e2m1_encode(h[4 * f + i] / sv) << (4 * i);
         }
       }
+      cw[f] = codes;
       const int i0 = ib + 16 * f + 4 * cc;  // 4 consecutive intermediate columns: half (cc & 1) of an 8-group
-      *(uint16_t*)(a.h_q + p * (I / 2) + i0 / 2) = (uint16_t)codes;
       if (a.h_k) {
         // f16 copy in the de-interleaved group order (a0,a2,a4,a6,a1,a3,a5,a7): this lane holds
         // a[4h..4h+3] (h = cc & 1) and writes words h ((a4h, a4h+2)) and 2 + h ((a4h+1, a4h+3)).
@@ -505,6 +506,12 @@ MOESQ_DEV float mlp_epilogue_token(const GemmArgs& a, int64_t p, bool tv, int ib
         *(uint32_t*)(grp + 8 + 4 * (cc & 1)) = __builtin_amdgcn_perm(v23, v01, 0x07060302u);
       }
     }
+    // The two lanes of a lane-row pair (cc = 2m, 2m + 1; same token) swap halves: the even lane then
+    // holds the 8 codes of columns ib + 4 cc .. + 7 of the first 16, the odd lane those of columns
+    // ib + 16 + 4 (cc - 1) .. + 7, and each stores them as one 4-byte word.
+    const auto pr = __builtin_amdgcn_permlane16_swap(cw[0], cw[1], false, false);
+    const int g0 = (cc & 1) ? ib + 16 + 4 * (cc - 1) : ib + 4 * cc;
+    *(uint32_t*)(a.h_q + p * (I / 2) + g0 / 2) = (pr[0] & 0xFFFFu) | (pr[1] << 16);
     if (cc == 0) a.h_s[p * (I / 32) + ib / 32] = (uint8_t)sc;
   }
   return tv ? am : 0.0f;
