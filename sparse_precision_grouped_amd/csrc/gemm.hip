@@ -1216,10 +1216,12 @@ MOESQ_DEV void build_tile_prefix(const GemmArgs& a, int32_t* full_pre, int32_t* 
 }
 
 // One output tile of the persistent schedule and the per-tile operand addressing (all wave uniform).
-template <int MF>
-struct TileCtx {
+struct TileEpi {  // what the MMA and the epilogue of a tile read
   int e, off, ne, tb, rb, nv;
   float alpha;
+};
+template <int MF>
+struct TileCtx : TileEpi {
   rsrc_t rw;          // expert's weights (kernel layout)
   WSrc src;           // the wave's m-fragments in the kernel layout
   rsrc_t rq, rs;      // expert's activation codes / scales (FP4 path) or f16 activations (rq, f16 path)
@@ -1230,19 +1232,23 @@ struct TileCtx {
 // partial last tiles in plist order, each with its RB row blocks.
 template <int MF, bool MLP, bool XK, bool DENSE>
 MOESQ_DEV TileCtx<MF> make_tile(const GemmArgs& a, const int32_t* full_pre, const int32_t* off_l, const int32_t* ne_l,
-                                const float* scal_l, const int32_t* plist, int RB, int t, int w) {
+                                const float* scal_l, const int32_t* plist, const uint16_t* lut, int RB, int t, int w) {
   TileCtx<MF> c;
   const int TA = __builtin_amdgcn_readfirstlane(full_pre[a.E]) * RB;
   if (t < TA) {
-    int lo = 0, hi = a.E - 1;  // largest e with full_pre[e] * RB <= t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (full_pre[mid] * RB <= t) lo = mid; else hi = mid - 1;
+    const int u = t / RB;  // full token tile u, row block t % RB
+    if (lut) {
+      c.e = __builtin_amdgcn_readfirstlane((int)lut[u]);
+    } else {
+      int lo = 0, hi = a.E - 1;  // largest e with full_pre[e] * RB <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (full_pre[mid] * RB <= t) lo = mid; else hi = mid - 1;
+      }
+      c.e = __builtin_amdgcn_readfirstlane(lo);
     }
-    c.e = __builtin_amdgcn_readfirstlane(lo);
-    const int local = t - __builtin_amdgcn_readfirstlane(full_pre[c.e]) * RB;
-    c.tb = __builtin_amdgcn_readfirstlane((local / RB) * kTileTok);
-    c.rb = __builtin_amdgcn_readfirstlane(local % RB);
+    c.tb = __builtin_amdgcn_readfirstlane((u - full_pre[c.e]) * kTileTok);
+    c.rb = __builtin_amdgcn_readfirstlane(t - u * RB);
   } else {
     const int u = t - TA;
     c.e = __builtin_amdgcn_readfirstlane(plist[u / RB]);
@@ -1327,7 +1333,7 @@ MOESQ_DEV void stage_b(const PStage& p, uint8_t* Bs, const BAddr& ba) { stage_p(
 
 // Epilogue of a finished tile.
 template <int MF, int NF, int MLP>
-MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileCtx<MF>& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc,
+MOESQ_DEV void tile_epilogue(const GemmArgs& a, const TileEpi& c, f32x4 (&acc)[MF][NF], int w, int r16, int cc,
                              const float* scal_l) {
   const int N = a.N;
   const float alpha = c.alpha;
@@ -1413,6 +1419,16 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   float* scal_l = (float*)(ne_l + a.E);                  // [3E]
   int32_t* plist = (int32_t*)(scal_l + 3 * a.E);         // [E+1]
   build_tile_prefix<kTileThreads>(a, full_pre, off_l, ne_l, scal_l, plist, part);
+  // the expert of every full token tile, when the table fits (lut_cap entries): one LDS read per tile
+  // switch instead of a binary search over full_pre
+  const uint16_t* lut = nullptr;
+  if (full_pre[a.E] <= a.lut_cap) {
+    uint16_t* l = (uint16_t*)(plist + a.E + 1);
+    for (int e = threadIdx.x; e < a.E; e += kTileThreads)
+      for (int u = full_pre[e]; u < full_pre[e + 1]; u++) l[u] = (uint16_t)e;
+    __syncthreads();
+    lut = l;
+  }
   const int K = a.K, nss = K / 256;
   const int RB = MLP ? a.N / 512 : (a.N + 511) / 512;   // MLP: 256 gate + 256 up rows per tile
   const int T = (full_pre[a.E] + plist[a.E]) * RB;
@@ -1432,12 +1448,15 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
     for (int n = 0; n < NF; n++) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   constexpr bool kMlp = MLP != kEpiPlain;
-  TileCtx<MF> cur = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, RB, t, w);
+  // nxt: the tile of the step whose operands are loaded next (the current tile until its last step);
+  // cur: the MMA and epilogue fields of the step being computed
+  TileCtx<MF> nxt = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, lut, RB, t, w);
+  TileEpi cur = nxt;
   TWS<MF, kMlp, DENSE> wc;
   PStage p;
-  wc.load0(cur.rw, cur.src, lane, 0);
-  wc.load1(cur.rw, cur.src, lane, 0);
-  issue_b<MF, XK>(cur, 0, Bs0, p, w, lane, ba, K);
+  wc.load0(nxt.rw, nxt.src, lane, 0);
+  wc.load1(nxt.rw, nxt.src, lane, 0);
+  issue_b<MF, XK>(nxt, 0, Bs0, p, w, lane, ba, K);
   if (!XK) stage_b(p, Bs0, ba);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1451,8 +1470,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
       t_n = t + 8 * J;
     }
     const bool has_n = t_n < tend;
-    TileCtx<MF> nxt = cur;
-    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, RB, t_n, w);
+    if (has_n && ss_n == 0) nxt = make_tile<MF, kMlp, XK, DENSE>(a, full_pre, off_l, ne_l, scal_l, plist, lut, RB, t_n, w);
     uint8_t* Bc = bsel ? Bs1 : Bs0;
     uint8_t* Bn = bsel ? Bs0 : Bs1;
     // The prefetches below are issued on every super-step, the last one too (there they read the current
@@ -1494,7 +1512,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void gemm_tile_kernel(GemmArgs a) 
   }
 }
 
-static size_t tile_lds_bytes(int E) { return 2 * (size_t)kBTileBytes + (3 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
+static size_t tile_tables_bytes(int E) { return 2 * (size_t)kBTileBytes + (3 * (size_t)(E + 1) + 4 * (size_t)E) * 4; }
+// Entries of the full-token-tile table: one per possible full tile (rows / kTileTok), as far as the LDS
+// left beside the tile tables and the kernel's static LDS holds them (0: the kernel searches full_pre).
+static int tile_lut_cap(int E, int64_t rows) {
+  const int64_t room = (160 * 1024 - (int64_t)tile_tables_bytes(E) - kTileThreads * 4) / 2;
+  return (int)std::max<int64_t>(0, std::min<int64_t>(rows / kTileTok, room & ~(int64_t)1));
+}
+static size_t tile_lds_bytes(int E, int lut_cap) { return tile_tables_bytes(E) + (size_t)(lut_cap + 1) / 2 * 4; }
 // the tile tables of the largest expert count the GEMM calls accept fit one workgroup's 160 KiB of LDS
 static_assert(2 * kBTileBytes + (3 * (kMaxExpertsGemm + 1) + 4 * kMaxExpertsGemm) * 4 + kTileThreads * 4 <= 160 * 1024,
               "tile tables for kMaxExpertsGemm experts exceed the LDS");
@@ -1570,21 +1595,23 @@ int launch_gemm_variant(hipStream_t st, const GemmArgs& a, int64_t rows, int var
     // persistent grid: one 8-wave workgroup per CU, a multiple of the 8 XCDs
     const int grid = 8 * ((device_cu_count() + 7) / 8);
     const bool xk = a.xk != nullptr;
-    const size_t lds = tile_lds_bytes(a.E);
+    GemmArgs at = a;
+    at.lut_cap = tile_lut_cap(a.E, rows);
+    const size_t lds = tile_lds_bytes(a.E, at.lut_cap);
     const dim3 g(grid), b(kTileThreads);
     if (xk) {
       switch (epi) {
-        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, true>), g, b, lds, st, a); break;
-        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, true>), g, b, lds, st, a); break;
-        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, true>), g, b, lds, st, a); break;
-        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true>), g, b, lds, st, a); break;
+        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, true>), g, b, lds, st, at); break;
+        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, true>), g, b, lds, st, at); break;
+        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, true>), g, b, lds, st, at); break;
+        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true>), g, b, lds, st, at); break;
       }
     } else {
       switch (epi) {
-        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, false>), g, b, lds, st, a); break;
-        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, false>), g, b, lds, st, a); break;
-        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, false>), g, b, lds, st, a); break;
-        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false>), g, b, lds, st, a); break;
+        case kEpiMlp: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlp, false>), g, b, lds, st, at); break;
+        case kEpiMlpDump: hipLaunchKernelGGL((gemm_tile_kernel<kEpiMlpDump, false>), g, b, lds, st, at); break;
+        case kEpiCalib: hipLaunchKernelGGL((gemm_tile_kernel<kEpiCalib, false>), g, b, lds, st, at); break;
+        default: hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false>), g, b, lds, st, at); break;
       }
     }
   }
@@ -1598,9 +1625,11 @@ int launch_dense_gemm(hipStream_t st, const GemmArgs& a, int64_t rows, int varia
     launch_decode<4, 4, 1, true>(st, a);
   } else {
     const int grid = 8 * ((device_cu_count() + 7) / 8);
-    const size_t lds = tile_lds_bytes(a.E);
-    if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
-    else hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false, true>), dim3(grid), dim3(kTileThreads), lds, st, a);
+    GemmArgs at = a;
+    at.lut_cap = tile_lut_cap(a.E, rows);
+    const size_t lds = tile_lds_bytes(a.E, at.lut_cap);
+    if (a.xk) hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, true, true>), dim3(grid), dim3(kTileThreads), lds, st, at);
+    else hipLaunchKernelGGL((gemm_tile_kernel<kEpiPlain, false, true>), dim3(grid), dim3(kTileThreads), lds, st, at);
   }
   return hipGetLastError() == hipSuccess ? MOESQ_OK : MOESQ_ERR_HIP;
 }

@@ -38,6 +38,7 @@ struct GemmArgs {
   float* hdump;           // [rows][I] fp32 h = SiLU(g) * u (the values the requantization reads), or nullptr
   uint32_t* amax_h;       // calibration: [E] per-expert amax(h) as float bits (atomic max; zeroed by the caller);
                           // when set the epilogue writes no h codes, scales or copies
+  int32_t lut_cap;        // tiled kernel (set by its launcher): LDS entries of the full-token-tile -> expert table
 };
 
 size_t route_workspace_bytes(int64_t n, int32_t E);
