@@ -661,6 +661,33 @@ def test_grouped_gemm_smallest_shapes(flags):
         gemm_gate(host(y), orc.grouped_gemm(Wo, qo, so, ga, R["offsets"]), "gemm E=%d N=64 K=256 %s" % (E, flags))
 
 
+@pytest.mark.parametrize("n_full", [1000, 1024])
+def test_grouped_gemm_many_full_tiles(n_full):
+    """The tiled kernel at the largest expert count it takes (E = 1024, N = 64, K = 256) with n_full
+    experts of 129 tokens (one full token tile and a 1-token partial tile each) and the rest empty. Its
+    workgroups look up the expert of a full token tile in an LDS table when the table fits beside the
+    tile tables (1018 entries at E = 1024): 1000 full tiles take the table, 1024 the binary search over
+    the tile prefix. Sampled rows (every nonempty expert's first and last row among them) against the
+    oracle."""
+    say("gemm many full tiles", n_full)
+    E, N, K = 1024, 64, 256
+    counts = np.zeros(E, np.int64)
+    counts[:n_full] = 129
+    rng = np.random.default_rng(2024)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    Wo, Wd = orc.compress(w), mq.moesq_compress_weights(dev(w))
+    rows = int(counts.sum())
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts).reshape(rows, 1)
+    R = orc.route(ids, E)
+    x = gen.student_t(93, gen.act_stream(5), rows * K).reshape(rows, K)
+    ga = np.full(E, orc.global_scale_of(x), np.float32)
+    qo, so = orc.dispatch_quantize(x, R["sorted_slot"], 1, R["offsets"], ga)
+    y = mq.moesq_grouped_gemm(Wd, dev(qo), dev(so), dev(ga), dev(R["offsets"]), y_dtype=torch.float32,
+                              flags=mq.F_FORCE_PREFILL)
+    sr = sample_rows(R["offsets"], 4096, seed=n_full)
+    gemm_gate(host(y)[sr], orc.grouped_gemm(Wo, qo, so, ga, R["offsets"], sr), "gemm E=1024 full tiles %d" % n_full)
+
+
 # ------------------------------------------------- dispatch + GEMM in one call --------------
 def _rqg_check(ids, x, E, ga, Wd, Wo=None, bf16=False, y_dtype=torch.float32, oracle_rows=None):
     """moesq_route_quantize_gemm byte for byte against moesq_route_quantize + moesq_grouped_gemm (the
